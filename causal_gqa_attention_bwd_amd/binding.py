@@ -1,0 +1,125 @@
+"""Thin ctypes binding over libattnbwd.so (C ABI declared in include/attnbwd.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+EXPORTED = ("attn_bwd", "attn_fwd_lse", "attn_last_error")
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str, msg: str):
+        super().__init__(f"{what} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_bwd.restype = I
+    lib.attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_fwd_lse.restype = I
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def _raise_on(status: int, what: str):
+    if status != ATTN_OK:
+        raise AttnError(status, what, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _check_tensors(named, dev):
+    import torch
+    for name, t, dtypes in named:
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _dims(Q, K):
+    if Q.dim() != 3 or K.dim() != 3:
+        raise ValueError("Q must be [S, H, d] and K [S, KV, d]")
+    S, H, d = Q.shape
+    if K.shape[0] != S or K.shape[2] != d:
+        raise ValueError(f"Q {tuple(Q.shape)} and K {tuple(K.shape)} disagree")
+    return S, H, K.shape[1], d
+
+
+def attn_bwd(Q, K, V, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
+    """dQ += ..., dK += ..., dV += ... (the C ABI's attn_bwd) on torch device tensors.
+
+    Q, dO, dQ [S,H,d]; K, V, dK, dV [S,KV,d]; LSE [S,H] float32; seg [S]
+    int32/uint32 document starts or None (plain causal).
+    """
+    import torch
+    S, H, KV, d = _dims(Q, K)
+    f32 = (torch.float32,)
+    _check_tensors([("Q", Q, f32), ("K", K, f32), ("V", V, f32), ("dO", dO, f32),
+                    ("LSE", LSE, f32), ("seg", seg, (torch.int32, torch.uint32)),
+                    ("dQ", dQ, f32), ("dK", dK, f32), ("dV", dV, f32)], Q.device)
+    for name, t, shape in (("V", V, K.shape), ("dO", dO, Q.shape), ("LSE", LSE, (S, H)),
+                           ("dQ", dQ, Q.shape), ("dK", dK, K.shape), ("dV", dV, K.shape)):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if seg is not None and tuple(seg.shape) != (S,):
+        raise ValueError(f"seg has shape {tuple(seg.shape)}, expected ({S},)")
+    st = load().attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(seg),
+                         _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
+                         _stream(stream))
+    _raise_on(st, "attn_bwd")
+
+
+def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):
+    """O, LSE = forward of the masked attention (the C ABI's attn_fwd_lse); O may be None."""
+    import torch
+    S, H, KV, d = _dims(Q, K)
+    f32 = (torch.float32,)
+    _check_tensors([("Q", Q, f32), ("K", K, f32), ("V", V, f32),
+                    ("seg", seg, (torch.int32, torch.uint32)), ("O", O, f32), ("LSE", LSE, f32)],
+                   Q.device)
+    if tuple(LSE.shape) != (S, H) or (O is not None and tuple(O.shape) != tuple(Q.shape)):
+        raise ValueError("O must be [S,H,d] and LSE [S,H]")
+    st = load().attn_fwd_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(seg), _ptr(O), _ptr(LSE),
+                             S, H, KV, d, float(scale), _stream(stream))
+    _raise_on(st, "attn_fwd_lse")

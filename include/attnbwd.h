@@ -1,0 +1,110 @@
+/*
+ * attnbwd.h -- C ABI of the MI355X (gfx950) attention-backward library.
+ *
+ * Operation.  Backward pass of causal grouped-query multi-head attention with
+ * a per-query document-start mask, as defined on the page
+ * "llm.istanbul -- 10_backward_attention.wgsl" (header comment; kernel
+ * attention_backward, Pass 0 / Pass A / Pass B / Final):
+ *
+ *   kv_h(h)  = h / (n_heads / n_kv_heads)            (contiguous head groups)
+ *   visible  : key j is visible to query s  iff  seg[s] <= j <= s
+ *   P[s,j]   = exp(scale * Q[s,h,:] . K[j,kv_h,:] - LSE[s,h])
+ *   dP[s,j]  = dO[s,h,:] . V[j,kv_h,:]
+ *   D[s,h]   = sum over visible j of P[s,j] * dP[s,j]
+ *   dS[s,j]  = scale * P[s,j] * (dP[s,j] - D[s,h])
+ *   dQ[s,h,:]    += sum_j dS[s,j] * K[j,kv_h,:]
+ *   dK[j,kv,:]   += sum over s and the heads h of group kv of dS[s,j] * Q[s,h,:]
+ *   dV[j,kv,:]   += sum over s and the heads h of group kv of P[s,j] * dO[s,h,:]
+ *
+ * Invisible (masked) pairs contribute exactly nothing: they are selected
+ * away, never multiplied by zero, so non-finite values at masked positions
+ * cannot leak into visible rows.
+ *
+ * Layouts (all fp32 unless noted, contiguous, row-major, no batch dimension --
+ * packed documents replace batching):
+ *   Q, dO, dQ, O   [seq_len, n_heads,    head_dim]
+ *   K, V, dK, dV   [seq_len, n_kv_heads, head_dim]
+ *   LSE            [seq_len, n_heads]      natural log
+ *   seg            [seq_len] uint32        start index of the query's document;
+ *                                          NULL means all zeros (plain causal).
+ *                                          Values must be < 2^31.  A row with
+ *                                          seg[s] > s sees no key: it contributes
+ *                                          nothing (and its forward LSE is -inf).
+ *
+ * Pointers.  Every tensor pointer is a device pointer on the current HIP
+ * device, 16-byte aligned.  The caller owns every buffer; the library keeps
+ * no pointer after a call returns.  dQ, dK, dV must not overlap each other
+ * or any input; inputs are only read.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ * enqueue work and return; kernel-execution faults surface at the caller's
+ * next synchronisation.  Launch-time errors return ATTN_ERR_HIP.
+ *
+ * Threads.  Reentrant.  The only global state is the thread-local text of
+ * the last error.
+ */
+#ifndef ATTNBWD_H
+#define ATTNBWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  /* a required pointer is NULL (only seg and, for attn_fwd_lse, O may be);
+     seq_len < 0; n_heads < 1; n_kv_heads < 1; n_heads % n_kv_heads != 0;
+     scale not finite */
+  ATTN_ERR_INVALID_ARG = 1,
+  /* head_dim not a multiple of 16 in [16, 256]; a pointer not 16-byte
+     aligned; sizes whose element offsets exceed 2^31 - 1 */
+  ATTN_ERR_UNSUPPORTED = 2,
+  /* a HIP runtime call or kernel launch failed (text: attn_last_error) */
+  ATTN_ERR_HIP = 3
+} attn_status_t;
+
+/*
+ * attn_bwd -- the backward pass above.
+ *
+ * dQ, dK and dV are ACCUMULATED ("+=": the header comment of the wgsl page
+ * gives dQ += semantics with the host zeroing before the first call, and dK,
+ * dV accumulate likewise).  Zero them before the first accumulation.
+ *
+ * Internally the call takes one stream-ordered workspace of
+ * seq_len * n_heads * 4 bytes (the row term D) plus seq_len / 8 bytes of tile
+ * metadata, allocated with hipMallocAsync on `stream` and released with
+ * hipFreeAsync on `stream` before returning.
+ *
+ * seq_len == 0 returns ATTN_OK and enqueues nothing.
+ */
+attn_status_t attn_bwd(const float* Q, const float* K, const float* V, const float* dO,
+                       const float* LSE, const uint32_t* seg,
+                       float* dQ, float* dK, float* dV,
+                       int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                       void* stream);
+
+/*
+ * attn_fwd_lse -- the forward pass that produces the backward's inputs:
+ *   LSE[s,h] = ln sum over visible j of exp(scale * Q[s,h,:] . K[j,kv_h,:])
+ *   O[s,h,:] = sum over visible j of exp(scale * Q[s,h,:] . K[j,kv_h,:] - LSE[s,h]) * V[j,kv_h,:]
+ * (page "tang 0.2.0 -- src/gpu/llm.rs", causal_attention_fused: row max,
+ * exp-sum, weighted V; with the document mask above and the log-sum-exp
+ * output the backward consumes).  O and LSE are OVERWRITTEN.  O may be NULL
+ * (LSE only).  A row that sees no key gets LSE = -inf and O = 0.
+ */
+attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const uint32_t* seg,
+                           float* O, float* LSE,
+                           int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                           void* stream);
+
+/* Text describing the last non-OK status returned on the calling thread
+   ("" if none).  The pointer stays valid until the thread's next call. */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNBWD_H */
