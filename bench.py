@@ -1,0 +1,222 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention backward on one MI355X.
+
+One step = one attn_bwd call (the whole hot path: the dQ/row-term kernel and
+the dK/dV kernel) on the S=4096, H=32, KV=8, d=128 plain-causal workload,
+fp32 inputs already resident in HBM.  The LSE input is produced beforehand on
+the GPU by attn_fwd_lse (untimed).
+
+Metric: credited TFLOP/s = 10 * d * H * N_valid / time per step, where
+N_valid is the number of visible (query, key) pairs (five contractions of 2*d
+flops per visible pair and head).  Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
+PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16/bf16 matrix
+PEAK_HBM = 8.0           # TB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_dkdv_s4096_h32_kv8_d128_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc", "attnbwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def valid_pairs(seg):
+    import numpy as np
+    s = np.arange(len(seg), dtype=np.int64)
+    return int(np.sum(np.maximum(s - np.asarray(seg, np.int64) + 1, 0)))
+
+
+def source_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(n_launch_note):
+    """HBM bytes per k_dkdv launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != source_sha():
+        log(f"traffic: {TRAFFIC_FILE} was taken on another kernel source; reporting null")
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x, groups):
+    """The oracle's backward on a bounded sample (the first `groups` KV groups:
+    all S rows, `groups` KV heads and their query heads), timed on host cores."""
+    import numpy as np
+    import oracle
+    w = x["workload"]
+    g = w.H // w.KV
+    groups = min(groups, w.KV)
+    nh = g * groups
+    Q = np.ascontiguousarray(x["Q"][:, :nh])
+    dO = np.ascontiguousarray(x["dO"][:, :nh])
+    K = np.ascontiguousarray(x["K"][:, :groups])
+    V = np.ascontiguousarray(x["V"][:, :groups])
+    threads = min(16, len(os.sched_getaffinity(0)))
+    _, lse = oracle.attn_fwd(Q, K, V, x["seg"], x["scale"], nthreads=threads, want_o=False)
+    t0 = time.perf_counter()
+    oracle.attn_bwd(Q, K, V, dO, lse, x["seg"], x["scale"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    flops = 10.0 * w.d * nh * valid_pairs(x["seg"])
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"oracle attn_bwd (fp64 C, {threads} threads) on KV heads 0..{groups - 1} "
+                      f"({nh} of {w.H} query heads, all {w.S} rows) of the same workload; "
+                      f"{dt:.2f} s wall; {cpu_model}",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=4, help="workload id (default: the headline one)")
+    ap.add_argument("--cpu-groups", type=int, default=8,
+                    help="KV groups in the oracle's timed sample (0: skip the CPU baseline)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from causal_gqa_attention_bwd_amd import binding
+    from causal_gqa_attention_bwd_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    x = make_inputs(args.workload)
+    w = x["workload"]
+    log(f"bench: workload {w.name}: S={w.S} H={w.H} KV={w.KV} d={w.d}")
+    t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev) for k in ("Q", "K", "V", "dO")}
+    seg_np = x["seg"]
+    seg = None if not np.any(seg_np) else torch.from_numpy(seg_np.astype(np.int32)).to(dev)
+    scale = float(x["scale"])
+    lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
+    binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, None, lse, scale)
+    dQ = torch.zeros_like(t["Q"])
+    dK = torch.zeros_like(t["K"])
+    dV = torch.zeros_like(t["V"])
+    torch.cuda.synchronize()
+
+    def step():
+        binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], lse, seg, dQ, dK, dV, scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"bench: calibration copy of {args.calib_copy_mb} MiB done")
+
+    binding.profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_dq, ms_dkdv, ncalls = binding.profile_end()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    assert ncalls == args.steps
+    if not (torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()):
+        raise RuntimeError("non-finite gradients")
+
+    npairs = valid_pairs(seg_np)
+    flops = 10.0 * w.d * w.H * npairs
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    avg_dq, avg_dkdv = ms_dq / ncalls, ms_dkdv / ncalls
+    log(f"bench: {ms_step:.3f} ms/step, k_dq {avg_dq:.3f} ms, k_dkdv {avg_dkdv:.3f} ms, "
+        f"{tflops:.2f} TFLOP/s credited")
+
+    # dominant kernel: algorithmic flops per launch / its measured average duration
+    if avg_dkdv >= avg_dq:
+        kname, kms = "k_dkdv", avg_dkdv
+        kflops = 8.0 * w.d * w.H * npairs  # Q.K^T, dO.V^T, P^T.dO, dS^T.Q
+        traffic = read_traffic("k_dkdv")
+    else:
+        kname, kms = "k_dq", avg_dq
+        kflops = 6.0 * w.d * w.H * npairs  # Q.K^T, dO.V^T (row term), dS.K
+        traffic = None
+    kach = kflops / (kms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
+                "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s", "frac": round(kach / PEAK_FP32_MFMA, 4),
+                "traffic": traffic, "avg_launch_ms": round(kms, 4)}
+
+    cpu = None
+    if args.cpu_groups > 0:
+        log("bench: timing the oracle on the host ...")
+        cpu = cpu_baseline(x, args.cpu_groups)
+        log(f"bench: oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads "
+            f"({cpu['seconds']:.1f} s)")
+        cpu = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cpu.items()
+               if k != "seconds"}
+
+    out = {
+        "metric": "attention-backward TFLOP/s (causal FLOPs) and % of MI355X matrix peak",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_peak_fp32_matrix": round(100.0 * tflops / PEAK_FP32_MFMA, 2),
+        "pct_of_peak_fp16_matrix": round(100.0 * tflops / PEAK_FP16_MFMA, 3),
+        "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
+                   "head_dim": w.d, "mask": "causal" if seg is None else "documents",
+                   "valid_pairs": npairs, "credited_flops_per_step": flops,
+                   "kernel_ms": {"k_dq": round(avg_dq, 4), "k_dkdv": round(avg_dkdv, 4)}},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -13,7 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_fwd_lse", "attn_last_error")
+EXPORTED = ("attn_bwd", "attn_fwd_lse", "attn_last_error", "attn_profile_begin",
+            "attn_profile_end")
 
 _lib = None
 
@@ -38,6 +39,10 @@ def load():
     lib.attn_bwd.restype = I
     lib.attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_fwd_lse.restype = I
+    lib.attn_profile_begin.argtypes = []
+    lib.attn_profile_begin.restype = I
+    lib.attn_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    lib.attn_profile_end.restype = I
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -123,3 +128,16 @@ def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):
     st = load().attn_fwd_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(seg), _ptr(O), _ptr(LSE),
                              S, H, KV, d, float(scale), _stream(stream))
     _raise_on(st, "attn_fwd_lse")
+
+
+def profile_begin():
+    """Start recording per-kernel HIP events inside attn_bwd (calling thread only)."""
+    _raise_on(load().attn_profile_begin(), "attn_profile_begin")
+
+
+def profile_end():
+    """Stop recording; returns (ms_dq_kernel, ms_dkdv_kernel, n_calls) summed over the calls."""
+    ms = (ctypes.c_double * 2)()
+    n = ctypes.c_int(0)
+    _raise_on(load().attn_profile_end(ms, ctypes.byref(n)), "attn_profile_end")
+    return float(ms[0]), float(ms[1]), int(n.value)

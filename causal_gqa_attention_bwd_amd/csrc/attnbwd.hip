@@ -31,14 +31,20 @@
 // (keys or queries), register r of an accumulator tile is directly the A
 // operand of the next product: no transposes anywhere.
 //
-// Masking selects (never multiplies by zero), so non-finite values at
-// invisible positions cannot leak into visible rows.
+// Masking selects the probability and score-gradient tiles (it never multiplies
+// a score by zero), so an overflowing exp or a -inf LSE at an invisible
+// position cannot leak into a visible row.  Input values themselves (K, V rows
+// of a staged key tile; Q, dO rows of a staged query tile) still enter the
+// tile products with a zero weight when invisible: finite inputs contribute
+// exactly 0, non-finite ones would propagate.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+
+#include <vector>
 
 #include "attnbwd.h"
 
@@ -585,6 +591,57 @@ static attn_status_t fail(attn_status_t st, const char* fmt, ...) {
 
 extern "C" const char* attn_last_error(void) { return g_err; }
 
+// Per-thread event log of the measurement hooks (see attn_profile_begin).
+struct ProfileLog {
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 3 per recorded attn_bwd call
+};
+static thread_local ProfileLog g_prof;
+
+static void profile_release() {
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+}
+
+extern "C" attn_status_t attn_profile_begin(void) {
+  g_err[0] = 0;
+  profile_release();
+  g_prof.on = true;
+  return ATTN_OK;
+}
+
+extern "C" attn_status_t attn_profile_end(double* ms, int* n_calls) {
+  g_err[0] = 0;
+  double sum[2] = {0.0, 0.0};
+  attn_status_t rc = ATTN_OK;
+  const size_t n = g_prof.ev.size() / 3;
+  for (size_t i = 0; i < n && rc == ATTN_OK; ++i) {
+    for (int k = 0; k < 2 && rc == ATTN_OK; ++k) {
+      float t = 0.f;
+      hipError_t e = hipEventSynchronize(g_prof.ev[3 * i + k + 1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof.ev[3 * i + k], g_prof.ev[3 * i + k + 1]);
+      if (e != hipSuccess) rc = fail(ATTN_ERR_HIP, "reading profile events: %s", hipGetErrorString(e));
+      sum[k] += t;
+    }
+  }
+  if (ms) { ms[0] = sum[0]; ms[1] = sum[1]; }
+  if (n_calls) *n_calls = (int)n;
+  profile_release();
+  g_prof.on = false;
+  return rc;
+}
+
+// Record one profile event on `st` if the measurement hooks are on.
+static attn_status_t profile_mark(hipStream_t st) {
+  if (!g_prof.on) return ATTN_OK;
+  hipEvent_t e;
+  hipError_t err = hipEventCreate(&e);
+  if (err == hipSuccess) err = hipEventRecord(e, st);
+  if (err != hipSuccess) return fail(ATTN_ERR_HIP, "profile event: %s", hipGetErrorString(err));
+  g_prof.ev.push_back(e);
+  return ATTN_OK;
+}
+
 static int padded_dim(int d) {
   if (d <= 32) return 32;
   if (d <= 64) return 64;
@@ -619,12 +676,17 @@ static attn_status_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   constexpr int DSPL = Geo<DP>::DSPL;
   const int BRq = 32 * (4 / DSPL);
   const int nqt = (a.S + BRq - 1) / BRq;
+  attn_status_t rc = profile_mark(st);
+  if (rc != ATTN_OK) return rc;
   hipLaunchKernelGGL(k_dq<DP>, dim3(nqt * a.H), dim3(256), 0, st, a);
-  attn_status_t rc = hip_check(hipGetLastError(), "launching k_dq");
+  rc = hip_check(hipGetLastError(), "launching k_dq");
+  if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
   const int nkt = (a.S + 63) / 64;
   hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
-  return hip_check(hipGetLastError(), "launching k_dkdv");
+  rc = hip_check(hipGetLastError(), "launching k_dkdv");
+  if (rc == ATTN_OK) rc = profile_mark(st);
+  return rc;
 }
 
 template <int DP>

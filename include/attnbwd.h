@@ -16,9 +16,11 @@
  *   dK[j,kv,:]   += sum over s and the heads h of group kv of dS[s,j] * Q[s,h,:]
  *   dV[j,kv,:]   += sum over s and the heads h of group kv of P[s,j] * dO[s,h,:]
  *
- * Invisible (masked) pairs contribute exactly nothing: they are selected
- * away, never multiplied by zero, so non-finite values at masked positions
- * cannot leak into visible rows.
+ * Invisible (masked) pairs contribute exactly nothing for finite inputs: the
+ * probability and score-gradient of an invisible pair are selected to zero
+ * (never computed as a product with zero), so an overflowing exponential or a
+ * -inf LSE there cannot reach a visible row.  A non-finite VALUE in an input
+ * row (Q, K, V, dO) may still propagate to rows that share its tile.
  *
  * Layouts (all fp32 unless noted, contiguous, row-major, no batch dimension --
  * packed documents replace batching):
@@ -40,8 +42,8 @@
  * enqueue work and return; kernel-execution faults surface at the caller's
  * next synchronisation.  Launch-time errors return ATTN_ERR_HIP.
  *
- * Threads.  Reentrant.  The only global state is the thread-local text of
- * the last error.
+ * Threads.  Reentrant.  The only global state is thread-local: the text of
+ * the last error and the event log of the measurement hooks.
  */
 #ifndef ATTNBWD_H
 #define ATTNBWD_H
@@ -98,6 +100,20 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
                            float* O, float* LSE,
                            int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
                            void* stream);
+
+/*
+ * Measurement hooks (benchmarks only; normal callers never need them).
+ *
+ * attn_profile_begin: from now on, on the calling thread, every attn_bwd call
+ *   records HIP events on its stream before, between and after its two
+ *   kernels (the dQ / row-term kernel, then the dK/dV kernel).
+ * attn_profile_end: waits for those events, writes into ms[0] and ms[1] the
+ *   summed device time in milliseconds of the dQ kernel and of the dK/dV
+ *   kernel over the recorded calls, into *n_calls their number, releases the
+ *   events and stops recording.  ms and n_calls may be NULL.
+ */
+attn_status_t attn_profile_begin(void);
+attn_status_t attn_profile_end(double* ms, int* n_calls);
 
 /* Text describing the last non-OK status returned on the calling thread
    ("" if none).  The pointer stays valid until the thread's next call. */
