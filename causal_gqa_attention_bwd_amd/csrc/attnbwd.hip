@@ -87,6 +87,7 @@ struct BwdArgs {
   float *dQ, *dK, *dV;
   float* Dws;            // [S, H] row term, written by k_dq, read by k_dkdv
   uint32_t* blk_min;     // [ceil(S/32)] min seg per 32-row query block
+  uint32_t* blk_max;     // [ceil(S/32)] max seg per 32-row query block
   int S, H, KV, d;
   float scale;
 };
@@ -109,6 +110,15 @@ __device__ __forceinline__ void load_row(const float* row, int cb, int d, bool o
     if (ok && cb + t < d) x = *reinterpret_cast<const float4*>(row + cb + t);
     out[t] = x.x; out[t + 1] = x.y; out[t + 2] = x.z; out[t + 3] = x.w;
   }
+}
+
+// Pin loop-invariant MFMA operands into accumulation registers (AGPRs): the
+// matrix cores read A/B operands from AGPRs directly, and the architectural
+// VGPRs stay free for keeping LDS reads in flight.
+template <int N>
+__device__ __forceinline__ void pin_agpr(float* v) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+a"(v[i]));
 }
 
 // Cooperative load of ROWS x DP floats of two row-major matrices that share
@@ -166,128 +176,309 @@ __device__ __forceinline__ void pair_exchange(float* sX, int wave, int lane, f32
 }
 
 // ---------------------------------------------------------------------------
+// Streaming tiles into LDS.
+//
+// The backward kernels stage row tiles (K/V rows in k_dq, Q/dO rows in
+// k_dkdv) with direct global->LDS loads (global_load_lds_dwordx4: each lane's
+// 16 bytes land at the wave's LDS base + 16 * lane), double-buffered so the
+// next tile streams in while the current one is multiplied.  A tile is kept
+// row-major with rows padded to DP + 4 floats, so that the b128 reads of 32
+// rows at one column and the b32 reads of 32 columns of one row hit distinct
+// banks, and so that every LDS address in the hot loops is one per-lane base
+// plus a compile-time offset.  Each 1 KiB chunk of the padded tile is one
+// wave-wide load; lanes that land on a pad granule, past the tile, past the
+// sequence or past head_dim load 16 zero bytes from g_zero16 instead.
+// ---------------------------------------------------------------------------
+__device__ __attribute__((aligned(16))) float g_zero16[4] = {0.f, 0.f, 0.f, 0.f};
+
+__device__ __forceinline__ void lds_dma16(const float* src, float* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 4, 0, 0);
+}
+
+// Padded ROWS x DP tile filled by 1 KiB chunks.
+template <int ROWS, int DP>
+struct PadTile {
+  static constexpr int LDR = DP + 4;                 // floats per padded row
+  static constexpr int GPR = LDR / 4;                // 16-byte granules per padded row
+  static constexpr int NCH = (ROWS * GPR + 63) / 64; // wave-wide loads per tile
+  static constexpr int FLOATS = NCH * 256;           // LDS floats reserved (>= ROWS * LDR)
+  static constexpr int CPW = (NCH + 3) / 4;          // loads per wave (some waves one fewer)
+};
+
+// Rows [r0, r0 + ROWS) of a row-major matrix (rows `stride` floats apart,
+// head_dim = d valid columns starting at `base`) into the padded LDS tile
+// `lds`.  wave_u must be wave-uniform.
+template <int ROWS, int DP>
+__device__ __forceinline__ void dma_tile(float* lds, const float* base, int r0, int S,
+                                         size_t stride, int d, int wave_u, int lane) {
+  using T = PadTile<ROWS, DP>;
+#pragma unroll
+  for (int i = 0; i < T::CPW; ++i) {
+    const int chunk = wave_u + 4 * i;
+    if (chunk < T::NCH) {
+      const int p = chunk * 64 + lane;  // granule of the padded tile
+      const int row = p / T::GPR, g4 = p % T::GPR;
+      const bool ok = row < ROWS && g4 < DP / 4 && r0 + row < S && 4 * g4 < d;
+      const float* real = base + (size_t)(ok ? r0 + row : 0) * stride + 4 * (ok ? g4 : 0);
+      lds_dma16(ok ? real : g_zero16, lds + chunk * 256);
+    }
+  }
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
+// then s_barrier.  Unlike __syncthreads it does not wait for outstanding global
+// loads, so direct-to-LDS loads of the next tile stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait for all of this wave's outstanding global loads (the current tile's
+// direct-to-LDS loads), then a workgroup barrier: the tile is complete in LDS
+// and every wave has finished with the previous tile.
+__device__ __forceinline__ void tile_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Above 128 columns a pair of waves shares one 32x32 score block by role:
+// role 0 forms the Q.K product, role 1 the dO.V product, over all DP columns,
+// and they swap results through LDS; each then owns DP/2 output columns.
+template <int DP>
+struct Pair {
+  static constexpr bool ROLE = DP > 128;
+  static constexpr int DW = ROLE ? DP / 2 : DP;  // output columns owned by a wave
+  static constexpr int NB = DW / 32;             // 32-column output blocks per wave
+  static constexpr int TH = DP / 2;              // score contraction steps per half-wave
+  static_assert(DW % 32 == 0, "whole 32-column blocks");
+};
+
+// Swap the role products of a wave pair through LDS (16 floats per lane).
+__device__ __forceinline__ f32x16 pair_swap(float* sX, int wave, int lane, const f32x16& mine) {
+  float* w = sX + (wave * 16) * 64 + lane;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) w[r * 64] = mine[r];
+  lds_barrier();
+  const float* o = sX + ((wave ^ 1) * 16) * 64 + lane;
+  f32x16 other;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) other[r] = o[r * 64];
+  return other;
+}
+
+// 32x32 score block over DP columns: acc = A_lds[row a_row][:] . B_reg, where
+// half-wave hf contracts columns [hf*TH, hf*TH + TH).  Two accumulation
+// chains, summed at the end.
+template <int DP>
+__device__ __forceinline__ f32x16 score_block(const float* tile, int a_row, int hf, const float* breg) {
+  constexpr int TH = Pair<DP>::TH, LDR = DP + 4;
+  const float* ap = tile + a_row * LDR + hf * TH;
+  f32x16 c0 = zero16(), c1 = zero16();
+#pragma unroll
+  for (int t = 0; t < TH; t += 4) {
+    const float4 a4 = *reinterpret_cast<const float4*>(ap + t);
+    c0 = mfma32(a4.x, breg[t], c0);
+    c1 = mfma32(a4.y, breg[t + 1], c1);
+    c0 = mfma32(a4.z, breg[t + 2], c0);
+    c1 = mfma32(a4.w, breg[t + 3], c1);
+  }
+  return c0 + c1;
+}
+
+// Two independent 32x32 score blocks sharing the LDS row (S and dP of one block).
+template <int DP>
+__device__ __forceinline__ void score_pair(const float* tA, const float* tB, int a_row, int hf,
+                                           const float* rA, const float* rB, f32x16& x, f32x16& y) {
+  constexpr int TH = Pair<DP>::TH, LDR = DP + 4;
+  const int o0 = a_row * LDR + hf * TH;
+  f32x16 cx = zero16(), cy = zero16();
+#pragma unroll
+  for (int t = 0; t < TH; t += 4) {
+    const float4 a4 = *reinterpret_cast<const float4*>(tA + o0 + t);
+    const float4 b4 = *reinterpret_cast<const float4*>(tB + o0 + t);
+    cx = mfma32(a4.x, rA[t], cx);
+    cy = mfma32(b4.x, rB[t], cy);
+    cx = mfma32(a4.y, rA[t + 1], cx);
+    cy = mfma32(b4.y, rB[t + 1], cy);
+    cx = mfma32(a4.z, rA[t + 2], cx);
+    cy = mfma32(b4.z, rB[t + 2], cy);
+    cx = mfma32(a4.w, rA[t + 3], cx);
+    cy = mfma32(b4.w, rB[t + 3], cy);
+  }
+  x = cx;
+  y = cy;
+}
+
+// Head served by block b of a (tile, head) grid, grouping the heads of one KV
+// group on one XCD: workgroups are dispatched round-robin over the 8 XCDs, so
+// blocks b, b+8, b+16, ... share an L2; when H is a multiple of 8 they get
+// heads x*(H/8) .. x*(H/8) + H/8 - 1 of XCD slot x = b % 8, i.e. whole groups.
+__device__ __forceinline__ int xcd_head(int r, int H) {
+  if (H % 8 != 0) return r;
+  return (r % 8) * (H / 8) + r / 8;
+}
+
+// ---------------------------------------------------------------------------
 // k_dq: D and dQ, one workgroup per (query tile of BR rows, head).
-// Wave w owns query block qb = w / DSPL (32 queries) and contraction half
-// ds = w % DSPL.  Key tiles of 32 rows of K and V are staged in LDS,
-// double-buffered through registers.
+// Wave w owns query block qb (32 queries); with the role split (DP > 128) two
+// waves share a block.  The key sweep streams 32-row K/V tiles through LDS:
+// one barrier per tile, and the next tile's loads are issued once this tile's
+// score products are under way.
 // ---------------------------------------------------------------------------
 template <int DP>
 __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
-  using G = Geo<DP>;
-  constexpr int QB = 4 / G::DSPL, BR = 32 * QB, BC = 32;
-  __shared__ __attribute__((aligned(16))) float sK[BC * G::LDR];
-  __shared__ __attribute__((aligned(16))) float sV[BC * G::LDR];
-  __shared__ __attribute__((aligned(16))) float sX[G::DSPL > 1 ? 4 * 32 * 64 : 4];
+  using PG = Pair<DP>;
+  constexpr int QB = PG::ROLE ? 2 : 4, BR = 32 * QB, BC = 32;
+  constexpr int LDR = DP + 4;
+  constexpr int TILE = PadTile<BC, DP>::FLOATS;
+  __shared__ __attribute__((aligned(1024))) float sKV[2][2 * TILE];
+  __shared__ __attribute__((aligned(16))) float sX[PG::ROLE ? 4 * 16 * 64 : 4];
   __shared__ float sD[4 * 32];
   __shared__ uint32_t sMin[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
-  const int ds = wave % G::DSPL, qb = wave / G::DSPL;
+  const int role = PG::ROLE ? (wave & 1) : 0;
+  const int qb = PG::ROLE ? (wave >> 1) : wave;
   const int S = a.S, H = a.H, d = a.d;
   const int g = H / a.KV;
   const int nqt = (S + BR - 1) / BR;
   const int qt = nqt - 1 - (int)(blockIdx.x / H);  // longest rows first
-  const int h = blockIdx.x % H, kvh = h / g;
+  const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
   const int i0 = qt * BR;
   const int q = i0 + qb * 32 + l32;
   const bool q_ok = q < S;
-  const int cb = ds * G::DW + hf * G::TH;
   const size_t qstride = (size_t)H * d, kstride = (size_t)a.KV * d;
   const float sc2 = a.scale * ATTN_LOG2E;
+  const float* Kh = a.K + (size_t)kvh * d;
+  const float* Vh = a.V + (size_t)kvh * d;
 
-  float qr[G::TH], gr[G::TH];
-  load_row<G::TH>(a.Q + (size_t)q * qstride + (size_t)h * d, cb, d, q_ok, qr);
-  load_row<G::TH>(a.dO + (size_t)q * qstride + (size_t)h * d, cb, d, q_ok, gr);
+  // B operands of the score blocks: this lane's query row, half-wave hf's columns
+  float qr[PG::TH], gr[PG::ROLE ? 1 : PG::TH];
+  if constexpr (PG::ROLE) {
+    load_row<PG::TH>((role ? a.dO : a.Q) + (size_t)q * qstride + (size_t)h * d, hf * PG::TH, d,
+                     q_ok, qr);
+  } else {
+    load_row<PG::TH>(a.Q + (size_t)q * qstride + (size_t)h * d, hf * PG::TH, d, q_ok, qr);
+    load_row<PG::TH>(a.dO + (size_t)q * qstride + (size_t)h * d, hf * PG::TH, d, q_ok, gr);
+    pin_agpr<PG::TH>(gr);
+  }
+  pin_agpr<PG::TH>(qr);
   const float lse2 = q_ok ? a.LSE[(size_t)q * H + h] * ATTN_LOG2E : 0.f;
   const uint32_t sq = (q_ok && a.seg) ? a.seg[q] : 0u;
 
-  // smallest document start of the tile bounds the key sweep
-  uint32_t mn = q_ok ? sq : 0xffffffffu;
+  // smallest document start of the tile bounds the key sweep; the largest one
+  // of the wave's block tells which key blocks the block sees entirely
+  uint32_t mn = q_ok ? sq : 0xffffffffu, mx = q_ok ? sq : 0u;
 #pragma unroll
-  for (int o = 16; o > 0; o >>= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+  for (int o = 16; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
   if (lane == 0) sMin[wave] = mn;
   __syncthreads();
   uint32_t tmin = sMin[0];
 #pragma unroll
   for (int w = 1; w < 4; ++w) tmin = min(tmin, sMin[w]);
-  if (h == 0 && ds == 0 && lane == 0 && i0 + qb * 32 < S) a.blk_min[(i0 >> 5) + qb] = mn;
+  const int qblk = (i0 >> 5) + qb;
+  if (h == 0 && role == 0 && lane == 0 && i0 + qb * 32 < S) {
+    a.blk_min[qblk] = mn;
+    a.blk_max[qblk] = mx;
+  }
+  const int q_first = i0 + qb * 32;
+  const bool rows_full = q_first + 31 < S;  // all 32 queries of the block exist
 
   const int last_q = min(i0 + BR, S) - 1;
   const int kt_lo = (int)(min(tmin, (uint32_t)last_q) / BC), kt_hi = last_q / BC;
 
-  f32x16 accA[G::NB], accB[G::NB];
+  f32x16 accA[PG::NB], accB[PG::NB];
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) { accA[nb] = zero16(); accB[nb] = zero16(); }
+  for (int nb = 0; nb < PG::NB; ++nb) { accA[nb] = zero16(); accB[nb] = zero16(); }
   float Dp = 0.f;
+  const int dcol0 = role * PG::DW;
 
-  TilePair<BC, DP> pf;
-  pf.fetch(a.K, a.V, kt_lo * BC, S, kstride, (size_t)kvh * d, d, tid);
-  pf.stash(sK, sV, tid);
-  __syncthreads();
-
+  dma_tile<BC, DP>(&sKV[0][0], Kh, kt_lo * BC, S, kstride, d, wave, lane);
+  dma_tile<BC, DP>(&sKV[0][TILE], Vh, kt_lo * BC, S, kstride, d, wave, lane);
+  int buf = 0;
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-    const bool more = kt < kt_hi;
-    if (more) pf.fetch(a.K, a.V, (kt + 1) * BC, S, kstride, (size_t)kvh * d, d, tid);
+    tile_barrier();  // tile kt resident; everyone done with tile kt-1
+    const float* sK = &sKV[buf][0];
+    const float* sV = &sKV[buf][TILE];
     const int j0 = kt * BC;
+    // every key of the tile visible to every query of the block: no masking
+    const bool full = rows_full && q_first >= j0 + 31 && mx <= (uint32_t)j0;
 
-    // S^T = K Q^T and dP^T = V dO^T for 32 keys x this wave's 32 queries
-    f32x16 st = zero16(), dpt = zero16();
-    const float* kp = sK + l32 * G::LDR + cb;
-    const float* vp = sV + l32 * G::LDR + cb;
+    // B operands of the accumulation below (independent of the scores): read
+    // them now so that the accumulation runs without LDS waits
+    float kv[16][PG::NB];
+    const float* kb0 = sK + (4 * hf) * LDR + dcol0 + l32;
 #pragma unroll
-    for (int t = 0; t < G::TH; t += 4) {
-      const float4 k4 = *reinterpret_cast<const float4*>(kp + t);
-      const float4 v4 = *reinterpret_cast<const float4*>(vp + t);
-      st = mfma32(k4.x, qr[t], st);
-      dpt = mfma32(v4.x, gr[t], dpt);
-      st = mfma32(k4.y, qr[t + 1], st);
-      dpt = mfma32(v4.y, gr[t + 1], dpt);
-      st = mfma32(k4.z, qr[t + 2], st);
-      dpt = mfma32(v4.z, gr[t + 2], dpt);
-      st = mfma32(k4.w, qr[t + 3], st);
-      dpt = mfma32(v4.w, gr[t + 3], dpt);
-    }
-    if constexpr (G::DSPL > 1) pair_exchange(sX, wave, lane, st, dpt);
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int nb = 0; nb < PG::NB; ++nb) kv[r][nb] = kb0[(8 * (r >> 2) + (r & 3)) * LDR + nb * 32];
 
-    // P and P*dP in place; this lane's query, key = crow(r, hf)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = j0 + crow(r, hf);
-      const bool vis = q_ok && key <= q && (uint32_t)key >= sq;
-      const float e = exp2f(fmaf(st[r], sc2, -lse2));
-      const float p = vis ? e : 0.f;
-      const float pdp = vis ? p * dpt[r] : 0.f;
-      Dp += pdp;
-      st[r] = p;
-      dpt[r] = pdp;
+    // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
+    f32x16 st, dpt;
+    if constexpr (PG::ROLE) {
+      const f32x16 mine = score_block<DP>(role ? sV : sK, l32, hf, qr);
+      const f32x16 other = pair_swap(sX, wave, lane, mine);
+      st = role ? other : mine;
+      dpt = role ? mine : other;
+    } else {
+      score_pair<DP>(sK, sV, l32, hf, qr, gr, st, dpt);
     }
-    // A += (P.dP) K,  B += P K over the 32 keys (register r = key crow(r, hf))
+    if (kt < kt_hi) {  // next tile into the other buffer (last read before this barrier)
+      dma_tile<BC, DP>(&sKV[buf ^ 1][0], Kh, (kt + 1) * BC, S, kstride, d, wave, lane);
+      dma_tile<BC, DP>(&sKV[buf ^ 1][TILE], Vh, (kt + 1) * BC, S, kstride, d, wave, lane);
+    }
+
+    // P and P*dP in place; this lane's query, key = j0 + crow(r, hf)
+    if (full) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float* krow = sK + crow(r, hf) * G::LDR + ds * G::DW + l32;
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(st[r], sc2, -lse2));
+        const float pdp = p * dpt[r];
+        Dp += pdp;
+        st[r] = p;
+        dpt[r] = pdp;
+      }
+    } else {
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) {
-        const float kb = krow[nb * 32];
-        accB[nb] = mfma32(st[r], kb, accB[nb]);
-        accA[nb] = mfma32(dpt[r], kb, accA[nb]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + crow(r, hf);
+        const bool vis = q_ok && key <= q && (uint32_t)key >= sq;
+        const float e = __builtin_amdgcn_exp2f(fmaf(st[r], sc2, -lse2));
+        const float p = vis ? e : 0.f;
+        const float pdp = vis ? p * dpt[r] : 0.f;
+        Dp += pdp;
+        st[r] = p;
+        dpt[r] = pdp;
       }
     }
-    __syncthreads();
-    if (more) {
-      pf.stash(sK, sV, tid);
-      __syncthreads();
+    // A += (P.dP) K,  B += P K over the 32 keys
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int nb = 0; nb < PG::NB; ++nb) {
+        accB[nb] = mfma32(st[r], kv[r][nb], accB[nb]);
+        accA[nb] = mfma32(dpt[r], kv[r][nb], accA[nb]);
+      }
     }
+    buf ^= 1;
   }
 
   // D of this lane's query: the two half-waves saw disjoint keys
   const float Dq = Dp + __shfl_xor(Dp, 32);
   if (hf == 0) sD[wave * 32 + l32] = Dq;
-  if (q_ok && hf == 0 && ds == 0) a.Dws[(size_t)q * H + h] = Dq;
+  if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * H + h] = Dq;
   __syncthreads();
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) {
-    const int col = ds * G::DW + nb * 32 + l32;
+  for (int nb = 0; nb < PG::NB; ++nb) {
+    const int col = dcol0 + nb * 32 + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = crow(r, hf);
@@ -302,151 +493,207 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // k_dkdv: dK and dV, one workgroup per (key tile of BC = 64 rows, KV head).
-// Wave w: key block kb (32 keys), query split qs, contraction half ds.  K and
-// V of the wave's keys live in registers; Q/dO tiles of BR rows of each head
-// of the group are staged in LDS.  Partial dK/dV of the QS query splits are
-// summed through LDS at the end; each (key, KV head) row has one writer.
+// Wave w: key block kb = w / 2 (32 keys), and either query block qs = w % 2
+// of each 64-row query tile (DP <= 128) or role w % 2 of the one 32-row query
+// block of a tile (DP > 128).  The K/V columns of the wave's keys stay in
+// registers.  The sweep visits, for query tiles from the last one down to the
+// tile holding the first key (so the workgroups resident on one XCD stream the
+// same tiles together), each head of the group, skipping tiles none of whose
+// queries can see these keys; Q/dO tiles are streamed through LDS with one
+// barrier per tile.  Partial dK/dV of the two query blocks are summed through
+// LDS at the end; each (key, KV head) row has a single writer.
 // ---------------------------------------------------------------------------
 template <int DP>
 __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
-  using G = Geo<DP>;
-  constexpr int KB = 2, QS = 2 / G::DSPL, BC = 32 * KB, BR = 32 * QS;
-  constexpr int TILE = BR * G::LDR;
-  static_assert(QS == 1 || 2 * TILE >= KB * 2 * G::NB * 16 * 64, "reduction buffer fits");
-  __shared__ __attribute__((aligned(16))) float sQG[2 * TILE];
-  __shared__ float sL[BR], sDD[BR];
-  __shared__ uint32_t sS[BR];
-  __shared__ __attribute__((aligned(16))) float sX[G::DSPL > 1 ? 4 * 32 * 64 : 4];
-  float* sQ = sQG;
-  float* sG = sQG + TILE;
+  using PG = Pair<DP>;
+  constexpr int KB = 2, QS = PG::ROLE ? 1 : 2, BC = 32 * KB, BR = 32 * QS;
+  constexpr int LDR = DP + 4;
+  constexpr int TILE = PadTile<BR, DP>::FLOATS;
+  static_assert(QS == 1 || 4 * TILE >= KB * 2 * PG::NB * 16 * 64, "reduction buffer fits");
+  __shared__ __attribute__((aligned(1024))) float sQG[2][2 * TILE];
+  __shared__ __attribute__((aligned(16))) float sRow[2][4][64];  // LSE, D, seg, unused
+  __shared__ __attribute__((aligned(16))) float sX[PG::ROLE ? 4 * 16 * 64 : 4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
-  const int ds = wave % G::DSPL, rest = wave / G::DSPL;
-  const int qs = rest % QS, kb = rest / QS;
+  const int kb = wave >> 1;
+  const int qs = PG::ROLE ? 0 : (wave & 1);
+  const int role = PG::ROLE ? (wave & 1) : 0;
   const int S = a.S, H = a.H, KV = a.KV, d = a.d;
   const int g = H / KV;
   const int kt = blockIdx.x / KV, kvh = blockIdx.x % KV;  // low key tiles (most queries) first
   const int j0 = kt * BC;
   const int key = j0 + kb * 32 + l32;
   const bool key_ok = key < S;
-  const int cb = ds * G::DW + hf * G::TH;
   const size_t qstride = (size_t)H * d, kstride = (size_t)KV * d;
   const float sc2 = a.scale * ATTN_LOG2E;
 
-  float kr[G::TH], vr[G::TH];
-  load_row<G::TH>(a.K + (size_t)key * kstride + (size_t)kvh * d, cb, d, key_ok, kr);
-  load_row<G::TH>(a.V + (size_t)key * kstride + (size_t)kvh * d, cb, d, key_ok, vr);
+  // B operands of the score blocks: this lane's key row, half-wave hf's columns
+  float kr[PG::TH], vr[PG::ROLE ? 1 : PG::TH];
+  if constexpr (PG::ROLE) {
+    load_row<PG::TH>((role ? a.V : a.K) + (size_t)key * kstride + (size_t)kvh * d, hf * PG::TH, d,
+                     key_ok, kr);
+  } else {
+    load_row<PG::TH>(a.K + (size_t)key * kstride + (size_t)kvh * d, hf * PG::TH, d, key_ok, kr);
+    load_row<PG::TH>(a.V + (size_t)key * kstride + (size_t)kvh * d, hf * PG::TH, d, key_ok, vr);
+    pin_agpr<PG::TH>(vr);
+  }
+  pin_agpr<PG::TH>(kr);
 
-  f32x16 accK[G::NB], accV[G::NB];
+  f32x16 accK[PG::NB], accV[PG::NB];
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) { accK[nb] = zero16(); accV[nb] = zero16(); }
+  for (int nb = 0; nb < PG::NB; ++nb) { accK[nb] = zero16(); accV[nb] = zero16(); }
 
   const int jlast = min(j0 + BC, S) - 1;
   const int nqt = (S + BR - 1) / BR, qt0 = j0 / BR;
   const int nblk = (S + 31) / 32;
+  const int dcol0 = role * PG::DW;
 
-  for (int hh = 0; hh < g; ++hh) {
-    const int h = kvh * g + hh;
-    for (int qt = qt0; qt < nqt; ++qt) {
-      const int i0 = qt * BR;
-      uint32_t mn = 0xffffffffu;
+  // query tile t can see a key of this tile unless every query's document
+  // starts after the tile's last key
+  auto visible_tile = [&](int t) {
+    uint32_t mn = 0xffffffffu;
 #pragma unroll
-      for (int b = 0; b < QS; ++b) {
-        const int bi = (i0 >> 5) + b;
-        if (bi < nblk) mn = min(mn, a.blk_min[bi]);
-      }
-      if (mn > (uint32_t)jlast) continue;  // no query of the tile sees these keys
+    for (int b = 0; b < QS; ++b) {
+      const int bi = t * QS + b;
+      if (bi < nblk) mn = min(mn, a.blk_min[bi]);
+    }
+    return mn <= (uint32_t)jlast;
+  };
+  auto prev_tile = [&](int t) {  // largest visible tile index <= t, or -1
+    for (; t >= qt0; --t)
+      if (visible_tile(t)) return t;
+    return -1;
+  };
+  auto issue = [&](int t, int hh, int b) {
+    const int i0 = t * BR, h = kvh * g + hh;
+    dma_tile<BR, DP>(&sQG[b][0], a.Q + (size_t)h * d, i0, S, qstride, d, wave, lane);
+    dma_tile<BR, DP>(&sQG[b][TILE], a.dO + (size_t)h * d, i0, S, qstride, d, wave, lane);
+    if (wave < 3) {
+      const int s = i0 + lane;
+      const bool ok = lane < BR && s < S && (wave != 2 || a.seg != nullptr);
+      const size_t sc = ok ? (size_t)s : 0;
+      const void* real = wave == 0 ? (const void*)(a.LSE + sc * H + h)
+                       : wave == 1 ? (const void*)(a.Dws + sc * H + h)
+                                   : (const void*)(a.seg + sc);
+      lds_dma4(ok ? real : (const void*)g_zero16, &sRow[b][wave][0]);
+    }
+  };
 
-      TilePair<BR, DP> t;
-      t.fetch(a.Q, a.dO, i0, S, qstride, (size_t)h * d, d, tid);
-      t.stash(sQ, sG, tid);
-      if (tid < BR) {
-        const int s = i0 + tid;
-        const bool ok = s < S;
-        sL[tid] = ok ? a.LSE[(size_t)s * H + h] * ATTN_LOG2E : 0.f;
-        sDD[tid] = ok ? a.Dws[(size_t)s * H + h] : 0.f;
-        sS[tid] = ok ? (a.seg ? a.seg[s] : 0u) : 0xffffffffu;
-      }
-      __syncthreads();
+  int qt = prev_tile(nqt - 1), hh = 0, buf = 0;
+  if (qt >= 0) issue(qt, 0, 0);
+  while (qt >= 0) {
+    int nqt_ = qt, nhh = hh + 1;
+    if (nhh == g) { nhh = 0; nqt_ = prev_tile(qt - 1); }
+    tile_barrier();  // this item resident; everyone done with the previous one
+    const float* sQ = &sQG[buf][0];
+    const float* sG = &sQG[buf][TILE];
+    const int i0 = qt * BR;
+    const int q_first = i0 + qs * 32, k_first = j0 + kb * 32;
+    // every query of the block sees every key of the wave: no masking
+    const bool full = q_first + 31 < S && q_first >= k_first + 31 &&
+                      a.blk_max[(i0 >> 5) + qs] <= (uint32_t)k_first;
 
-      // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys
-      f32x16 s = zero16(), dp = zero16();
-      const float* qp = sQ + (qs * 32 + l32) * G::LDR + cb;
-      const float* gp = sG + (qs * 32 + l32) * G::LDR + cb;
+    // dO operands of the dV accumulation below (independent of the scores)
+    float gv[16][PG::NB];
+    const int ob = (qs * 32 + 4 * hf) * LDR + dcol0 + l32;
 #pragma unroll
-      for (int t4 = 0; t4 < G::TH; t4 += 4) {
-        const float4 q4 = *reinterpret_cast<const float4*>(qp + t4);
-        const float4 g4 = *reinterpret_cast<const float4*>(gp + t4);
-        s = mfma32(q4.x, kr[t4], s);
-        dp = mfma32(g4.x, vr[t4], dp);
-        s = mfma32(q4.y, kr[t4 + 1], s);
-        dp = mfma32(g4.y, vr[t4 + 1], dp);
-        s = mfma32(q4.z, kr[t4 + 2], s);
-        dp = mfma32(g4.z, vr[t4 + 2], dp);
-        s = mfma32(q4.w, kr[t4 + 3], s);
-        dp = mfma32(g4.w, vr[t4 + 3], dp);
-      }
-      if constexpr (G::DSPL > 1) pair_exchange(sX, wave, lane, s, dp);
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int nb = 0; nb < PG::NB; ++nb) gv[r][nb] = sG[ob + (8 * (r >> 2) + (r & 3)) * LDR + nb * 32];
 
-      // P and dS in place; register r = query qs*32 + crow(r, hf), lane = key
+    // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys
+    f32x16 s, dp;
+    if constexpr (PG::ROLE) {
+      const f32x16 mine = score_block<DP>(role ? sG : sQ, l32, hf, kr);
+      const f32x16 other = pair_swap(sX, wave, lane, mine);
+      s = role ? other : mine;
+      dp = role ? mine : other;
+    } else {
+      score_pair<DP>(sQ, sG, qs * 32 + l32, hf, kr, vr, s, dp);
+    }
+    if (nqt_ >= 0) issue(nqt_, nhh, buf ^ 1);
+
+    // P and (dP - D) P in place (scale is applied to dK at the end);
+    // register r = query qs*32 + crow(r, hf), lane = key
+    const float* rowv = &sRow[buf][0][qs * 32 + 4 * hf];
+    if (full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int o = 8 * (r >> 2) + (r & 3);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -rowv[o] * ATTN_LOG2E));
+        dp[r] = p * (dp[r] - rowv[64 + o]);
+        s[r] = p;
+      }
+    } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = qs * 32 + crow(r, hf);
         const int qi = i0 + row;
-        const bool vis = key <= qi && sS[row] <= (uint32_t)key && qi < S;
-        const float e = exp2f(fmaf(s[r], sc2, -sL[row]));
+        const int o = 8 * (r >> 2) + (r & 3);
+        const float lse2 = rowv[o] * ATTN_LOG2E;
+        const float Dv = rowv[64 + o];
+        const uint32_t sg = __float_as_uint(rowv[128 + o]);
+        const bool vis = key <= qi && sg <= (uint32_t)key && qi < S;
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
         const float p = vis ? e : 0.f;
-        const float dsv = vis ? a.scale * p * (dp[r] - sDD[row]) : 0.f;
+        const float dsv = vis ? p * (dp[r] - Dv) : 0.f;
         s[r] = p;
         dp[r] = dsv;
       }
-      // dV += P^T dO,  dK += dS^T Q over the 32 queries
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = qs * 32 + crow(r, hf);
-        const float* grow = sG + row * G::LDR + ds * G::DW + l32;
-        const float* qrow = sQ + row * G::LDR + ds * G::DW + l32;
-#pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) {
-          accV[nb] = mfma32(s[r], grow[nb * 32], accV[nb]);
-          accK[nb] = mfma32(dp[r], qrow[nb * 32], accK[nb]);
-        }
-      }
-      __syncthreads();
     }
+    // Q operands of the dK accumulation, read while the dV products run
+    float qv[16][PG::NB];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int nb = 0; nb < PG::NB; ++nb) qv[r][nb] = sQ[ob + (8 * (r >> 2) + (r & 3)) * LDR + nb * 32];
+    // dV += P^T dO, then dK += (dS/scale)^T Q over the 32 queries
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int nb = 0; nb < PG::NB; ++nb) accV[nb] = mfma32(s[r], gv[r][nb], accV[nb]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+#pragma unroll
+      for (int nb = 0; nb < PG::NB; ++nb) accK[nb] = mfma32(dp[r], qv[r][nb], accK[nb]);
+    qt = nqt_;
+    hh = nhh;
+    buf ^= 1;
   }
 
   if constexpr (QS > 1) {
-    float* red = sQG + kb * (2 * G::NB * 16 * 64) + lane;
+    __syncthreads();  // every wave is done with the tiles: reuse them for the reduction
+    float* red = &sQG[0][0] + kb * (2 * PG::NB * 16 * 64) + lane;
     if (qs == 1) {
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
+      for (int nb = 0; nb < PG::NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          red[((0 * G::NB + nb) * 16 + r) * 64] = accK[nb][r];
-          red[((1 * G::NB + nb) * 16 + r) * 64] = accV[nb][r];
+          red[((0 * PG::NB + nb) * 16 + r) * 64] = accK[nb][r];
+          red[((1 * PG::NB + nb) * 16 + r) * 64] = accV[nb][r];
         }
     }
     __syncthreads();
     if (qs == 1) return;
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb)
+    for (int nb = 0; nb < PG::NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        accK[nb][r] += red[((0 * G::NB + nb) * 16 + r) * 64];
-        accV[nb][r] += red[((1 * G::NB + nb) * 16 + r) * 64];
+        accK[nb][r] += red[((0 * PG::NB + nb) * 16 + r) * 64];
+        accV[nb][r] += red[((1 * PG::NB + nb) * 16 + r) * 64];
       }
   }
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) {
-    const int col = ds * G::DW + nb * 32 + l32;
+  for (int nb = 0; nb < PG::NB; ++nb) {
+    const int col = dcol0 + nb * 32 + l32;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = j0 + kb * 32 + crow(r, hf);
       if (row < S && col < d) {
         const size_t off = (size_t)row * kstride + (size_t)kvh * d + col;
-        a.dK[off] += accK[nb][r];
+        a.dK[off] += a.scale * accK[nb][r];
         a.dV[off] += accV[nb][r];
       }
     }
@@ -673,8 +920,7 @@ static attn_status_t hip_check(hipError_t e, const char* what) {
 
 template <int DP>
 static attn_status_t launch_bwd(const BwdArgs& a, hipStream_t st) {
-  constexpr int DSPL = Geo<DP>::DSPL;
-  const int BRq = 32 * (4 / DSPL);
+  const int BRq = Pair<DP>::ROLE ? 64 : 128;
   const int nqt = (a.S + BRq - 1) / BRq;
   attn_status_t rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
@@ -715,7 +961,7 @@ extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V
   const size_t nD = (size_t)seq_len * n_heads;
   const size_t nblk = ((size_t)seq_len + 31) / 32;
   void* ws = nullptr;
-  rc = hip_check(hipMallocAsync(&ws, nD * sizeof(float) + nblk * sizeof(uint32_t), st),
+  rc = hip_check(hipMallocAsync(&ws, nD * sizeof(float) + 2 * nblk * sizeof(uint32_t), st),
                  "hipMallocAsync(workspace)");
   if (rc != ATTN_OK) return rc;
 
@@ -724,6 +970,7 @@ extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.Dws = static_cast<float*>(ws);
   a.blk_min = reinterpret_cast<uint32_t*>(static_cast<float*>(ws) + nD);
+  a.blk_max = a.blk_min + nblk;
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim; a.scale = scale;
 
   switch (padded_dim(head_dim)) {
