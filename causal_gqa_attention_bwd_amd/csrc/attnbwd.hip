@@ -179,25 +179,33 @@ __device__ __forceinline__ void pair_exchange(float* sX, int wave, int lane, f32
 // Streaming tiles into LDS.
 //
 // The backward kernels stage row tiles (K/V rows in k_dq, Q/dO rows in
-// k_dkdv) with direct global->LDS loads (global_load_lds_dwordx4: each lane's
-// 16 bytes land at the wave's LDS base + 16 * lane), double-buffered so the
-// next tile streams in while the current one is multiplied.  A tile is kept
-// row-major with rows padded to DP + 4 floats, so that the b128 reads of 32
-// rows at one column and the b32 reads of 32 columns of one row hit distinct
-// banks, and so that every LDS address in the hot loops is one per-lane base
+// k_dkdv) with direct buffer->LDS loads (buffer_load_dwordx4 ... lds: each
+// lane's 16 bytes land at the wave's LDS base + 16 * lane), double-buffered
+// so the next tile streams in while the current one is multiplied.  A tile is
+// kept row-major with rows padded to DP + 4 floats, so that the b128 reads of
+// 32 rows at one column and the b32 reads of 32 columns of one row hit
+// distinct banks, and every LDS address in the hot loops is one per-lane base
 // plus a compile-time offset.  Each 1 KiB chunk of the padded tile is one
-// wave-wide load; lanes that land on a pad granule, past the tile, past the
-// sequence or past head_dim load 16 zero bytes from g_zero16 instead.
+// wave-wide load.  Zero fill is left to the buffer range check: the buffer
+// resource of a tile ends with the tile's last valid row, and lanes that land
+// on a pad granule or past head_dim carry an offset beyond any range, so all
+// of them deposit zeros without touching memory.
 // ---------------------------------------------------------------------------
-__device__ __attribute__((aligned(16))) float g_zero16[4] = {0.f, 0.f, 0.f, 0.f};
+#define ATTN_BUF_OOB 0x80000000u        // beyond every buffer range used here
+#define ATTN_BUF_WORD3 0x00020000u      // raw buffer, 32-bit data format
 
-__device__ __forceinline__ void lds_dma16(const float* src, float* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                           (int)ATTN_BUF_WORD3);
 }
-__device__ __forceinline__ void lds_dma4(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                   (void __attribute__((address_space(3)))*)lds_dst, 4, 0, 0);
+
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, float* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 16,
+                                           voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 4,
+                                           voff, 0, 0, 0);
 }
 
 // Padded ROWS x DP tile filled by 1 KiB chunks.
@@ -210,25 +218,37 @@ struct PadTile {
   static constexpr int CPW = (NCH + 3) / 4;          // loads per wave (some waves one fewer)
 };
 
-// Rows [r0, r0 + ROWS) of a row-major matrix (rows `stride` floats apart,
-// head_dim = d valid columns starting at `base`) into the padded LDS tile
-// `lds`.  wave_u must be wave-uniform.
+// Per-lane byte offsets, relative to a tile's first row, of the granules this
+// lane loads for a padded ROWS x DP tile of a matrix whose rows are `stride`
+// floats apart with d valid columns.  Computed once per kernel.
 template <int ROWS, int DP>
-__device__ __forceinline__ void dma_tile(float* lds, const float* base, int r0, int S,
-                                         size_t stride, int d, int wave_u, int lane) {
+struct TileLoader {
   using T = PadTile<ROWS, DP>;
+  uint32_t off[T::CPW];
+
+  __device__ __forceinline__ void init(size_t stride, int d, int wave_u, int lane) {
 #pragma unroll
-  for (int i = 0; i < T::CPW; ++i) {
-    const int chunk = wave_u + 4 * i;
-    if (chunk < T::NCH) {
-      const int p = chunk * 64 + lane;  // granule of the padded tile
+    for (int i = 0; i < T::CPW; ++i) {
+      const int p = (wave_u + 4 * i) * 64 + lane;  // granule of the padded tile
       const int row = p / T::GPR, g4 = p % T::GPR;
-      const bool ok = row < ROWS && g4 < DP / 4 && r0 + row < S && 4 * g4 < d;
-      const float* real = base + (size_t)(ok ? r0 + row : 0) * stride + 4 * (ok ? g4 : 0);
-      lds_dma16(ok ? real : g_zero16, lds + chunk * 256);
+      const bool ok = row < ROWS && g4 < DP / 4 && 4 * g4 < d;
+      off[i] = ok ? (uint32_t)(((size_t)row * stride + 4 * g4) * 4) : ATTN_BUF_OOB;
     }
   }
-}
+  // Rows [r0, min(r0 + ROWS, S)) of the matrix starting at `base` (already at
+  // the head's first column) into the padded LDS tile `lds`.
+  __device__ __forceinline__ void load(float* lds, const float* base, int r0, int S, size_t stride,
+                                       int d, int wave_u) const {
+    const int rows = min(S - r0, ROWS);
+    const uint32_t nbytes = (uint32_t)(((size_t)(rows - 1) * stride + d) * 4);
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(base + (size_t)r0 * stride, nbytes);
+#pragma unroll
+    for (int i = 0; i < T::CPW; ++i) {
+      const int chunk = wave_u + 4 * i;
+      if (4 * (i + 1) <= T::NCH || chunk < T::NCH) lds_load16(r, off[i], lds + chunk * 256);
+    }
+  }
+};
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
 // then s_barrier.  Unlike __syncthreads it does not wait for outstanding global
@@ -401,8 +421,10 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   float Dp = 0.f;
   const int dcol0 = role * PG::DW;
 
-  dma_tile<BC, DP>(&sKV[0][0], Kh, kt_lo * BC, S, kstride, d, wave, lane);
-  dma_tile<BC, DP>(&sKV[0][TILE], Vh, kt_lo * BC, S, kstride, d, wave, lane);
+  TileLoader<BC, DP> ld;
+  ld.init(kstride, d, wave, lane);
+  ld.load(&sKV[0][0], Kh, kt_lo * BC, S, kstride, d, wave);
+  ld.load(&sKV[0][TILE], Vh, kt_lo * BC, S, kstride, d, wave);
   int buf = 0;
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     tile_barrier();  // tile kt resident; everyone done with tile kt-1
@@ -432,8 +454,8 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       score_pair<DP>(sK, sV, l32, hf, qr, gr, st, dpt);
     }
     if (kt < kt_hi) {  // next tile into the other buffer (last read before this barrier)
-      dma_tile<BC, DP>(&sKV[buf ^ 1][0], Kh, (kt + 1) * BC, S, kstride, d, wave, lane);
-      dma_tile<BC, DP>(&sKV[buf ^ 1][TILE], Vh, (kt + 1) * BC, S, kstride, d, wave, lane);
+      ld.load(&sKV[buf ^ 1][0], Kh, (kt + 1) * BC, S, kstride, d, wave);
+      ld.load(&sKV[buf ^ 1][TILE], Vh, (kt + 1) * BC, S, kstride, d, wave);
     }
 
     // P and P*dP in place; this lane's query, key = j0 + crow(r, hf)
@@ -566,34 +588,47 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
       if (visible_tile(t)) return t;
     return -1;
   };
+  TileLoader<BR, DP> ld;
+  ld.init(qstride, d, wave, lane);
+  // per-row values of a tile: wave 0 LSE, wave 1 D (rows H floats apart),
+  // wave 2 seg; lanes past the tile read nothing
+  const uint32_t row_off = lane < BR ? (uint32_t)(lane * (wave == 2 ? 4 : 4 * H)) : ATTN_BUF_OOB;
   auto issue = [&](int t, int hh, int b) {
     const int i0 = t * BR, h = kvh * g + hh;
-    dma_tile<BR, DP>(&sQG[b][0], a.Q + (size_t)h * d, i0, S, qstride, d, wave, lane);
-    dma_tile<BR, DP>(&sQG[b][TILE], a.dO + (size_t)h * d, i0, S, qstride, d, wave, lane);
-    if (wave < 3) {
-      const int s = i0 + lane;
-      const bool ok = lane < BR && s < S && (wave != 2 || a.seg != nullptr);
-      const size_t sc = ok ? (size_t)s : 0;
-      const void* real = wave == 0 ? (const void*)(a.LSE + sc * H + h)
-                       : wave == 1 ? (const void*)(a.Dws + sc * H + h)
-                                   : (const void*)(a.seg + sc);
-      lds_dma4(ok ? real : (const void*)g_zero16, &sRow[b][wave][0]);
+    ld.load(&sQG[b][0], a.Q + (size_t)h * d, i0, S, qstride, d, wave);
+    ld.load(&sQG[b][TILE], a.dO + (size_t)h * d, i0, S, qstride, d, wave);
+    const int rows = min(S - i0, BR);
+    if (wave < 2) {
+      const float* base = (wave == 0 ? a.LSE : a.Dws) + (size_t)i0 * H + h;
+      lds_load4(buf_rsrc(base, (uint32_t)(((rows - 1) * (size_t)H + 1) * 4)), row_off, &sRow[b][wave][0]);
+    } else if (wave == 2) {
+      const uint32_t* base = a.seg ? a.seg + i0 : nullptr;
+      lds_load4(buf_rsrc(base, a.seg ? (uint32_t)(rows * 4) : 0u), row_off, &sRow[b][2][0]);
     }
+  };
+  auto next_item = [&](int t, int hx, int& nt, int& nh) {  // item after (t, hx), nt = -1 at the end
+    nt = t;
+    nh = hx + 1;
+    if (nh == g) { nh = 0; nt = prev_tile(t - 1); }
   };
 
   int qt = prev_tile(nqt - 1), hh = 0, buf = 0;
-  if (qt >= 0) issue(qt, 0, 0);
+  int nqt_ = -1, nhh = 0;
+  uint32_t bmax = 0;
+  if (qt >= 0) {
+    issue(qt, 0, 0);
+    next_item(qt, 0, nqt_, nhh);
+    const int bi = qt * QS + qs;  // may not exist in a partial last tile
+    bmax = bi < nblk ? a.blk_max[bi] : 0u;
+  }
   while (qt >= 0) {
-    int nqt_ = qt, nhh = hh + 1;
-    if (nhh == g) { nhh = 0; nqt_ = prev_tile(qt - 1); }
     tile_barrier();  // this item resident; everyone done with the previous one
     const float* sQ = &sQG[buf][0];
     const float* sG = &sQG[buf][TILE];
     const int i0 = qt * BR;
     const int q_first = i0 + qs * 32, k_first = j0 + kb * 32;
     // every query of the block sees every key of the wave: no masking
-    const bool full = q_first + 31 < S && q_first >= k_first + 31 &&
-                      a.blk_max[(i0 >> 5) + qs] <= (uint32_t)k_first;
+    const bool full = q_first + 31 < S && q_first >= k_first + 31 && bmax <= (uint32_t)k_first;
 
     // dO operands of the dV accumulation below (independent of the scores)
     float gv[16][PG::NB];
@@ -613,7 +648,16 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     } else {
       score_pair<DP>(sQ, sG, qs * 32 + l32, hf, kr, vr, s, dp);
     }
-    if (nqt_ >= 0) issue(nqt_, nhh, buf ^ 1);
+    // next item into the other buffer; then look one item further ahead (the
+    // scalar loads this needs complete under the products below)
+    int nnqt = -1, nnhh = 0;
+    uint32_t nbmax = 0;
+    if (nqt_ >= 0) {
+      issue(nqt_, nhh, buf ^ 1);
+      next_item(nqt_, nhh, nnqt, nnhh);
+      const int bi = nqt_ * QS + qs;
+      nbmax = bi < nblk ? a.blk_max[bi] : 0u;
+    }
 
     // P and (dP - D) P in place (scale is applied to dK at the end);
     // register r = query qs*32 + crow(r, hf), lane = key
@@ -660,6 +704,9 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
       for (int nb = 0; nb < PG::NB; ++nb) accK[nb] = mfma32(dp[r], qv[r][nb], accK[nb]);
     qt = nqt_;
     hh = nhh;
+    nqt_ = nnqt;
+    nhh = nnhh;
+    bmax = nbmax;
     buf ^= 1;
   }
 
@@ -910,6 +957,9 @@ static attn_status_t check_common(int S, int H, int KV, int d, float scale) {
     return fail(ATTN_ERR_UNSUPPORTED, "head_dim = %d (supported: multiples of 16 in [16, 256])", d);
   if ((long long)S * H >= (1ll << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "seq_len * n_heads = %lld is too large", (long long)S * H);
+  // byte offsets inside one staged 64-row tile must fit the 32-bit buffer offsets
+  if ((long long)H * d >= (1ll << 23))
+    return fail(ATTN_ERR_UNSUPPORTED, "n_heads * head_dim = %lld is too large", (long long)H * d);
   return ATTN_OK;
 }
 

@@ -61,7 +61,7 @@ typedef enum {
      scale not finite */
   ATTN_ERR_INVALID_ARG = 1,
   /* head_dim not a multiple of 16 in [16, 256]; a pointer not 16-byte
-     aligned; sizes whose element offsets exceed 2^31 - 1 */
+     aligned; seq_len * n_heads >= 2^31; n_heads * head_dim >= 2^23 */
   ATTN_ERR_UNSUPPORTED = 2,
   /* a HIP runtime call or kernel launch failed (text: attn_last_error) */
   ATTN_ERR_HIP = 3
@@ -75,8 +75,8 @@ typedef enum {
  * dV accumulate likewise).  Zero them before the first accumulation.
  *
  * Internally the call takes one stream-ordered workspace of
- * seq_len * n_heads * 4 bytes (the row term D) plus seq_len / 8 bytes of tile
- * metadata, allocated with hipMallocAsync on `stream` and released with
+ * seq_len * n_heads * 4 bytes (the row term D) plus 8 bytes per 32 rows of
+ * tile metadata, allocated with hipMallocAsync on `stream` and released with
  * hipFreeAsync on `stream` before returning.
  *
  * seq_len == 0 returns ATTN_OK and enqueues nothing.
