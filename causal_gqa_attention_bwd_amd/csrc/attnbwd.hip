@@ -84,7 +84,7 @@ struct Geo {
 struct BwdArgs {
   const float *Q, *K, *V, *dO, *LSE;
   const uint32_t* seg;  // NULL = all zeros
-  float *dQ, *dK, *dV;
+  float *dQ, *dK, *dV;  // never overlap each other or an input
   float* Dws;            // [S, H] row term, written by k_dq, read by k_dkdv
   uint32_t* blk_min;     // [ceil(S/32)] min seg per 32-row query block
   uint32_t* blk_max;     // [ceil(S/32)] max seg per 32-row query block
@@ -192,20 +192,54 @@ __device__ __forceinline__ void pair_exchange(float* sX, int wave, int lane, f32
 // of them deposit zeros without touching memory.
 // ---------------------------------------------------------------------------
 #define ATTN_BUF_OOB 0x80000000u        // beyond every buffer range used here
-#define ATTN_BUF_WORD3 0x00020000u      // raw buffer, 32-bit data format
+#define ATTN_BUF_WORD3 0x00020000       // raw buffer, 32-bit data format
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t nbytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
-                                           (int)ATTN_BUF_WORD3);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource of `nbytes` bytes at `base` (nbytes = 0: every load reads zeros).
+__device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t p = (uint64_t)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
+  r.w = ATTN_BUF_WORD3;
+  return r;
 }
 
-__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, float* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 16,
-                                           voff, 0, 0, 0);
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
-__device__ __forceinline__ void lds_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)lds_dst, 4,
-                                           voff, 0, 0, 0);
+
+// Direct buffer->LDS loads (16 or 4 bytes per lane; lane i's data lands at
+// lds + i * size).  Issued from inline assembly so that the compiler does not
+// treat every later LDS read as possibly overlapping these writes and wait for
+// them: ordering is explicit instead -- every reader of a tile passes a
+// tile_barrier (s_waitcnt vmcnt(0) + s_barrier) issued after the tile's loads,
+// and no buffer is refilled before all waves have passed a barrier after
+// their last read of it.  M0 carries the LDS address and is restored.
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, const void* lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr(lds))), "v"(voff), "s"(r)
+      : "memory");
+}
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, const void* lds) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr(lds))), "v"(voff), "s"(r)
+      : "memory");
 }
 
 // Padded ROWS x DP tile filled by 1 KiB chunks.
@@ -235,18 +269,23 @@ struct TileLoader {
       off[i] = ok ? (uint32_t)(((size_t)row * stride + 4 * g4) * 4) : ATTN_BUF_OOB;
     }
   }
-  // Rows [r0, min(r0 + ROWS, S)) of the matrix starting at `base` (already at
-  // the head's first column) into the padded LDS tile `lds`.
-  __device__ __forceinline__ void load(float* lds, const float* base, int r0, int S, size_t stride,
-                                       int d, int wave_u) const {
-    const int rows = min(S - r0, ROWS);
-    const uint32_t nbytes = (uint32_t)(((size_t)(rows - 1) * stride + d) * 4);
-    const __amdgpu_buffer_rsrc_t r = buf_rsrc(base + (size_t)r0 * stride, nbytes);
+  // Buffer resource of rows [r0, min(r0 + ROWS, S)) of the matrix starting at
+  // `base` (already at the head's first column); no rows (live = false) gives
+  // an empty range.
+  __device__ __forceinline__ i32x4 rsrc(const float* base, int r0, int S, size_t stride, int d,
+                                         bool live) const {
+    const int rows = live ? min(S - r0, ROWS) : 0;
+    const uint32_t nbytes = rows > 0 ? (uint32_t)(((size_t)(rows - 1) * stride + d) * 4) : 0u;
+    return buf_rsrc(live ? base + (size_t)r0 * stride : base, nbytes);
+  }
+  // The i-th of this wave's loads of a tile into the padded LDS tile `lds`.
+  __device__ __forceinline__ void load(int i, const i32x4& r, float* lds, int wave_u) const {
+    const int chunk = wave_u + 4 * i;
+    if (4 * (i + 1) <= T::NCH || chunk < T::NCH) dma16(r, off[i], lds + chunk * 256);
+  }
+  __device__ __forceinline__ void load_all(const i32x4& r, float* lds, int wave_u) const {
 #pragma unroll
-    for (int i = 0; i < T::CPW; ++i) {
-      const int chunk = wave_u + 4 * i;
-      if (4 * (i + 1) <= T::NCH || chunk < T::NCH) lds_load16(r, off[i], lds + chunk * 256);
-    }
+    for (int i = 0; i < T::CPW; ++i) load(i, r, lds, wave_u);
   }
 };
 
@@ -289,11 +328,18 @@ __device__ __forceinline__ f32x16 pair_swap(float* sX, int wave, int lane, const
   return other;
 }
 
+// No side work inside a score loop.
+struct NoSide {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // 32x32 score block over DP columns: acc = A_lds[row a_row][:] . B_reg, where
 // half-wave hf contracts columns [hf*TH, hf*TH + TH).  Two accumulation
-// chains, summed at the end.
-template <int DP>
-__device__ __forceinline__ f32x16 score_block(const float* tile, int a_row, int hf, const float* breg) {
+// chains, summed at the end.  side(step) is called once per 4-column step
+// (TH/4 steps) so that other instructions issue between the products.
+template <int DP, class Side>
+__device__ __forceinline__ f32x16 score_block(const float* tile, int a_row, int hf, const float* breg,
+                                              const Side& side) {
   constexpr int TH = Pair<DP>::TH, LDR = DP + 4;
   const float* ap = tile + a_row * LDR + hf * TH;
   f32x16 c0 = zero16(), c1 = zero16();
@@ -302,6 +348,7 @@ __device__ __forceinline__ f32x16 score_block(const float* tile, int a_row, int 
     const float4 a4 = *reinterpret_cast<const float4*>(ap + t);
     c0 = mfma32(a4.x, breg[t], c0);
     c1 = mfma32(a4.y, breg[t + 1], c1);
+    side(t / 4);
     c0 = mfma32(a4.z, breg[t + 2], c0);
     c1 = mfma32(a4.w, breg[t + 3], c1);
   }
@@ -309,9 +356,10 @@ __device__ __forceinline__ f32x16 score_block(const float* tile, int a_row, int 
 }
 
 // Two independent 32x32 score blocks sharing the LDS row (S and dP of one block).
-template <int DP>
+template <int DP, class Side>
 __device__ __forceinline__ void score_pair(const float* tA, const float* tB, int a_row, int hf,
-                                           const float* rA, const float* rB, f32x16& x, f32x16& y) {
+                                           const float* rA, const float* rB, f32x16& x, f32x16& y,
+                                           const Side& side) {
   constexpr int TH = Pair<DP>::TH, LDR = DP + 4;
   const int o0 = a_row * LDR + hf * TH;
   f32x16 cx = zero16(), cy = zero16();
@@ -323,6 +371,7 @@ __device__ __forceinline__ void score_pair(const float* tA, const float* tB, int
     cy = mfma32(b4.x, rB[t], cy);
     cx = mfma32(a4.y, rA[t + 1], cx);
     cy = mfma32(b4.y, rB[t + 1], cy);
+    side(t / 4);
     cx = mfma32(a4.z, rA[t + 2], cx);
     cy = mfma32(b4.z, rB[t + 2], cy);
     cx = mfma32(a4.w, rA[t + 3], cx);
@@ -331,6 +380,18 @@ __device__ __forceinline__ void score_pair(const float* tA, const float* tB, int
   x = cx;
   y = cy;
 }
+
+// Spreads N loads over the STEPS steps of a score loop: step t issues loads
+// [t*N/STEPS, (t+1)*N/STEPS).
+template <int N, int STEPS, class Issue>
+struct SpreadLoads {
+  const Issue& issue;
+  __device__ __forceinline__ void operator()(int t) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (j * STEPS >= t * N && j * STEPS < (t + 1) * N) issue(j);
+  }
+};
 
 // Head served by block b of a (tile, head) grid, grouping the heads of one KV
 // group on one XCD: workgroups are dispatched round-robin over the 8 XCDs, so
@@ -423,16 +484,33 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 
   TileLoader<BC, DP> ld;
   ld.init(kstride, d, wave, lane);
-  ld.load(&sKV[0][0], Kh, kt_lo * BC, S, kstride, d, wave);
-  ld.load(&sKV[0][TILE], Vh, kt_lo * BC, S, kstride, d, wave);
+  {
+    const i32x4 rk = ld.rsrc(Kh, kt_lo * BC, S, kstride, d, true);
+    const i32x4 rv = ld.rsrc(Vh, kt_lo * BC, S, kstride, d, true);
+    ld.load_all(rk, &sKV[0][0], wave);
+    ld.load_all(rv, &sKV[0][TILE], wave);
+  }
+  constexpr int NLOAD = 2 * PadTile<BC, DP>::CPW;  // loads per wave per tile
   int buf = 0;
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     tile_barrier();  // tile kt resident; everyone done with tile kt-1
     const float* sK = &sKV[buf][0];
     const float* sV = &sKV[buf][TILE];
+    float* nxt = &sKV[buf ^ 1][0];
     const int j0 = kt * BC;
     // every key of the tile visible to every query of the block: no masking
     const bool full = rows_full && q_first >= j0 + 31 && mx <= (uint32_t)j0;
+
+    // loads of the next tile into the other buffer (empty ranges after the
+    // last tile), issued between the score products below
+    const bool more = kt < kt_hi;
+    const i32x4 rk = ld.rsrc(Kh, (kt + 1) * BC, S, kstride, d, more);
+    const i32x4 rv = ld.rsrc(Vh, (kt + 1) * BC, S, kstride, d, more);
+    auto issue = [&](int j) {
+      if (j < NLOAD / 2) ld.load(j, rk, nxt, wave);
+      else ld.load(j - NLOAD / 2, rv, nxt + TILE, wave);
+    };
+    const SpreadLoads<NLOAD, PG::TH / 4, decltype(issue)> spread{issue};
 
     // B operands of the accumulation below (independent of the scores): read
     // them now so that the accumulation runs without LDS waits
@@ -446,16 +524,12 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
     f32x16 st, dpt;
     if constexpr (PG::ROLE) {
-      const f32x16 mine = score_block<DP>(role ? sV : sK, l32, hf, qr);
+      const f32x16 mine = score_block<DP>(role ? sV : sK, l32, hf, qr, spread);
       const f32x16 other = pair_swap(sX, wave, lane, mine);
       st = role ? other : mine;
       dpt = role ? mine : other;
     } else {
-      score_pair<DP>(sK, sV, l32, hf, qr, gr, st, dpt);
-    }
-    if (kt < kt_hi) {  // next tile into the other buffer (last read before this barrier)
-      ld.load(&sKV[buf ^ 1][0], Kh, (kt + 1) * BC, S, kstride, d, wave);
-      ld.load(&sKV[buf ^ 1][TILE], Vh, (kt + 1) * BC, S, kstride, d, wave);
+      score_pair<DP>(sK, sV, l32, hf, qr, gr, st, dpt, spread);
     }
 
     // P and P*dP in place; this lane's query, key = j0 + crow(r, hf)
@@ -492,12 +566,25 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     }
     buf ^= 1;
   }
+  tile_barrier();  // the last (empty) loads have landed before the LDS is reused or released
 
   // D of this lane's query: the two half-waves saw disjoint keys
   const float Dq = Dp + __shfl_xor(Dp, 32);
   if (hf == 0) sD[wave * 32 + l32] = Dq;
   if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * H + h] = Dq;
   __syncthreads();
+  // dQ += scale * (A - D B): all old values are read first, then all written
+  float* __restrict__ dQh = a.dQ + (size_t)h * d;
+  float old[PG::NB][16];
+#pragma unroll
+  for (int nb = 0; nb < PG::NB; ++nb) {
+    const int col = dcol0 + nb * 32 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = i0 + qb * 32 + crow(r, hf);
+      old[nb][r] = (row < S && col < d) ? dQh[(size_t)row * qstride + col] : 0.f;
+    }
+  }
 #pragma unroll
   for (int nb = 0; nb < PG::NB; ++nb) {
     const int col = dcol0 + nb * 32 + l32;
@@ -505,10 +592,9 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int m = crow(r, hf);
       const int row = i0 + qb * 32 + m;
-      if (row < S && col < d) {
-        float* o = a.dQ + (size_t)row * qstride + (size_t)h * d + col;
-        *o += a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
-      }
+      if (row < S && col < d)
+        dQh[(size_t)row * qstride + col] =
+            old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
     }
   }
 }
@@ -590,22 +676,27 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   };
   TileLoader<BR, DP> ld;
   ld.init(qstride, d, wave, lane);
-  // per-row values of a tile: wave 0 LSE, wave 1 D (rows H floats apart),
-  // wave 2 seg; lanes past the tile read nothing
+  // per-row values of a tile, one wave-wide 4-byte load per wave: wave 0 LSE,
+  // wave 1 D (rows H floats apart), wave 2 seg, wave 3 nothing (empty range
+  // into a spare slot); lanes past the tile read nothing
   const uint32_t row_off = lane < BR ? (uint32_t)(lane * (wave == 2 ? 4 : 4 * H)) : ATTN_BUF_OOB;
-  auto issue = [&](int t, int hh, int b) {
+  auto row_rsrc = [&](int t, int hh, bool live) {
     const int i0 = t * BR, h = kvh * g + hh;
-    ld.load(&sQG[b][0], a.Q + (size_t)h * d, i0, S, qstride, d, wave);
-    ld.load(&sQG[b][TILE], a.dO + (size_t)h * d, i0, S, qstride, d, wave);
-    const int rows = min(S - i0, BR);
-    if (wave < 2) {
-      const float* base = (wave == 0 ? a.LSE : a.Dws) + (size_t)i0 * H + h;
-      lds_load4(buf_rsrc(base, (uint32_t)(((rows - 1) * (size_t)H + 1) * 4)), row_off, &sRow[b][wave][0]);
-    } else if (wave == 2) {
-      const uint32_t* base = a.seg ? a.seg + i0 : nullptr;
-      lds_load4(buf_rsrc(base, a.seg ? (uint32_t)(rows * 4) : 0u), row_off, &sRow[b][2][0]);
+    const int rows = live ? min(S - i0, BR) : 0;
+    const void* base = a.LSE;
+    uint32_t nbytes = 0;
+    if (rows > 0) {
+      if (wave == 0 || wave == 1) {
+        base = (wave == 0 ? a.LSE : a.Dws) + (size_t)i0 * H + h;
+        nbytes = (uint32_t)(((rows - 1) * (size_t)H + 1) * 4);
+      } else if (wave == 2 && a.seg) {
+        base = a.seg + i0;
+        nbytes = (uint32_t)(rows * 4);
+      }
     }
+    return buf_rsrc(base, nbytes);
   };
+  constexpr int NLOAD = 2 * PadTile<BR, DP>::CPW + 1;  // loads per wave per item
   auto next_item = [&](int t, int hx, int& nt, int& nh) {  // item after (t, hx), nt = -1 at the end
     nt = t;
     nh = hx + 1;
@@ -616,7 +707,11 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   int nqt_ = -1, nhh = 0;
   uint32_t bmax = 0;
   if (qt >= 0) {
-    issue(qt, 0, 0);
+    const i32x4 rq = ld.rsrc(a.Q + (size_t)(kvh * g) * d, qt * BR, S, qstride, d, true);
+    const i32x4 rg = ld.rsrc(a.dO + (size_t)(kvh * g) * d, qt * BR, S, qstride, d, true);
+    ld.load_all(rq, &sQG[0][0], wave);
+    ld.load_all(rg, &sQG[0][TILE], wave);
+    dma4(row_rsrc(qt, 0, true), row_off, &sRow[0][wave][0]);
     next_item(qt, 0, nqt_, nhh);
     const int bi = qt * QS + qs;  // may not exist in a partial last tile
     bmax = bi < nblk ? a.blk_max[bi] : 0u;
@@ -630,6 +725,23 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     // every query of the block sees every key of the wave: no masking
     const bool full = q_first + 31 < S && q_first >= k_first + 31 && bmax <= (uint32_t)k_first;
 
+    // loads of the next item into the other buffer (empty ranges after the
+    // last item), issued between the score products below
+    const bool more = nqt_ >= 0;
+    const int nh_ = kvh * g + (more ? nhh : 0);
+    const i32x4 rq = ld.rsrc(a.Q + (size_t)nh_ * d, nqt_ * BR, S, qstride, d, more);
+    const i32x4 rg = ld.rsrc(a.dO + (size_t)nh_ * d, nqt_ * BR, S, qstride, d, more);
+    const i32x4 rr = row_rsrc(nqt_, nhh, more);
+    float* nxt = &sQG[buf ^ 1][0];
+    float* nrow = &sRow[buf ^ 1][wave][0];
+    auto issue = [&](int j) {
+      constexpr int C = PadTile<BR, DP>::CPW;
+      if (j < C) ld.load(j, rq, nxt, wave);
+      else if (j < 2 * C) ld.load(j - C, rg, nxt + TILE, wave);
+      else dma4(rr, row_off, nrow);
+    };
+    const SpreadLoads<NLOAD, PG::TH / 4, decltype(issue)> spread{issue};
+
     // dO operands of the dV accumulation below (independent of the scores)
     float gv[16][PG::NB];
     const int ob = (qs * 32 + 4 * hf) * LDR + dcol0 + l32;
@@ -641,19 +753,18 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys
     f32x16 s, dp;
     if constexpr (PG::ROLE) {
-      const f32x16 mine = score_block<DP>(role ? sG : sQ, l32, hf, kr);
+      const f32x16 mine = score_block<DP>(role ? sG : sQ, l32, hf, kr, spread);
       const f32x16 other = pair_swap(sX, wave, lane, mine);
       s = role ? other : mine;
       dp = role ? mine : other;
     } else {
-      score_pair<DP>(sQ, sG, qs * 32 + l32, hf, kr, vr, s, dp);
+      score_pair<DP>(sQ, sG, qs * 32 + l32, hf, kr, vr, s, dp, spread);
     }
-    // next item into the other buffer; then look one item further ahead (the
-    // scalar loads this needs complete under the products below)
+
+    // look one item further ahead (scalar loads, complete under the products)
     int nnqt = -1, nnhh = 0;
     uint32_t nbmax = 0;
-    if (nqt_ >= 0) {
-      issue(nqt_, nhh, buf ^ 1);
+    if (more) {
       next_item(nqt_, nhh, nnqt, nnhh);
       const int bi = nqt_ * QS + qs;
       nbmax = bi < nblk ? a.blk_max[bi] : 0u;
@@ -709,9 +820,9 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     bmax = nbmax;
     buf ^= 1;
   }
+  tile_barrier();  // the last (empty) loads have landed before the LDS is reused or released
 
   if constexpr (QS > 1) {
-    __syncthreads();  // every wave is done with the tiles: reuse them for the reduction
     float* red = &sQG[0][0] + kb * (2 * PG::NB * 16 * 64) + lane;
     if (qs == 1) {
 #pragma unroll
@@ -732,6 +843,22 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
         accV[nb][r] += red[((1 * PG::NB + nb) * 16 + r) * 64];
       }
   }
+  // dK += scale * accK, dV += accV: all old values are read first, then all written
+  float* __restrict__ dKh = a.dK + (size_t)kvh * d;
+  float* __restrict__ dVh = a.dV + (size_t)kvh * d;
+  float oldK[PG::NB][16], oldV[PG::NB][16];
+#pragma unroll
+  for (int nb = 0; nb < PG::NB; ++nb) {
+    const int col = dcol0 + nb * 32 + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = j0 + kb * 32 + crow(r, hf);
+      const bool ok = row < S && col < d;
+      const size_t off = (size_t)row * kstride + col;
+      oldK[nb][r] = ok ? dKh[off] : 0.f;
+      oldV[nb][r] = ok ? dVh[off] : 0.f;
+    }
+  }
 #pragma unroll
   for (int nb = 0; nb < PG::NB; ++nb) {
     const int col = dcol0 + nb * 32 + l32;
@@ -739,9 +866,9 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     for (int r = 0; r < 16; ++r) {
       const int row = j0 + kb * 32 + crow(r, hf);
       if (row < S && col < d) {
-        const size_t off = (size_t)row * kstride + (size_t)kvh * d + col;
-        a.dK[off] += a.scale * accK[nb][r];
-        a.dV[off] += accV[nb][r];
+        const size_t off = (size_t)row * kstride + col;
+        dKh[off] = oldK[nb][r] + a.scale * accK[nb][r];
+        dVh[off] = oldV[nb][r] + accV[nb][r];
       }
     }
   }
