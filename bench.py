@@ -1,10 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of the attention backward on one MI355X.
 
-One step = one attn_bwd call (the whole hot path: the dQ/row-term kernel and
+One step = one attn_bwd call (the whole hot path: the small block-metadata
+kernel, the dQ/row-term kernel, which also stores the P and P*dP tiles, and
 the dK/dV kernel) on the S=4096, H=32, KV=8, d=128 plain-causal workload,
-fp32 inputs already resident in HBM.  The LSE input is produced beforehand on
-the GPU by attn_fwd_lse (untimed).
+fp32 inputs already resident in HBM.  The LSE
+input is produced beforehand on the GPU by attn_fwd_lse (untimed).
 
 Metric: credited TFLOP/s = 10 * d * H * N_valid / time per step, where
 N_valid is the number of visible (query, key) pairs (five contractions of 2*d
@@ -25,7 +26,6 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16/bf16 matrix
 PEAK_HBM = 8.0           # TB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_dkdv_s4096_h32_kv8_d128_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc", "attnbwd.hip")
 
 
@@ -44,18 +44,21 @@ def source_sha():
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic(n_launch_note):
-    """HBM bytes per k_dkdv launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def read_traffic(kname, workload):
+    """HBM bytes per launch of kernel `kname` on `workload` from the committed
+    rocprofv3 counter summary, or None when it is missing or was taken on a
+    different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"{kname}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        log(f"traffic: no counter summary {path}; reporting null")
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256_16") != source_sha():
-        log(f"traffic: {TRAFFIC_FILE} was taken on another kernel source; reporting null")
+        log(f"traffic: {path} was taken on another kernel source; reporting null")
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -129,6 +132,9 @@ def main():
     scale = float(x["scale"])
     lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
     binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, None, lse, scale)
+    ws_bytes, stored = binding.bwd_plan(w.S, w.H, w.KV, w.d)
+    log(f"bench: workspace {ws_bytes / 2**30:.2f} GiB, "
+        f"{'stored' if stored else 'recomputed'} probability tiles")
     dQ = torch.zeros_like(t["Q"])
     dK = torch.zeros_like(t["K"])
     dV = torch.zeros_like(t["V"])
@@ -159,7 +165,7 @@ def main():
     torch.cuda.synchronize()
     ms_dq, ms_dkdv, ncalls = binding.profile_end()
     ms_step = e0.elapsed_time(e1) / args.steps
-    assert ncalls == args.steps
+    assert ncalls == args.steps, (ncalls, args.steps)
     if not (torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()):
         raise RuntimeError("non-finite gradients")
 
@@ -167,18 +173,19 @@ def main():
     flops = 10.0 * w.d * w.H * npairs
     tflops = flops / (ms_step * 1e-3) / 1e12
     avg_dq, avg_dkdv = ms_dq / ncalls, ms_dkdv / ncalls
-    log(f"bench: {ms_step:.3f} ms/step, k_dq {avg_dq:.3f} ms, k_dkdv {avg_dkdv:.3f} ms, "
+    kv_name = "k_dkdv_p" if stored else "k_dkdv"
+    log(f"bench: {ms_step:.3f} ms/step, k_dq {avg_dq:.3f} ms, {kv_name} {avg_dkdv:.3f} ms, "
         f"{tflops:.2f} TFLOP/s credited")
 
     # dominant kernel: algorithmic flops per launch / its measured average duration
     if avg_dkdv >= avg_dq:
-        kname, kms = "k_dkdv", avg_dkdv
-        kflops = 8.0 * w.d * w.H * npairs  # Q.K^T, dO.V^T, P^T.dO, dS^T.Q
-        traffic = read_traffic("k_dkdv")
+        kname, kms = kv_name, avg_dkdv
+        # stored tiles: P^T.dO, dS^T.Q; recomputed: also Q.K^T, dO.V^T
+        kflops = (4.0 if stored else 8.0) * w.d * w.H * npairs
     else:
         kname, kms = "k_dq", avg_dq
         kflops = 6.0 * w.d * w.H * npairs  # Q.K^T, dO.V^T (row term), dS.K
-        traffic = None
+    traffic = read_traffic(kname, w.name)
     kach = kflops / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
                 "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s", "frac": round(kach / PEAK_FP32_MFMA, 4),
@@ -211,7 +218,9 @@ def main():
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
                    "head_dim": w.d, "mask": "causal" if seg is None else "documents",
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
-                   "kernel_ms": {"k_dq": round(avg_dq, 4), "k_dkdv": round(avg_dkdv, 4)}},
+                   "stored_tiles": stored,
+                   "workspace_bytes": ws_bytes,
+                   "kernel_ms": {"k_dq": round(avg_dq, 4), kv_name: round(avg_dkdv, 4)}},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

@@ -13,8 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_fwd_lse", "attn_last_error", "attn_profile_begin",
-            "attn_profile_end")
+EXPORTED = ("attn_bwd", "attn_bwd_plan", "attn_fwd_lse", "attn_last_error",
+            "attn_profile_begin", "attn_profile_end")
 
 _lib = None
 
@@ -37,6 +37,9 @@ def load():
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd.restype = I
+    lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
+                                  ctypes.POINTER(ctypes.c_int)]
+    lib.attn_bwd_plan.restype = I
     lib.attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_fwd_lse.restype = I
     lib.attn_profile_begin.argtypes = []
@@ -128,6 +131,15 @@ def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):
     st = load().attn_fwd_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(seg), _ptr(O), _ptr(LSE),
                              S, H, KV, d, float(scale), _stream(stream))
     _raise_on(st, "attn_fwd_lse")
+
+
+def bwd_plan(seq_len, n_heads, n_kv_heads, head_dim):
+    """(workspace bytes, stored probability tiles?) of one attn_bwd call."""
+    nbytes = ctypes.c_size_t(0)
+    stored = ctypes.c_int(0)
+    _raise_on(load().attn_bwd_plan(seq_len, n_heads, n_kv_heads, head_dim, ctypes.byref(nbytes),
+                                   ctypes.byref(stored)), "attn_bwd_plan")
+    return int(nbytes.value), bool(stored.value)
 
 
 def profile_begin():

@@ -44,6 +44,9 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "attnbwd.h"
@@ -86,8 +89,10 @@ struct BwdArgs {
   const uint32_t* seg;  // NULL = all zeros
   float *dQ, *dK, *dV;  // never overlap each other or an input
   float* Dws;            // [S, H] row term, written by k_dq, read by k_dkdv
-  uint32_t* blk_min;     // [ceil(S/32)] min seg per 32-row query block
-  uint32_t* blk_max;     // [ceil(S/32)] max seg per 32-row query block
+  uint32_t* blk_min;     // [ceil(S/32)] min seg per 32-row query block (k_prep)
+  uint32_t* blk_max;     // [ceil(S/32)] max seg per 32-row query block (k_prep)
+  long long* slot_off;   // [ceil(S/32) + 1] first tile slot of each query block (k_prep)
+  float* scratch;        // P and P*dP tiles of every visible pair, or NULL
   int S, H, KV, d;
   float scale;
 };
@@ -219,7 +224,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // tile_barrier (s_waitcnt vmcnt(0) + s_barrier) issued after the tile's loads,
 // and no buffer is refilled before all waves have passed a barrier after
 // their last read of it.  M0 carries the LDS address and is restored.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, const void* lds) {
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_byte) {
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -227,10 +232,10 @@ __device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, const void*
       "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr(lds))), "v"(voff), "s"(r)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(r)
       : "memory");
 }
-__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, const void* lds) {
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, uint32_t lds_byte) {
   int saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
@@ -238,8 +243,14 @@ __device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, const void* 
       "buffer_load_dword %2, %3, 0 offen lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)lds_addr(lds))), "v"(voff), "s"(r)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(r)
       : "memory");
+}
+__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, const void* lds) {
+  dma16(r, voff, lds_addr(lds));
+}
+__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, const void* lds) {
+  dma4(r, voff, lds_addr(lds));
 }
 
 // Padded ROWS x DP tile filled by 1 KiB chunks.
@@ -287,6 +298,15 @@ struct TileLoader {
 #pragma unroll
     for (int i = 0; i < T::CPW; ++i) load(i, r, lds, wave_u);
   }
+  // The same with the tile given by its LDS byte address.
+  __device__ __forceinline__ void load(int i, const i32x4& r, uint32_t lds_byte, int wave_u) const {
+    const int chunk = wave_u + 4 * i;
+    if (4 * (i + 1) <= T::NCH || chunk < T::NCH) dma16(r, off[i], lds_byte + chunk * 1024);
+  }
+  __device__ __forceinline__ void load_all(const i32x4& r, uint32_t lds_byte, int wave_u) const {
+#pragma unroll
+    for (int i = 0; i < T::CPW; ++i) load(i, r, lds_byte, wave_u);
+  }
 };
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
@@ -296,11 +316,14 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Wait for all of this wave's outstanding global loads (the current tile's
-// direct-to-LDS loads), then a workgroup barrier: the tile is complete in LDS
-// and every wave has finished with the previous tile.
+// Wait for all of this wave's outstanding memory operations (the current
+// tile's direct-to-LDS loads among them), then a workgroup barrier: the tile is
+// complete in LDS and every wave has finished with the previous tile.  The
+// wait is the compiler's own s_waitcnt, so it also knows that every load it
+// issued before has landed and adds no later waits for them.
 __device__ __forceinline__ void tile_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Above 128 columns a pair of waves shares one 32x32 score block by role:
@@ -403,6 +426,55 @@ __device__ __forceinline__ int xcd_head(int r, int H) {
 }
 
 // ---------------------------------------------------------------------------
+// k_prep: per 32-row query block, the smallest and largest document start,
+// and the slot offsets of the P / P*dP tile scratch.  A query block qb can see
+// keys only in key blocks [blk_min/32, qb]; each (query block, key block)
+// pair in that range owns one slot, numbered query block by query block.
+// One workgroup; a block-wide scan per 1024 query blocks.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint32_t* blk_min,
+                                               uint32_t* blk_max, long long* slot_off) {
+  __shared__ long long sScan[1024];
+  const int nblk = (S + 31) / 32;
+  const int t = threadIdx.x;
+  long long carry = 0;
+  for (int b0 = 0; b0 < nblk; b0 += 1024) {
+    const int b = b0 + t;
+    long long cnt = 0;
+    if (b < nblk) {
+      uint32_t mn = 0xffffffffu, mx = 0u;
+      const int r1 = min(b * 32 + 32, S);
+      for (int r = b * 32; r < r1; ++r) {
+        const uint32_t v = seg ? seg[r] : 0u;
+        mn = min(mn, v);
+        mx = max(mx, v);
+      }
+      blk_min[b] = mn;
+      blk_max[b] = mx;
+      cnt = max(0ll, (long long)b - (long long)(mn / 32) + 1);
+    }
+    sScan[t] = cnt;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {  // inclusive scan
+      const long long v = t >= o ? sScan[t - o] : 0;
+      __syncthreads();
+      sScan[t] += v;
+      __syncthreads();
+    }
+    if (b < nblk) slot_off[b] = carry + sScan[t] - cnt;
+    carry += sScan[1023];
+    __syncthreads();
+  }
+  if (t == 0) slot_off[nblk] = carry;
+}
+
+// The P / P*dP scratch holds, per slot and head, two 32x32 tiles (P, then
+// P*dP) of one (query block, key block) pair, stored in the register layout
+// of the key-major kernel: element R*64 + L is what its lane L holds in
+// register R, i.e. P[query crow(R, L/32)][key L%32].  Masked pairs are zero.
+#define ATTN_TILE_FLOATS 2048
+
+// ---------------------------------------------------------------------------
 // k_dq: D and dQ, one workgroup per (query tile of BR rows, head).
 // Wave w owns query block qb (32 queries); with the role split (DP > 128) two
 // waves share a block.  The key sweep streams 32-row K/V tiles through LDS:
@@ -427,8 +499,8 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   const int qb = PG::ROLE ? (wave >> 1) : wave;
   const int S = a.S, H = a.H, d = a.d;
   const int g = H / a.KV;
-  const int nqt = (S + BR - 1) / BR;
-  const int qt = nqt - 1 - (int)(blockIdx.x / H);  // longest rows first
+  const int qt_hi = (S - 1) / BR;
+  const int qt = qt_hi - (int)(blockIdx.x / H);  // longest rows first
   const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
   const int i0 = qt * BR;
   const int q = i0 + qb * 32 + l32;
@@ -466,11 +538,13 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 #pragma unroll
   for (int w = 1; w < 4; ++w) tmin = min(tmin, sMin[w]);
   const int qblk = (i0 >> 5) + qb;
-  if (h == 0 && role == 0 && lane == 0 && i0 + qb * 32 < S) {
-    a.blk_min[qblk] = mn;
-    a.blk_max[qblk] = mx;
-  }
   const int q_first = i0 + qb * 32;
+  // scratch slots of this wave's query block: key blocks [kb_lo, qblk]
+  const bool store = a.scratch != nullptr && q_first < S;
+  const int kb_lo = store ? (int)(a.blk_min[qblk] / 32) : 0;
+  const long long slot0 = store ? a.slot_off[qblk] - kb_lo : 0;
+  // lane's element offset in a stored tile (see ATTN_TILE_FLOATS)
+  const int st_base = 64 * (4 * (l32 >> 3) + (l32 & 3)) + 32 * ((l32 >> 2) & 1) + 4 * hf;
   const bool rows_full = q_first + 31 < S;  // all 32 queries of the block exist
 
   const int last_q = min(i0 + BR, S) - 1;
@@ -553,6 +627,18 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
         Dp += pdp;
         st[r] = p;
         dpt[r] = pdp;
+      }
+    }
+    // P and P.dP of a pair the key-major kernel will read: store them, transposed
+    if (store && kt >= kb_lo && kt <= qblk) {
+      float* tile = a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base;
+      if (!PG::ROLE || role == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tile[8 * (r >> 2) + (r & 3)] = st[r];
+      }
+      if (!PG::ROLE || role == 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tile[1024 + 8 * (r >> 2) + (r & 3)] = dpt[r];
       }
     }
     // A += (P.dP) K,  B += P K over the 32 keys
@@ -875,6 +961,272 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_dkdv_p: dK and dV from the stored P and P*dP tiles.
+// Same decomposition and sweep as k_dkdv -- one workgroup per (key tile of
+// 64 rows, KV head), wave w on key block kb = w / 2 -- but the score
+// products are not recomputed: per (query block, key block, head) the wave
+// loads the two stored tiles (prefetched one item ahead into registers),
+// forms dS/scale = P*dP - P*D and runs the two accumulations
+// dV += P^T dO and dK += (dS/scale)^T Q.  Above 128 columns the two waves of a
+// key block split the output columns instead of the query rows.
+//
+// Output columns are permuted: lane l's accumulator block nb holds column
+// dcol0 + NB*(l%32) + nb, so that the NB operands a lane needs per step are
+// adjacent in LDS (one wide read) and its NB results adjacent in memory.
+//
+// The sweep order is kept in registers: the query tiles are scanned in
+// segments of 64 (lane i <-> tile top - i); a ballot gives the tiles any query
+// of which sees these keys, and each lane keeps its tile's slot base for this
+// wave's block pair.  The walk over a segment is scalar bit arithmetic, so no
+// memory read sits between an item and the next one's prefetch.
+// ---------------------------------------------------------------------------
+template <int DP>
+__global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
+  constexpr bool DSPLIT = DP > 128;
+  constexpr int KB = 2, QS = DSPLIT ? 1 : 2, BC = 32 * KB, BR = 32 * QS;
+  constexpr int DW = DSPLIT ? DP / 2 : DP, NB = DW / 32;
+  constexpr int LDR = DP + 4;
+  constexpr int TILE = PadTile<BR, DP>::FLOATS;
+  constexpr int CPW = PadTile<BR, DP>::CPW;
+  static_assert(QS == 1 || 4 * TILE >= KB * 2 * NB * 16 * 64, "reduction buffer fits");
+  __shared__ __attribute__((aligned(1024))) float sQG[2][2 * TILE];
+  __shared__ __attribute__((aligned(16))) float sRow[2][4][64];  // D of a tile (slot 0)
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int kb = wave >> 1;
+  const int qs = DSPLIT ? 0 : (wave & 1);
+  const int dcol0 = DSPLIT ? (wave & 1) * DW : 0;
+  const int S = a.S, H = a.H, KV = a.KV, d = a.d;
+  const int g = H / KV;
+  const int kt = blockIdx.x / KV, kvh = blockIdx.x % KV;  // low key tiles (most queries) first
+  const int j0 = kt * BC;
+  const int kblk = kt * KB + kb;  // this wave's key block
+  const int head0 = kvh * g;
+  const size_t qstride = (size_t)H * d, kstride = (size_t)KV * d;
+
+  f32x16 accK[NB], accV[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) { accK[nb] = zero16(); accV[nb] = zero16(); }
+
+  const int jlast = min(j0 + BC, S) - 1;
+  const int nblk = (S + 31) / 32;
+  // query tiles that can see these keys: [qt_lo, qt_hi]
+  const int qt_lo = j0 / BR, qt_hi = (S - 1) / BR;
+
+  // segment of tiles top, top-1, ..., top-63 (lane i <-> tile top - i):
+  // the mask of tiles with a visible pair, and this lane's slot base of the
+  // wave's (query block, key block) pair (-1: no visible key in the pair)
+  int seg_top = qt_hi, sbv = -1;
+  uint64_t mask = 0;
+  auto build = [&](int top) {
+    const int t = top - lane;
+    bool vis = false;
+    int sb = -1;
+    if (t >= qt_lo) {
+      uint32_t mn = 0xffffffffu, mine = 0xffffffffu;
+#pragma unroll
+      for (int b = 0; b < QS; ++b) {
+        const int bi = t * QS + b;
+        const uint32_t v = bi < nblk ? a.blk_min[bi] : 0xffffffffu;
+        mn = min(mn, v);
+        if (b == qs) mine = v;
+      }
+      vis = mn <= (uint32_t)jlast;
+      const int qb = t * QS + qs;
+      const int lo = (int)(mine / 32);
+      if (vis && qb < nblk && kblk <= qb && kblk >= lo)
+        sb = (int)a.slot_off[qb] + (kblk - lo);
+    }
+    sbv = sb;
+    mask = __ballot(vis);
+  };
+  // step (li, hh) to the next item of the sweep; false at its end
+  auto advance = [&](int& li, int& hh) -> bool {
+    if (++hh < g) return true;
+    hh = 0;
+    uint64_t rest = li < 0 ? mask : (li >= 63 ? 0ull : mask & (~0ull << (li + 1)));
+    while (rest == 0) {
+      seg_top -= 64;
+      if (seg_top < qt_lo) return false;
+      build(seg_top);
+      rest = mask;
+    }
+    li = __builtin_ctzll(rest);
+    return true;
+  };
+  auto item_slot = [&](int li, int hh) -> int {
+    const int sb = __builtin_amdgcn_readlane(sbv, li);
+    return sb < 0 ? -1 : sb * H + head0 + hh;
+  };
+
+  TileLoader<BR, DP> ld;
+  ld.init(qstride, d, wave, lane);
+  const uint32_t row_off = lane < BR ? (uint32_t)(lane * 4 * H) : ATTN_BUF_OOB;
+  auto row_rsrc = [&](int t, int hh, bool live) {  // D of the tile's rows (wave 0 only)
+    const int i0 = t * BR;
+    const int rows = (live && wave == 0) ? min(S - i0, BR) : 0;
+    return buf_rsrc(rows > 0 ? a.Dws + (size_t)i0 * H + head0 + hh : a.Dws,
+                    rows > 0 ? (uint32_t)(((rows - 1) * (size_t)H + 1) * 4) : 0u);
+  };
+  const uint32_t lds_qg = lds_addr(&sQG[0][0]), lds_row = lds_addr(&sRow[0][wave][0]);
+  constexpr uint32_t QG_BYTES = 2 * TILE * 4, ROW_BYTES = 4 * 64 * 4;
+  float pn[16], pdn[16];  // the next item's stored tiles
+  auto fetch_tiles = [&](int slot) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { pn[r] = 0.f; pdn[r] = 0.f; }
+    if (slot >= 0) {
+      const float* t = a.scratch + (size_t)slot * ATTN_TILE_FLOATS + lane;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pn[r] = t[64 * r];
+        pdn[r] = t[1024 + 64 * r];
+      }
+    }
+  };
+
+  build(seg_top);
+  int li = -1, hh = g - 1, buf = 0, cslot = -1;
+  bool has = advance(li, hh);
+  if (has) {
+    const int t = seg_top - li;
+    const i32x4 rq = ld.rsrc(a.Q + (size_t)(head0 + hh) * d, t * BR, S, qstride, d, true);
+    const i32x4 rg = ld.rsrc(a.dO + (size_t)(head0 + hh) * d, t * BR, S, qstride, d, true);
+    ld.load_all(rq, lds_qg, wave);
+    ld.load_all(rg, lds_qg + TILE * 4, wave);
+    dma4(row_rsrc(t, hh, true), row_off, lds_row);
+    cslot = item_slot(li, hh);
+    fetch_tiles(cslot);
+  }
+  // this lane's operand offset in a Q/dO tile: query row qs*32 + 4*hf (+ the
+  // step's row), columns dcol0 + NB*l32 ..
+  const int ob = (qs * 32 + 4 * hf) * LDR + dcol0 + NB * l32;
+  while (has) {
+    tile_barrier();  // this item resident; everyone done with the previous one
+    const float* sQ = &sQG[buf][0];
+    const float* sG = &sQG[buf][TILE];
+    float p[16], pd[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { p[r] = pn[r]; pd[r] = pdn[r]; }
+    const bool vis = cslot >= 0;
+    const float* Dv = &sRow[buf][0][qs * 32 + 4 * hf];
+
+    // the next item: its stored tiles into registers, its Q/dO/D rows into
+    // the other buffers (issued between the dV products below)
+    const bool more = advance(li, hh);
+    const int nt = more ? seg_top - li : 0;
+    const int nslot = more ? item_slot(li, hh) : -1;
+    fetch_tiles(nslot);
+    const int nh = head0 + (more ? hh : 0);
+    const i32x4 rq = ld.rsrc(a.Q + (size_t)nh * d, nt * BR, S, qstride, d, more);
+    const i32x4 rg = ld.rsrc(a.dO + (size_t)nh * d, nt * BR, S, qstride, d, more);
+    const i32x4 rr = row_rsrc(nt, more ? hh : 0, more);
+    const uint32_t nxt = lds_qg + (buf ^ 1) * QG_BYTES;
+    const uint32_t nrow = lds_row + (buf ^ 1) * ROW_BYTES;
+    auto issue = [&](int j) {
+      if (j < CPW) ld.load(j, rq, nxt, wave);
+      else if (j < 2 * CPW) ld.load(j - CPW, rg, nxt + TILE * 4, wave);
+      else dma4(rr, row_off, nrow);
+    };
+    constexpr int NLOAD = 2 * CPW + 1;
+
+    if (vis) {
+      // dO operands of all 16 steps, then dS/scale = P*dP - P*D
+      float gv[16][NB], qv[16][NB];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float* row = sG + ob + (8 * (r >> 2) + (r & 3)) * LDR;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) gv[r][nb] = row[nb];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pd[r] = fmaf(-p[r], Dv[8 * (r >> 2) + (r & 3)], pd[r]);
+      // dV += P^T dO; the Q operands of the dK products and the next item's
+      // loads go out between these products
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) accV[nb] = mfma32(p[r], gv[r][nb], accV[nb]);
+        const float* row = sQ + ob + (8 * (r >> 2) + (r & 3)) * LDR;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) qv[r][nb] = row[nb];
+        SpreadLoads<NLOAD, 16, decltype(issue)>{issue}(r);
+      }
+      // dK += (dS/scale)^T Q
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) accK[nb] = mfma32(pd[r], qv[r][nb], accK[nb]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLOAD; ++j) issue(j);
+    }
+    // keep the accumulators in AGPRs across the loop (both paths above meet here)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      asm volatile("" : "+a"(accK[nb]));
+      asm volatile("" : "+a"(accV[nb]));
+    }
+    cslot = nslot;
+    has = more;
+    buf ^= 1;
+  }
+  tile_barrier();  // the last loads have landed before the LDS is reused or released
+
+  if constexpr (QS > 1) {
+    float* red = &sQG[0][0] + kb * (2 * NB * 16 * 64) + lane;
+    if (qs == 1) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          red[((0 * NB + nb) * 16 + r) * 64] = accK[nb][r];
+          red[((1 * NB + nb) * 16 + r) * 64] = accV[nb][r];
+        }
+    }
+    __syncthreads();
+    if (qs == 1) return;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        accK[nb][r] += red[((0 * NB + nb) * 16 + r) * 64];
+        accV[nb][r] += red[((1 * NB + nb) * 16 + r) * 64];
+      }
+  }
+  // dK += scale * accK, dV += accV: all old values are read first, then all written
+  float* __restrict__ dKh = a.dK + (size_t)kvh * d;
+  float* __restrict__ dVh = a.dV + (size_t)kvh * d;
+  const int col0 = dcol0 + NB * l32;
+  float oldK[16][NB], oldV[16][NB];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = j0 + kb * 32 + crow(r, hf);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const bool ok = row < S && col0 + nb < d;
+      const size_t off = (size_t)row * kstride + col0 + nb;
+      oldK[r][nb] = ok ? dKh[off] : 0.f;
+      oldV[r][nb] = ok ? dVh[off] : 0.f;
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = j0 + kb * 32 + crow(r, hf);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (row < S && col0 + nb < d) {
+        const size_t off = (size_t)row * kstride + col0 + nb;
+        dKh[off] = oldK[r][nb] + a.scale * accK[nb][r];
+        dVh[off] = oldV[r][nb] + accV[nb][r];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_fwd: LSE (pass 1, running max and sum per query) and O (pass 2, with the
 // final LSE, no rescaling).  Same tiling as k_dq.
 // ---------------------------------------------------------------------------
@@ -1095,8 +1447,10 @@ static attn_status_t hip_check(hipError_t e, const char* what) {
   return ATTN_OK;
 }
 
+// k_dq over all query tiles, then the dK/dV kernel over all key tiles (from
+// the stored tiles when a.scratch is set, by recomputing the scores otherwise).
 template <int DP>
-static attn_status_t launch_bwd(const BwdArgs& a, hipStream_t st) {
+static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   const int BRq = Pair<DP>::ROLE ? 64 : 128;
   const int nqt = (a.S + BRq - 1) / BRq;
   attn_status_t rc = profile_mark(st);
@@ -1106,10 +1460,109 @@ static attn_status_t launch_bwd(const BwdArgs& a, hipStream_t st) {
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
   const int nkt = (a.S + 63) / 64;
-  hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
-  rc = hip_check(hipGetLastError(), "launching k_dkdv");
+  if (a.scratch)
+    hipLaunchKernelGGL(k_dkdv_p<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
+  rc = hip_check(hipGetLastError(), "launching the dK/dV kernel");
   if (rc == ATTN_OK) rc = profile_mark(st);
   return rc;
+}
+
+static attn_status_t launch_bwd(const BwdArgs& a, int dp, hipStream_t st) {
+  switch (dp) {
+    case 32: return launch_dqkv<32>(a, st);
+    case 64: return launch_dqkv<64>(a, st);
+    case 96: return launch_dqkv<96>(a, st);
+    case 128: return launch_dqkv<128>(a, st);
+    case 192: return launch_dqkv<192>(a, st);
+    default: return launch_dqkv<256>(a, st);
+  }
+}
+
+// The library's own stream-ordered memory pool for the per-call workspace:
+// it keeps freed memory for reuse, so large workspaces cost no mapping work
+// after the first call.  One pool per device, created on first use.
+static std::mutex g_pool_mu;
+static std::map<int, hipMemPool_t> g_pools;
+
+static attn_status_t device_pool(hipMemPool_t* out) {
+  int dev = 0;
+  attn_status_t rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != ATTN_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  auto it = g_pools.find(dev);
+  if (it != g_pools.end()) {
+    *out = it->second;
+    return ATTN_OK;
+  }
+  hipMemPoolProps props = {};
+  props.allocType = hipMemAllocationTypePinned;
+  props.location.type = hipMemLocationTypeDevice;
+  props.location.id = dev;
+  hipMemPool_t pool;
+  rc = hip_check(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate");
+  if (rc != ATTN_OK) return rc;
+  uint64_t keep = UINT64_MAX;
+  rc = hip_check(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep),
+                 "hipMemPoolSetAttribute");
+  if (rc != ATTN_OK) return rc;
+  g_pools[dev] = pool;
+  *out = pool;
+  return ATTN_OK;
+}
+
+// Bytes the P / P*dP scratch can need: at most qb + 1 key blocks per query
+// block qb (the causal triangle; a document mask only shrinks it), two 4 KiB
+// tiles per (block pair, head).
+static long long scratch_bound(long long nblk, int H) {
+  return nblk * (nblk + 1) / 2 * H * ATTN_TILE_FLOATS * (long long)sizeof(float);
+}
+
+// Scratch budget in bytes: ATTNBWD_SCRATCH_MB (MiB, a decimal number) if set
+// (0 disables the stored tiles), else 32 GiB.
+static long long scratch_budget() {
+  const char* e = getenv("ATTNBWD_SCRATCH_MB");
+  if (e && *e) {
+    const double mb = atof(e);
+    return mb > 0 ? (long long)(mb * (double)(1ll << 20)) : 0;
+  }
+  return 32ll << 30;
+}
+
+// How attn_bwd runs a problem: with the stored P / P*dP tiles when their
+// bound fits the budget (tile indices then also stay below 2^31), else with
+// the scores recomputed by the key-major kernel; and the layout of the
+// per-call workspace: D [S, H], per-block seg min/max and slot offsets, then
+// the scratch.
+struct Plan {
+  bool stored = false;
+  size_t off_blk = 0, off_slot = 0, off_scr = 0, bytes = 0;
+};
+
+static Plan make_plan(int S, int H) {
+  Plan p;
+  const long long nblk = ((long long)S + 31) / 32;
+  const long long need = scratch_bound(nblk, H);
+  const long long budget = std::min(scratch_budget(), 0x7fffffffll * ATTN_TILE_FLOATS * 4);
+  p.stored = need > 0 && need <= budget;
+  const size_t nD = (size_t)S * H;
+  p.off_blk = (nD * sizeof(float) + 255) & ~(size_t)255;
+  p.off_slot = (p.off_blk + 2 * nblk * sizeof(uint32_t) + 255) & ~(size_t)255;
+  p.off_scr = (p.off_slot + (nblk + 1) * sizeof(long long) + 255) & ~(size_t)255;
+  p.bytes = p.off_scr + (p.stored ? (size_t)need : 0);
+  return p;
+}
+
+extern "C" attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                                       size_t* workspace_bytes, int* stored_tiles) {
+  g_err[0] = 0;
+  attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, 1.f);
+  if (rc != ATTN_OK) return rc;
+  const Plan p = make_plan(seq_len, n_heads);
+  if (workspace_bytes) *workspace_bytes = seq_len ? p.bytes : 0;
+  if (stored_tiles) *stored_tiles = p.stored ? 1 : 0;
+  return ATTN_OK;
 }
 
 template <int DP>
@@ -1135,29 +1588,30 @@ extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V
   if (seq_len == 0) return ATTN_OK;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const size_t nD = (size_t)seq_len * n_heads;
-  const size_t nblk = ((size_t)seq_len + 31) / 32;
-  void* ws = nullptr;
-  rc = hip_check(hipMallocAsync(&ws, nD * sizeof(float) + 2 * nblk * sizeof(uint32_t), st),
-                 "hipMallocAsync(workspace)");
+  const int dp = padded_dim(head_dim);
+  const long long nblk = ((long long)seq_len + 31) / 32;
+  const Plan pl = make_plan(seq_len, n_heads);
+  hipMemPool_t pool;
+  rc = device_pool(&pool);
   if (rc != ATTN_OK) return rc;
+  void* ws = nullptr;
+  rc = hip_check(hipMallocFromPoolAsync(&ws, pl.bytes, pool, st), "hipMallocFromPoolAsync(workspace)");
+  if (rc != ATTN_OK) return rc;
+  char* wsb = static_cast<char*>(ws);
 
   BwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.LSE = LSE; a.seg = seg;
   a.dQ = dQ; a.dK = dK; a.dV = dV;
-  a.Dws = static_cast<float*>(ws);
-  a.blk_min = reinterpret_cast<uint32_t*>(static_cast<float*>(ws) + nD);
+  a.Dws = reinterpret_cast<float*>(wsb);
+  a.blk_min = reinterpret_cast<uint32_t*>(wsb + pl.off_blk);
   a.blk_max = a.blk_min + nblk;
+  a.slot_off = reinterpret_cast<long long*>(wsb + pl.off_slot);
+  a.scratch = pl.stored ? reinterpret_cast<float*>(wsb + pl.off_scr) : nullptr;
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim; a.scale = scale;
 
-  switch (padded_dim(head_dim)) {
-    case 32: rc = launch_bwd<32>(a, st); break;
-    case 64: rc = launch_bwd<64>(a, st); break;
-    case 96: rc = launch_bwd<96>(a, st); break;
-    case 128: rc = launch_bwd<128>(a, st); break;
-    case 192: rc = launch_bwd<192>(a, st); break;
-    default: rc = launch_bwd<256>(a, st); break;
-  }
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, st, seg, seq_len, a.blk_min, a.blk_max, a.slot_off);
+  rc = hip_check(hipGetLastError(), "launching k_prep");
+  if (rc == ATTN_OK) rc = launch_bwd(a, dp, st);
   attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");
   return rc != ATTN_OK ? rc : rc2;
 }

@@ -42,12 +42,14 @@
  * enqueue work and return; kernel-execution faults surface at the caller's
  * next synchronisation.  Launch-time errors return ATTN_ERR_HIP.
  *
- * Threads.  Reentrant.  The only global state is thread-local: the text of
- * the last error and the event log of the measurement hooks.
+ * Threads.  Reentrant.  Global state: the per-device memory pools (created
+ * once, under a lock) and, per thread, the text of the last error and the
+ * event log of the measurement hooks.
  */
 #ifndef ATTNBWD_H
 #define ATTNBWD_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -74,10 +76,20 @@ typedef enum {
  * gives dQ += semantics with the host zeroing before the first call, and dK,
  * dV accumulate likewise).  Zero them before the first accumulation.
  *
- * Internally the call takes one stream-ordered workspace of
- * seq_len * n_heads * 4 bytes (the row term D) plus 8 bytes per 32 rows of
- * tile metadata, allocated with hipMallocAsync on `stream` and released with
- * hipFreeAsync on `stream` before returning.
+ * Workspace.  Each call takes one stream-ordered workspace from a private
+ * per-device memory pool (hipMallocFromPoolAsync on `stream`, released with
+ * hipFreeAsync on `stream` before returning; the pool keeps freed memory for
+ * later calls until the process ends).  It holds the row term D
+ * (seq_len * n_heads * 4 bytes), per-32-row block metadata, and -- when it
+ * fits the budget -- a scratch of the probabilities P and the products P*dP
+ * of every visible (32-query block, 32-key block, head) tile, written by the
+ * first pass and read by the key-major pass instead of recomputing the
+ * scores.  The scratch is sized by the causal bound, 8 KiB per block pair
+ * and head: 2 GiB at seq_len 4096 with 32 heads, 16 GiB at 16384 with 16.
+ * The budget is 32 GiB, or ATTNBWD_SCRATCH_MB MiB (a decimal number) when
+ * that environment variable is set, read at every call; above it (or at 0)
+ * there is no scratch and the key-major pass recomputes the scores.
+ * attn_bwd_plan reports the choice and the size for a problem.
  *
  * seq_len == 0 returns ATTN_OK and enqueues nothing.
  */
@@ -86,6 +98,15 @@ attn_status_t attn_bwd(const float* Q, const float* K, const float* V, const flo
                        float* dQ, float* dK, float* dV,
                        int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
                        void* stream);
+
+/*
+ * attn_bwd_plan -- host-side query (no GPU work): the workspace bytes one
+ * attn_bwd call of this size takes, and whether its key-major pass reads
+ * stored probability tiles (1) or recomputes them (0).  Either output pointer
+ * may be NULL.  Same argument checks as attn_bwd.
+ */
+attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                            size_t* workspace_bytes, int* stored_tiles);
 
 /*
  * attn_fwd_lse -- the forward pass that produces the backward's inputs:
@@ -105,12 +126,12 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
  * Measurement hooks (benchmarks only; normal callers never need them).
  *
  * attn_profile_begin: from now on, on the calling thread, every attn_bwd call
- *   records HIP events on its stream before, between and after its two
+ *   records HIP events on its stream before, between and after its two main
  *   kernels (the dQ / row-term kernel, then the dK/dV kernel).
  * attn_profile_end: waits for those events, writes into ms[0] and ms[1] the
- *   summed device time in milliseconds of the dQ kernel and of the dK/dV
- *   kernel over the recorded calls, into *n_calls their number, releases the
- *   events and stops recording.  ms and n_calls may be NULL.
+ *   summed device time in milliseconds of the dQ kernels and of the dK/dV
+ *   kernels over the recorded calls, into *n_calls their number, releases
+ *   the events and stops recording.  ms and n_calls may be NULL.
  */
 attn_status_t attn_profile_begin(void);
 attn_status_t attn_profile_end(double* ms, int* n_calls);

@@ -36,3 +36,50 @@ def test_argument_errors_need_no_gpu():
                       ctypes.c_float(0.125), null)
     assert st == binding.ATTN_ERR_INVALID_ARG
     assert "NULL" in binding.last_error()
+
+
+def causal_pairs(nblk):
+    return nblk * (nblk + 1) // 2
+
+
+def up(n):
+    return (n + 255) // 256 * 256
+
+
+def test_plan_sizes_the_workspace(monkeypatch):
+    # host-only query: D [S,H], block metadata, and the P / P*dP tile scratch
+    # (two 32x32 fp32 tiles per (query block, key block, head) of the causal
+    # triangle), each part 256-byte aligned
+    monkeypatch.delenv("ATTNBWD_SCRATCH_MB", raising=False)
+    S, H = 4096, 32
+    nblk = S // 32
+    meta = up(up(up(S * H * 4) + 2 * nblk * 4) + (nblk + 1) * 8)
+    assert binding.bwd_plan(S, H, 8, 128) == (meta + causal_pairs(nblk) * H * 8192, True)
+    monkeypatch.setenv("ATTNBWD_SCRATCH_MB", "0")
+    assert binding.bwd_plan(S, H, 8, 128) == (meta, False)
+
+
+def test_plan_recomputes_above_the_budget(monkeypatch):
+    # 16384 rows, 16 heads: the tiles need 16.03 GiB, within the default
+    # budget; a smaller budget switches to recomputed scores
+    monkeypatch.delenv("ATTNBWD_SCRATCH_MB", raising=False)
+    S, H = 16384, 16
+    need = causal_pairs(S // 32) * H * 8192
+    nbytes, stored = binding.bwd_plan(S, H, 2, 256)
+    assert stored and nbytes > need
+    monkeypatch.setenv("ATTNBWD_SCRATCH_MB", repr(need / 2**20))
+    assert binding.bwd_plan(S, H, 2, 256)[1]
+    monkeypatch.setenv("ATTNBWD_SCRATCH_MB", repr((need - 1) / 2**20))
+    nbytes, stored = binding.bwd_plan(S, H, 2, 256)
+    assert not stored and nbytes < 2 * S * H * 4
+
+
+def test_plan_rejects_bad_shapes():
+    for args in ((8, 3, 2, 64), (8, 2, 1, 250), (-1, 2, 1, 64)):
+        try:
+            binding.bwd_plan(*args)
+        except binding.AttnError as e:
+            assert e.status in (binding.ATTN_ERR_INVALID_ARG, binding.ATTN_ERR_UNSUPPORTED)
+        else:
+            raise AssertionError(f"bwd_plan{args} accepted")
+    assert binding.bwd_plan(0, 2, 1, 64) == (0, False)
