@@ -2,9 +2,10 @@
 """Benchmark of the attention backward on one MI355X.
 
 One step = one attn_bwd call (the whole hot path: the small block-metadata
-kernel, the dQ/row-term kernel, which also stores the P and P*dP tiles, and
-the dK/dV kernel) on the S=4096, H=32, KV=8, d=128 plain-causal workload,
-fp32 inputs already resident in HBM.  The LSE
+kernel; the query-major pass, which forms P, P*dP and the row term D and
+stores the tiles; the key-major dK/dV pass, which also forms dS; the dQ pass)
+on the S=4096, H=32, KV=8, d=128 plain-causal workload, fp32 inputs already
+resident in HBM.  The LSE
 input is produced beforehand on the GPU by attn_fwd_lse (untimed).
 
 Metric: credited TFLOP/s = 10 * d * H * N_valid / time per step, where
@@ -163,7 +164,7 @@ def main():
         step()
     e1.record()
     torch.cuda.synchronize()
-    ms_dq, ms_dkdv, ncalls = binding.profile_end()
+    ms_q, ms_k, ms_s, ncalls = binding.profile_end()
     ms_step = e0.elapsed_time(e1) / args.steps
     assert ncalls == args.steps, (ncalls, args.steps)
     if not (torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()):
@@ -172,19 +173,22 @@ def main():
     npairs = valid_pairs(seg_np)
     flops = 10.0 * w.d * w.H * npairs
     tflops = flops / (ms_step * 1e-3) / 1e12
-    avg_dq, avg_dkdv = ms_dq / ncalls, ms_dkdv / ncalls
-    kv_name = "k_dkdv_p" if stored else "k_dkdv"
-    log(f"bench: {ms_step:.3f} ms/step, k_dq {avg_dq:.3f} ms, {kv_name} {avg_dkdv:.3f} ms, "
-        f"{tflops:.2f} TFLOP/s credited")
+    # the passes, with the algorithmic flops per visible (pair, head) of each
+    # (2*d per contraction): with stored tiles k_dq forms S = Q.K^T and
+    # dP = dO.V^T, k_dkdv_p P^T.dO and dS^T.Q, k_dqs dS.K; recomputing, k_dq
+    # forms Q.K^T, dO.V^T and dS.K (with the row term), k_dkdv all four
+    if stored:
+        passes = [("k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0), ("k_dqs", ms_s, 2.0)]
+    else:
+        passes = [("k_dq", ms_q, 6.0), ("k_dkdv", ms_k, 8.0)]
+    kernel_ms = {n: round(t / ncalls, 4) for n, t, _ in passes}
+    log(f"bench: {ms_step:.3f} ms/step, " + ", ".join(f"{n} {t:.3f} ms" for n, t in kernel_ms.items())
+        + f", {tflops:.2f} TFLOP/s credited")
 
     # dominant kernel: algorithmic flops per launch / its measured average duration
-    if avg_dkdv >= avg_dq:
-        kname, kms = kv_name, avg_dkdv
-        # stored tiles: P^T.dO, dS^T.Q; recomputed: also Q.K^T, dO.V^T
-        kflops = (4.0 if stored else 8.0) * w.d * w.H * npairs
-    else:
-        kname, kms = "k_dq", avg_dq
-        kflops = 6.0 * w.d * w.H * npairs  # Q.K^T, dO.V^T (row term), dS.K
+    kname, kms_sum, per_pair = max(passes, key=lambda p: p[1])
+    kms = kms_sum / ncalls
+    kflops = per_pair * w.d * w.H * npairs
     traffic = read_traffic(kname, w.name)
     kach = kflops / (kms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
@@ -220,7 +224,7 @@ def main():
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
                    "stored_tiles": stored,
                    "workspace_bytes": ws_bytes,
-                   "kernel_ms": {"k_dq": round(avg_dq, 4), kv_name: round(avg_dkdv, 4)}},
+                   "kernel_ms": kernel_ms},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

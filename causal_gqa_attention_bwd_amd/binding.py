@@ -148,8 +148,9 @@ def profile_begin():
 
 
 def profile_end():
-    """Stop recording; returns (ms_dq_kernel, ms_dkdv_kernel, n_calls) summed over the calls."""
-    ms = (ctypes.c_double * 2)()
+    """Stop recording; returns (ms of the query-major pass, of the key-major pass,
+    of the dQ pass, n_calls), the times summed over the recorded calls."""
+    ms = (ctypes.c_double * 3)()
     n = ctypes.c_int(0)
     _raise_on(load().attn_profile_end(ms, ctypes.byref(n)), "attn_profile_end")
-    return float(ms[0]), float(ms[1]), int(n.value)
+    return float(ms[0]), float(ms[1]), float(ms[2]), int(n.value)

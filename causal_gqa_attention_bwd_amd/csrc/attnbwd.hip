@@ -475,13 +475,16 @@ __global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint3
 #define ATTN_TILE_FLOATS 2048
 
 // ---------------------------------------------------------------------------
-// k_dq: D and dQ, one workgroup per (query tile of BR rows, head).
+// k_dq: the query-major pass, one workgroup per (query tile of BR rows, head).
 // Wave w owns query block qb (32 queries); with the role split (DP > 128) two
 // waves share a block.  The key sweep streams 32-row K/V tiles through LDS:
 // one barrier per tile, and the next tile's loads are issued once this tile's
 // score products are under way.
+//   ACC = true:  D and dQ (A, B accumulated as above, dQ = scale*(A - D*B)).
+//   ACC = false: D, and the P and P*dP tiles of every visible pair stored for
+//                the key-major kernel (which then forms dS; k_dqs adds dS*K).
 // ---------------------------------------------------------------------------
-template <int DP>
+template <int DP, bool ACC>
 __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   using PG = Pair<DP>;
   constexpr int QB = PG::ROLE ? 2 : 4, BR = 32 * QB, BC = 32;
@@ -540,7 +543,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   const int qblk = (i0 >> 5) + qb;
   const int q_first = i0 + qb * 32;
   // scratch slots of this wave's query block: key blocks [kb_lo, qblk]
-  const bool store = a.scratch != nullptr && q_first < S;
+  const bool store = !ACC && q_first < S;
   const int kb_lo = store ? (int)(a.blk_min[qblk] / 32) : 0;
   const long long slot0 = store ? a.slot_off[qblk] - kb_lo : 0;
   // lane's element offset in a stored tile (see ATTN_TILE_FLOATS)
@@ -550,9 +553,11 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   const int last_q = min(i0 + BR, S) - 1;
   const int kt_lo = (int)(min(tmin, (uint32_t)last_q) / BC), kt_hi = last_q / BC;
 
-  f32x16 accA[PG::NB], accB[PG::NB];
+  f32x16 accA[ACC ? PG::NB : 1], accB[ACC ? PG::NB : 1];
+  if constexpr (ACC) {
 #pragma unroll
-  for (int nb = 0; nb < PG::NB; ++nb) { accA[nb] = zero16(); accB[nb] = zero16(); }
+    for (int nb = 0; nb < PG::NB; ++nb) { accA[nb] = zero16(); accB[nb] = zero16(); }
+  }
   float Dp = 0.f;
   const int dcol0 = role * PG::DW;
 
@@ -588,12 +593,14 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 
     // B operands of the accumulation below (independent of the scores): read
     // them now so that the accumulation runs without LDS waits
-    float kv[16][PG::NB];
-    const float* kb0 = sK + (4 * hf) * LDR + dcol0 + l32;
+    float kv[16][ACC ? PG::NB : 1];
+    if constexpr (ACC) {
+      const float* kb0 = sK + (4 * hf) * LDR + dcol0 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int nb = 0; nb < PG::NB; ++nb) kv[r][nb] = kb0[(8 * (r >> 2) + (r & 3)) * LDR + nb * 32];
+        for (int nb = 0; nb < PG::NB; ++nb) kv[r][nb] = kb0[(8 * (r >> 2) + (r & 3)) * LDR + nb * 32];
+    }
 
     // S^T = K Q^T and dP^T = V dO^T: 32 keys x this wave's 32 queries
     f32x16 st, dpt;
@@ -630,7 +637,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       }
     }
     // P and P.dP of a pair the key-major kernel will read: store them, transposed
-    if (store && kt >= kb_lo && kt <= qblk) {
+    if (!ACC && store && kt >= kb_lo && kt <= qblk) {
       float* tile = a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base;
       if (!PG::ROLE || role == 0) {
 #pragma unroll
@@ -642,12 +649,14 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       }
     }
     // A += (P.dP) K,  B += P K over the 32 keys
+    if constexpr (ACC) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+      for (int r = 0; r < 16; ++r) {
 #pragma unroll
-      for (int nb = 0; nb < PG::NB; ++nb) {
-        accB[nb] = mfma32(st[r], kv[r][nb], accB[nb]);
-        accA[nb] = mfma32(dpt[r], kv[r][nb], accA[nb]);
+        for (int nb = 0; nb < PG::NB; ++nb) {
+          accB[nb] = mfma32(st[r], kv[r][nb], accB[nb]);
+          accA[nb] = mfma32(dpt[r], kv[r][nb], accA[nb]);
+        }
       }
     }
     buf ^= 1;
@@ -656,31 +665,33 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 
   // D of this lane's query: the two half-waves saw disjoint keys
   const float Dq = Dp + __shfl_xor(Dp, 32);
-  if (hf == 0) sD[wave * 32 + l32] = Dq;
+  if (ACC && hf == 0) sD[wave * 32 + l32] = Dq;
   if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * H + h] = Dq;
-  __syncthreads();
-  // dQ += scale * (A - D B): all old values are read first, then all written
-  float* __restrict__ dQh = a.dQ + (size_t)h * d;
-  float old[PG::NB][16];
+  if constexpr (ACC) {
+    __syncthreads();
+    // dQ += scale * (A - D B): all old values are read first, then all written
+    float* __restrict__ dQh = a.dQ + (size_t)h * d;
+    float old[PG::NB][16];
 #pragma unroll
-  for (int nb = 0; nb < PG::NB; ++nb) {
-    const int col = dcol0 + nb * 32 + l32;
+    for (int nb = 0; nb < PG::NB; ++nb) {
+      const int col = dcol0 + nb * 32 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = i0 + qb * 32 + crow(r, hf);
-      old[nb][r] = (row < S && col < d) ? dQh[(size_t)row * qstride + col] : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        const int row = i0 + qb * 32 + crow(r, hf);
+        old[nb][r] = (row < S && col < d) ? dQh[(size_t)row * qstride + col] : 0.f;
+      }
     }
-  }
 #pragma unroll
-  for (int nb = 0; nb < PG::NB; ++nb) {
-    const int col = dcol0 + nb * 32 + l32;
+    for (int nb = 0; nb < PG::NB; ++nb) {
+      const int col = dcol0 + nb * 32 + l32;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = crow(r, hf);
-      const int row = i0 + qb * 32 + m;
-      if (row < S && col < d)
-        dQh[(size_t)row * qstride + col] =
-            old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
+      for (int r = 0; r < 16; ++r) {
+        const int m = crow(r, hf);
+        const int row = i0 + qb * 32 + m;
+        if (row < S && col < d)
+          dQh[(size_t)row * qstride + col] =
+              old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
+      }
     }
   }
 }
@@ -966,9 +977,10 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 // 64 rows, KV head), wave w on key block kb = w / 2 -- but the score
 // products are not recomputed: per (query block, key block, head) the wave
 // loads the two stored tiles (prefetched one item ahead into registers),
-// forms dS/scale = P*dP - P*D and runs the two accumulations
-// dV += P^T dO and dK += (dS/scale)^T Q.  Above 128 columns the two waves of a
-// key block split the output columns instead of the query rows.
+// forms dS/scale = P*dP - P*D (written back over P*dP for k_dqs) and runs
+// the two accumulations dV += P^T dO and dK += (dS/scale)^T Q.  Above 128
+// columns the two waves of a key block split the output columns instead of
+// the query rows.
 //
 // Output columns are permuted: lane l's accumulator block nb holds column
 // dcol0 + NB*(l%32) + nb, so that the NB operands a lane needs per step are
@@ -1142,6 +1154,13 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) pd[r] = fmaf(-p[r], Dv[8 * (r >> 2) + (r & 3)], pd[r]);
+      // dS/scale replaces P*dP in the scratch for k_dqs (all waves read this
+      // item's tiles before the barrier above; one writer per tile)
+      if (!DSPLIT || (wave & 1) == 0) {
+        float* t = a.scratch + (size_t)cslot * ATTN_TILE_FLOATS + 1024 + lane;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[64 * r] = pd[r];
+      }
       // dV += P^T dO; the Q operands of the dK products and the next item's
       // loads go out between these products
 #pragma unroll
@@ -1223,6 +1242,146 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
         dVh[off] = oldV[r][nb] + accV[nb][r];
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_dqs: dQ += scale * sum_j (dS/scale)_ij k_j from the dS tiles k_dkdv_p left
+// in the scratch.  One workgroup per (query tile, head); wave w owns query
+// block qb and a DW-column slice (DP <= 128: 4 blocks, all columns; DP > 128:
+// 2 blocks x 2 column halves).  The sweep streams 64-key K tiles through LDS
+// (one barrier per tile; 32 keys above 128 columns) and prefetches the
+// wave's dS tiles of the next tile into registers.  dS is zero wherever the mask hides a key, and pairs
+// outside the stored range are skipped, so no masking is needed here.
+// Output columns are permuted as in k_dkdv_p (lane l, block nb: column
+// dcol0 + NB*(l%32) + nb).
+// ---------------------------------------------------------------------------
+template <int DP>
+__global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
+  constexpr bool CSPLIT = DP > 128;
+  constexpr int QB = CSPLIT ? 2 : 4, BR = 32 * QB, KB = CSPLIT ? 1 : 2, BC = 32 * KB;
+  constexpr int DW = CSPLIT ? DP / 2 : DP, NB = DW / 32;
+  constexpr int LDR = DP + 4;
+  constexpr int TILE = PadTile<BC, DP>::FLOATS;
+  constexpr int CPW = PadTile<BC, DP>::CPW;
+  __shared__ __attribute__((aligned(1024))) float sK[2][TILE];
+  __shared__ uint32_t sMin[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int qb = CSPLIT ? (wave >> 1) : wave;
+  const int dcol0 = CSPLIT ? (wave & 1) * DW : 0;
+  const int S = a.S, H = a.H, d = a.d;
+  const int g = H / a.KV;
+  const int qt_hi = (S - 1) / BR;
+  const int qt = qt_hi - (int)(blockIdx.x / H);  // longest rows first
+  const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
+  const int i0 = qt * BR;
+  const int nblk = (S + 31) / 32;
+  const int qblk = (i0 >> 5) + qb;
+  const bool blk_ok = qblk < nblk;
+  // stored pairs of this wave's query block: key blocks [lo, qblk]
+  const int lo = blk_ok ? (int)(a.blk_min[qblk] / 32) : 0x7fffffff;
+  const long long slot0 = blk_ok ? a.slot_off[qblk] - lo : 0;
+  if (lane == 0) sMin[wave] = (blk_ok && lo <= qblk) ? (uint32_t)lo : 0x7fffffffu;
+  __syncthreads();
+  int kb_first = (int)sMin[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) kb_first = min(kb_first, (int)sMin[w]);
+  // key tiles holding a stored pair of some block of the tile (none: empty range)
+  const int last_blk = (min(i0 + BR, S) - 1) / 32;
+  const bool any = kb_first <= last_blk;
+  const int kt_lo = any ? kb_first / KB : 1, kt_hi = any ? last_blk / KB : 0;
+  const size_t kstride = (size_t)a.KV * d;
+  const float* Kh = a.K + (size_t)kvh * d;
+  // lane's offset in a stored tile: dS[query l32][key crow(r, hf)] sits at
+  // st_base + 8*(r/4) + r%4
+  const int st_base = 64 * (4 * (l32 >> 3) + (l32 & 3)) + 32 * ((l32 >> 2) & 1) + 4 * hf;
+
+  f32x16 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = zero16();
+
+  float sn[KB][16];  // the next tile's dS values of this wave (zero when not stored)
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int kb = t * KB + k;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sn[k][r] = 0.f;
+      if (blk_ok && kb >= lo && kb <= qblk) {
+        const float* src = a.scratch + ((slot0 + kb) * H + h) * ATTN_TILE_FLOATS + 1024 + st_base;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float4 v = *reinterpret_cast<const float4*>(src + 8 * m);
+          sn[k][4 * m] = v.x; sn[k][4 * m + 1] = v.y; sn[k][4 * m + 2] = v.z; sn[k][4 * m + 3] = v.w;
+        }
+      }
+    }
+  };
+
+  TileLoader<BC, DP> ld;
+  ld.init(kstride, d, wave, lane);
+  const uint32_t lds_k = lds_addr(&sK[0][0]);
+  if (kt_lo <= kt_hi) {
+    ld.load_all(ld.rsrc(Kh, kt_lo * BC, S, kstride, d, true), lds_k, wave);
+    fetch(kt_lo);
+  }
+  const int ob = (4 * hf) * LDR + dcol0 + NB * l32;
+  int buf = 0;
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    tile_barrier();  // tile kt resident; everyone done with tile kt-1
+    const float* sKt = &sK[buf][0];
+    float sv[KB][16];
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sv[k][r] = sn[k][r];
+    const bool more = kt < kt_hi;
+    if (more) fetch(kt + 1);
+    const i32x4 rk = ld.rsrc(Kh, (kt + 1) * BC, S, kstride, d, more);
+    const uint32_t nxt = lds_k + (buf ^ 1) * (TILE * 4);
+    auto issue = [&](int j) { ld.load(j, rk, nxt, wave); };
+    // (a block pair that holds no stored tile runs on zeros: no branches here)
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float* row = sKt + ob + (32 * k + 8 * (r >> 2) + (r & 3)) * LDR;
+        float kv[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) kv[nb] = row[nb];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma32(sv[k][r], kv[nb], acc[nb]);
+        if (k == 0) SpreadLoads<CPW, 16, decltype(issue)>{issue}(r);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(acc[nb]));
+    buf ^= 1;
+  }
+  tile_barrier();  // the last loads have landed before the LDS is released
+
+  // dQ += scale * acc: all old values are read first, then all written
+  float* __restrict__ dQh = a.dQ + (size_t)h * d;
+  const size_t qstride = (size_t)H * d;
+  const int col0 = dcol0 + NB * l32;
+  float old[16][NB];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = i0 + qb * 32 + crow(r, hf);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      old[r][nb] = (row < S && col0 + nb < d) ? dQh[(size_t)row * qstride + col0 + nb] : 0.f;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = i0 + qb * 32 + crow(r, hf);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      if (row < S && col0 + nb < d)
+        dQh[(size_t)row * qstride + col0 + nb] = old[r][nb] + a.scale * acc[nb][r];
   }
 }
 
@@ -1364,16 +1523,19 @@ static attn_status_t fail(attn_status_t st, const char* fmt, ...) {
 
 extern "C" const char* attn_last_error(void) { return g_err; }
 
-// Per-thread event log of the measurement hooks (see attn_profile_begin).
+// Per-thread event log of the measurement hooks (see attn_profile_begin):
+// per recorded attn_bwd call, one event before its first pass and one after
+// each of its passes (2 or 3).
 struct ProfileLog {
   bool on = false;
-  std::vector<hipEvent_t> ev;  // 3 per recorded attn_bwd call
+  std::vector<std::vector<hipEvent_t>> calls;
 };
 static thread_local ProfileLog g_prof;
 
 static void profile_release() {
-  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
-  g_prof.ev.clear();
+  for (auto& c : g_prof.calls)
+    for (hipEvent_t e : c) (void)hipEventDestroy(e);
+  g_prof.calls.clear();
 }
 
 extern "C" attn_status_t attn_profile_begin(void) {
@@ -1385,33 +1547,35 @@ extern "C" attn_status_t attn_profile_begin(void) {
 
 extern "C" attn_status_t attn_profile_end(double* ms, int* n_calls) {
   g_err[0] = 0;
-  double sum[2] = {0.0, 0.0};
+  double sum[3] = {0.0, 0.0, 0.0};
   attn_status_t rc = ATTN_OK;
-  const size_t n = g_prof.ev.size() / 3;
-  for (size_t i = 0; i < n && rc == ATTN_OK; ++i) {
-    for (int k = 0; k < 2 && rc == ATTN_OK; ++k) {
+  for (size_t i = 0; i < g_prof.calls.size() && rc == ATTN_OK; ++i) {
+    const auto& ev = g_prof.calls[i];
+    for (size_t k = 0; k + 1 < ev.size() && k < 3 && rc == ATTN_OK; ++k) {
       float t = 0.f;
-      hipError_t e = hipEventSynchronize(g_prof.ev[3 * i + k + 1]);
-      if (e == hipSuccess) e = hipEventElapsedTime(&t, g_prof.ev[3 * i + k], g_prof.ev[3 * i + k + 1]);
+      hipError_t e = hipEventSynchronize(ev[k + 1]);
+      if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
       if (e != hipSuccess) rc = fail(ATTN_ERR_HIP, "reading profile events: %s", hipGetErrorString(e));
       sum[k] += t;
     }
   }
-  if (ms) { ms[0] = sum[0]; ms[1] = sum[1]; }
-  if (n_calls) *n_calls = (int)n;
+  if (ms) { ms[0] = sum[0]; ms[1] = sum[1]; ms[2] = sum[2]; }
+  if (n_calls) *n_calls = (int)g_prof.calls.size();
   profile_release();
   g_prof.on = false;
   return rc;
 }
 
-// Record one profile event on `st` if the measurement hooks are on.
-static attn_status_t profile_mark(hipStream_t st) {
+// Record one profile event on `st` if the measurement hooks are on; `first`
+// opens the record of a new call.
+static attn_status_t profile_mark(hipStream_t st, bool first = false) {
   if (!g_prof.on) return ATTN_OK;
   hipEvent_t e;
   hipError_t err = hipEventCreate(&e);
   if (err == hipSuccess) err = hipEventRecord(e, st);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "profile event: %s", hipGetErrorString(err));
-  g_prof.ev.push_back(e);
+  if (first || g_prof.calls.empty()) g_prof.calls.emplace_back();
+  g_prof.calls.back().push_back(e);
   return ATTN_OK;
 }
 
@@ -1447,15 +1611,19 @@ static attn_status_t hip_check(hipError_t e, const char* what) {
   return ATTN_OK;
 }
 
-// k_dq over all query tiles, then the dK/dV kernel over all key tiles (from
-// the stored tiles when a.scratch is set, by recomputing the scores otherwise).
+// With stored tiles (a.scratch set): k_dq storing P and P*dP and emitting D,
+// k_dkdv_p (dK, dV, and dS over P*dP), then k_dqs (dQ).  Without: k_dq
+// accumulating dQ and emitting D, then k_dkdv recomputing the scores.
 template <int DP>
 static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   const int BRq = Pair<DP>::ROLE ? 64 : 128;
   const int nqt = (a.S + BRq - 1) / BRq;
-  attn_status_t rc = profile_mark(st);
+  attn_status_t rc = profile_mark(st, true);
   if (rc != ATTN_OK) return rc;
-  hipLaunchKernelGGL(k_dq<DP>, dim3(nqt * a.H), dim3(256), 0, st, a);
+  if (a.scratch)
+    hipLaunchKernelGGL((k_dq<DP, false>), dim3(nqt * a.H), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_dq<DP, true>), dim3(nqt * a.H), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching k_dq");
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
@@ -1465,6 +1633,11 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching the dK/dV kernel");
+  if (rc == ATTN_OK) rc = profile_mark(st);
+  if (rc != ATTN_OK || !a.scratch) return rc;
+  const int BRs = DP > 128 ? 64 : 128;
+  hipLaunchKernelGGL(k_dqs<DP>, dim3((a.S + BRs - 1) / BRs * a.H), dim3(256), 0, st, a);
+  rc = hip_check(hipGetLastError(), "launching k_dqs");
   if (rc == ATTN_OK) rc = profile_mark(st);
   return rc;
 }

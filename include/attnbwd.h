@@ -126,12 +126,14 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
  * Measurement hooks (benchmarks only; normal callers never need them).
  *
  * attn_profile_begin: from now on, on the calling thread, every attn_bwd call
- *   records HIP events on its stream before, between and after its two main
- *   kernels (the dQ / row-term kernel, then the dK/dV kernel).
- * attn_profile_end: waits for those events, writes into ms[0] and ms[1] the
- *   summed device time in milliseconds of the dQ kernels and of the dK/dV
- *   kernels over the recorded calls, into *n_calls their number, releases
- *   the events and stops recording.  ms and n_calls may be NULL.
+ *   records HIP events on its stream before, between and after its passes:
+ *   the query-major pass (row term D, and dQ or the stored tiles), the
+ *   key-major pass (dK, dV), and -- with stored tiles -- the dQ pass.
+ * attn_profile_end: waits for those events, writes into ms[0], ms[1], ms[2]
+ *   the summed device time in milliseconds of each of the three passes over
+ *   the recorded calls (ms[2] = 0 for calls without the dQ pass), into
+ *   *n_calls their number, releases the events and stops recording.  ms
+ *   (room for 3 doubles) and n_calls may be NULL.
  */
 attn_status_t attn_profile_begin(void);
 attn_status_t attn_profile_end(double* ms, int* n_calls);
