@@ -563,19 +563,39 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 
   TileLoader<BC, DP> ld;
   ld.init(kstride, d, wave, lane);
+  const uint32_t lds_kv = lds_addr(&sKV[0][0]);
   {
     const i32x4 rk = ld.rsrc(Kh, kt_lo * BC, S, kstride, d, true);
     const i32x4 rv = ld.rsrc(Vh, kt_lo * BC, S, kstride, d, true);
-    ld.load_all(rk, &sKV[0][0], wave);
-    ld.load_all(rv, &sKV[0][TILE], wave);
+    ld.load_all(rk, lds_kv, wave);
+    ld.load_all(rv, lds_kv + TILE * 4, wave);
   }
   constexpr int NLOAD = 2 * PadTile<BC, DP>::CPW;  // loads per wave per tile
   int buf = 0;
+  // the previous tile's P and P.dP, stored after the barrier that follows
+  // them: issued just before a barrier, the stores would hold it up until
+  // memory acknowledged them (the barrier's wait counts stores too)
+  bool pend = false;
+  float* pend_at = nullptr;
+  f32x16 pst, pdt;
+  auto flush = [&]() {
+    if (ACC || !pend) return;
+    if (!PG::ROLE || role == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pend_at[8 * (r >> 2) + (r & 3)] = pst[r];
+    }
+    if (!PG::ROLE || role == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pend_at[1024 + 8 * (r >> 2) + (r & 3)] = pdt[r];
+    }
+    pend = false;
+  };
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     tile_barrier();  // tile kt resident; everyone done with tile kt-1
+    flush();
     const float* sK = &sKV[buf][0];
     const float* sV = &sKV[buf][TILE];
-    float* nxt = &sKV[buf ^ 1][0];
+    const uint32_t nxt = lds_kv + (buf ^ 1) * (2 * TILE * 4);
     const int j0 = kt * BC;
     // every key of the tile visible to every query of the block: no masking
     const bool full = rows_full && q_first >= j0 + 31 && mx <= (uint32_t)j0;
@@ -587,7 +607,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     const i32x4 rv = ld.rsrc(Vh, (kt + 1) * BC, S, kstride, d, more);
     auto issue = [&](int j) {
       if (j < NLOAD / 2) ld.load(j, rk, nxt, wave);
-      else ld.load(j - NLOAD / 2, rv, nxt + TILE, wave);
+      else ld.load(j - NLOAD / 2, rv, nxt + TILE * 4, wave);
     };
     const SpreadLoads<NLOAD, PG::TH / 4, decltype(issue)> spread{issue};
 
@@ -636,18 +656,13 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
         dpt[r] = pdp;
       }
     }
-    // P and P.dP of a pair the key-major kernel will read: store them, transposed
-    if (!ACC && store && kt >= kb_lo && kt <= qblk) {
-      float* tile = a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base;
-      if (!PG::ROLE || role == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tile[8 * (r >> 2) + (r & 3)] = st[r];
-      }
-      if (!PG::ROLE || role == 1) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tile[1024 + 8 * (r >> 2) + (r & 3)] = dpt[r];
-      }
-    }
+    // P and P.dP of a pair the key-major kernel will read: kept for storing,
+    // transposed, right after the next barrier
+    // (copied unconditionally, so that the previous values die at the flush)
+    pend = !ACC && store && kt >= kb_lo && kt <= qblk;
+    pend_at = pend ? a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base : nullptr;
+    pst = st;
+    pdt = dpt;
     // A += (P.dP) K,  B += P K over the 32 keys
     if constexpr (ACC) {
 #pragma unroll
@@ -662,6 +677,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     buf ^= 1;
   }
   tile_barrier();  // the last (empty) loads have landed before the LDS is reused or released
+  flush();
 
   // D of this lane's query: the two half-waves saw disjoint keys
   const float Dq = Dp + __shfl_xor(Dp, 32);
@@ -773,6 +789,7 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   };
   TileLoader<BR, DP> ld;
   ld.init(qstride, d, wave, lane);
+  const uint32_t lds_qg = lds_addr(&sQG[0][0]);
   // per-row values of a tile, one wave-wide 4-byte load per wave: wave 0 LSE,
   // wave 1 D (rows H floats apart), wave 2 seg, wave 3 nothing (empty range
   // into a spare slot); lanes past the tile read nothing
@@ -806,8 +823,8 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   if (qt >= 0) {
     const i32x4 rq = ld.rsrc(a.Q + (size_t)(kvh * g) * d, qt * BR, S, qstride, d, true);
     const i32x4 rg = ld.rsrc(a.dO + (size_t)(kvh * g) * d, qt * BR, S, qstride, d, true);
-    ld.load_all(rq, &sQG[0][0], wave);
-    ld.load_all(rg, &sQG[0][TILE], wave);
+    ld.load_all(rq, lds_qg, wave);
+    ld.load_all(rg, lds_qg + TILE * 4, wave);
     dma4(row_rsrc(qt, 0, true), row_off, &sRow[0][wave][0]);
     next_item(qt, 0, nqt_, nhh);
     const int bi = qt * QS + qs;  // may not exist in a partial last tile
@@ -829,12 +846,12 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     const i32x4 rq = ld.rsrc(a.Q + (size_t)nh_ * d, nqt_ * BR, S, qstride, d, more);
     const i32x4 rg = ld.rsrc(a.dO + (size_t)nh_ * d, nqt_ * BR, S, qstride, d, more);
     const i32x4 rr = row_rsrc(nqt_, nhh, more);
-    float* nxt = &sQG[buf ^ 1][0];
+    const uint32_t nxt = lds_qg + (buf ^ 1) * (2 * TILE * 4);
     float* nrow = &sRow[buf ^ 1][wave][0];
     auto issue = [&](int j) {
       constexpr int C = PadTile<BR, DP>::CPW;
       if (j < C) ld.load(j, rq, nxt, wave);
-      else if (j < 2 * C) ld.load(j - C, rg, nxt + TILE, wave);
+      else if (j < 2 * C) ld.load(j - C, rg, nxt + TILE * 4, wave);
       else dma4(rr, row_off, nrow);
     };
     const SpreadLoads<NLOAD, PG::TH / 4, decltype(issue)> spread{issue};
@@ -1343,19 +1360,23 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
     const i32x4 rk = ld.rsrc(Kh, (kt + 1) * BC, S, kstride, d, more);
     const uint32_t nxt = lds_k + (buf ^ 1) * (TILE * 4);
     auto issue = [&](int j) { ld.load(j, rk, nxt, wave); };
-    // (a block pair that holds no stored tile runs on zeros: no branches here)
+    // (a block pair that holds no stored tile runs on zeros: no branches
+    // here); step u = 16k + r, its K operands read one step ahead
+    auto krow = [&](int u) { return sKt + ob + (32 * (u >> 4) + 8 * ((u >> 2) & 3) + (u & 3)) * LDR; };
+    float kv[NB];
 #pragma unroll
-    for (int k = 0; k < KB; ++k) {
+    for (int nb = 0; nb < NB; ++nb) kv[nb] = krow(0)[nb];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float* row = sKt + ob + (32 * k + 8 * (r >> 2) + (r & 3)) * LDR;
-        float kv[NB];
+    for (int u = 0; u < 16 * KB; ++u) {
+      float kn[NB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) kv[nb] = row[nb];
+      for (int nb = 0; nb < NB; ++nb) kn[nb] = u + 1 < 16 * KB ? krow(u + 1)[nb] : kv[nb];
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads a full step ahead
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma32(sv[k][r], kv[nb], acc[nb]);
-        if (k == 0) SpreadLoads<CPW, 16, decltype(issue)>{issue}(r);
-      }
+      for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma32(sv[u >> 4][u & 15], kv[nb], acc[nb]);
+      if (u < 16) SpreadLoads<CPW, 16, decltype(issue)>{issue}(u);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) kv[nb] = kn[nb];
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+a"(acc[nb]));
