@@ -49,13 +49,19 @@ def _load():
     lib.oracle_attn_fwd_f64.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_double, I]
     lib.oracle_attn_bwd_f64.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I,
                                         ctypes.c_double, I]
+    lib.oracle_attn_bwd_o_f64.argtypes = [P, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I,
+                                          ctypes.c_double, I]
     lib.oracle_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, ctypes.c_float, I]
     lib.oracle_attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_float, I]
+    lib.oracle_attn_bwd_o.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_float, I]
     lib.oracle_attn_bwd_rows.argtypes = [P, P, P, P, P, P, P, I, P, I, P, P, P, I, I, I, I,
                                          ctypes.c_float, I]
+    lib.oracle_attn_bwd_rows_o.argtypes = [P, P, P, P, P, P, P, P, I, P, I, P, P, P, I, I, I, I,
+                                           ctypes.c_float, I]
     lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I, ctypes.c_float, I]
-    for f in (lib.oracle_attn_fwd_f64, lib.oracle_attn_bwd_f64, lib.oracle_attn_fwd,
-              lib.oracle_attn_bwd, lib.oracle_attn_bwd_rows, lib.oracle_attn_fwd_rows):
+    for f in (lib.oracle_attn_fwd_f64, lib.oracle_attn_bwd_f64, lib.oracle_attn_bwd_o_f64,
+              lib.oracle_attn_fwd, lib.oracle_attn_bwd, lib.oracle_attn_bwd_o,
+              lib.oracle_attn_bwd_rows, lib.oracle_attn_bwd_rows_o, lib.oracle_attn_fwd_rows):
         f.restype = I
     _lib = lib
     return lib
@@ -122,12 +128,15 @@ def attn_fwd_f64(Q, K, V, seg, scale, nthreads=0):
     return O, LSE
 
 
-def attn_bwd_f64(Q, K, V, dO, LSE, seg, scale, nthreads=0, debug=False):
+def attn_bwd_f64(Q, K, V, dO, LSE, seg, scale, nthreads=0, debug=False, O=None):
     """fp64 backward gradients of this call (no accumulation).
 
-    Returns (dQ, dK, dV), plus (D, rowsum_dS) [S,H] when ``debug``.
+    With ``O`` (the forward output [S,H,d]) the row term is D = dO . O instead
+    of sum_j P * dP.  Returns (dQ, dK, dV), plus (D, rowsum_dS) [S,H] when
+    ``debug``.
     """
     Q, K, V, dO, LSE = (np.ascontiguousarray(x, dtype=np.float64) for x in (Q, K, V, dO, LSE))
+    O = None if O is None else np.ascontiguousarray(O, dtype=np.float64)
     S, H, KV, d = _dims(Q, K)
     seg = _seg(seg, S)
     dQ = np.zeros((S, H, d), np.float64)
@@ -135,9 +144,12 @@ def attn_bwd_f64(Q, K, V, dO, LSE, seg, scale, nthreads=0, debug=False):
     dV = np.zeros((S, KV, d), np.float64)
     D = np.zeros((S, H), np.float64)
     rs = np.zeros((S, H), np.float64)
-    _check(_load().oracle_attn_bwd_f64(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(seg),
-                                       _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(D), _ptr(rs),
-                                       S, H, KV, d, float(scale), nthreads), "attn_bwd_f64")
+    if O is not None:
+        assert O.shape == Q.shape
+    _check(_load().oracle_attn_bwd_o_f64(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
+                                         _ptr(seg), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(D),
+                                         _ptr(rs), S, H, KV, d, float(scale), nthreads),
+           "attn_bwd_f64")
     if debug:
         return dQ, dK, dV, D, rs
     return dQ, dK, dV
@@ -155,29 +167,34 @@ def attn_fwd(Q, K, V, seg, scale, nthreads=0, want_o=True):
     return O, LSE
 
 
-def attn_bwd(Q, K, V, dO, LSE, seg, scale, dQ=None, dK=None, dV=None, nthreads=0):
+def attn_bwd(Q, K, V, dO, LSE, seg, scale, dQ=None, dK=None, dV=None, nthreads=0, O=None):
     """fp32 backward with "+=" semantics on dQ, dK, dV (zeros when not given).
 
-    Returns the (updated) float32 arrays (dQ, dK, dV).
+    With ``O`` (the forward output) the row term is D = dO . O.  Returns the
+    (updated) float32 arrays (dQ, dK, dV).
     """
     Q, K, V, dO, LSE = (np.ascontiguousarray(x, dtype=np.float32) for x in (Q, K, V, dO, LSE))
+    O = None if O is None else np.ascontiguousarray(O, dtype=np.float32)
     S, H, KV, d = _dims(Q, K)
     seg = _seg(seg, S)
     dQ = np.zeros((S, H, d), np.float32) if dQ is None else np.array(dQ, np.float32, order="C")
     dK = np.zeros((S, KV, d), np.float32) if dK is None else np.array(dK, np.float32, order="C")
     dV = np.zeros((S, KV, d), np.float32) if dV is None else np.array(dV, np.float32, order="C")
-    _check(_load().oracle_attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(seg),
-                                   _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
-                                   np.float32(scale), nthreads), "attn_bwd")
+    if O is not None:
+        assert O.shape == Q.shape
+    _check(_load().oracle_attn_bwd_o(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
+                                     _ptr(seg), _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
+                                     np.float32(scale), nthreads), "attn_bwd")
     return dQ, dK, dV
 
 
-def attn_bwd_rows(Q, K, V, dO, LSE, seg, scale, q_rows, k_rows, nthreads=0):
-    """fp64 gradients for selected rows only.
+def attn_bwd_rows(Q, K, V, dO, LSE, seg, scale, q_rows, k_rows, nthreads=0, O=None):
+    """fp64 gradients for selected rows only (with ``O``: D = dO . O).
 
     Returns (dQ_sel [nq,H,d], dK_sel [nk,KV,d], dV_sel [nk,KV,d]).
     """
     Q, K, V, dO, LSE = (np.ascontiguousarray(x, dtype=np.float32) for x in (Q, K, V, dO, LSE))
+    O = None if O is None else np.ascontiguousarray(O, dtype=np.float32)
     S, H, KV, d = _dims(Q, K)
     seg = _seg(seg, S)
     q_rows = np.ascontiguousarray(q_rows, dtype=np.int32)
@@ -185,10 +202,12 @@ def attn_bwd_rows(Q, K, V, dO, LSE, seg, scale, q_rows, k_rows, nthreads=0):
     dQ = np.zeros((len(q_rows), H, d), np.float64)
     dK = np.zeros((len(k_rows), KV, d), np.float64)
     dV = np.zeros((len(k_rows), KV, d), np.float64)
-    _check(_load().oracle_attn_bwd_rows(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(seg),
-                                        _ptr(q_rows), len(q_rows), _ptr(k_rows), len(k_rows),
-                                        _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
-                                        np.float32(scale), nthreads), "attn_bwd_rows")
+    if O is not None:
+        assert O.shape == Q.shape
+    _check(_load().oracle_attn_bwd_rows_o(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
+                                          _ptr(seg), _ptr(q_rows), len(q_rows), _ptr(k_rows),
+                                          len(k_rows), _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
+                                          np.float32(scale), nthreads), "attn_bwd_rows")
     return dQ, dK, dV
 
 

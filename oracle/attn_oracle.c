@@ -43,10 +43,15 @@
  * float entry points round once at the end: out = (float)((double)init + g).
  * No -ffast-math.
  *
+ * The _o entry points take the forward output O and read the row term off it
+ * (D = dO . O, see bwd_row); the others compute D = sum_j P * dP.
+ *
  * Parity status: every function here is pinned by the CPU tests (finite
  * differences, sum_j dS = 0, masked-key zeros, plain-causal equality with an
  * independent dense implementation, packed == per-document, GQA == replicated
- * MHA, closed forms, linearity / "+=").
+ * MHA, closed forms, linearity / "+="; for the _o entry points: agreement with
+ * D = sum_j P * dP at the exact forward output, and the closed-form effect of
+ * a perturbed O on each gradient).
  */
 #include <math.h>
 #include <pthread.h>
@@ -63,6 +68,7 @@ typedef struct {
   const uint32_t *seg; /* NULL means all zeros */
   int S, H, KV, d;
   double scale;
+  const double *O; /* forward output [S,H,d]: when given, D = dO . O (see bwd_row) */
 } problem_t;
 
 static long first_key(const problem_t *p, long s) { return p->seg ? (long)p->seg[s] : 0; }
@@ -230,6 +236,11 @@ static void bwd_row(void *vctx, long item) {
     dP[j - lo] = dprob(p, s, h, j);
     D += P[j - lo] * dP[j - lo];
   }
+  /* With the forward output given, the row term is read off it instead:
+   * sum_j P_j (dO . v_j) = dO . (sum_j P_j v_j) = dO . O, where O is the
+   * forward's probability-weighted sum of V (page "tang 0.2.0 --
+   * src/gpu/llm.rs", causal_attention_fused). */
+  if (p->O) D = dot(q_row(p, p->dO, s, h), q_row(p, p->O, s, h), p->d);
   c->D[r] = D;
   int want_dq = c->dQ && (!c->dq_needed || c->dq_needed[s]);
   double *dq = want_dq ? c->dQ + r * d : NULL;
@@ -275,15 +286,16 @@ static void bwd_key(void *vctx, long item) {
   }
 }
 
-/* Gradients of this call (no accumulation), fp64 in and out.  D_out and
- * rowsum_dS are optional debug outputs [S,H]. */
-int oracle_attn_bwd_f64(const double *Q, const double *K, const double *V, const double *dO,
-                        const double *LSE, const uint32_t *seg, double *dQ, double *dK,
-                        double *dV, double *D_out, double *rowsum_dS, int S, int H, int KV,
-                        int d, double scale, int nthreads) {
+/* Gradients of this call (no accumulation), fp64 in and out.  O (may be
+ * NULL) is the forward output: when given, D = dO . O.  D_out and rowsum_dS
+ * are optional debug outputs [S,H]. */
+int oracle_attn_bwd_o_f64(const double *Q, const double *K, const double *V, const double *O,
+                          const double *dO, const double *LSE, const uint32_t *seg, double *dQ,
+                          double *dK, double *dV, double *D_out, double *rowsum_dS, int S, int H,
+                          int KV, int d, double scale, int nthreads) {
   if (check_dims(S, H, KV, d)) return 1;
   if (S == 0) return 0;
-  problem_t p = {Q, K, V, dO, LSE, seg, S, H, KV, d, scale};
+  problem_t p = {Q, K, V, dO, LSE, seg, S, H, KV, d, scale, O};
   double *D = D_out ? D_out : (double *)malloc(sizeof(double) * (size_t)S * H);
   if (!D) return 2;
   bwd_ctx_t c = {&p, D, rowsum_dS, dQ, dK, dV, NULL, NULL, NULL};
@@ -291,6 +303,14 @@ int oracle_attn_bwd_f64(const double *Q, const double *K, const double *V, const
   if (dK && dV) parallel_for((long)S * KV, nthreads, bwd_key, &c);
   if (!D_out) free(D);
   return 0;
+}
+
+int oracle_attn_bwd_f64(const double *Q, const double *K, const double *V, const double *dO,
+                        const double *LSE, const uint32_t *seg, double *dQ, double *dK,
+                        double *dV, double *D_out, double *rowsum_dS, int S, int H, int KV,
+                        int d, double scale, int nthreads) {
+  return oracle_attn_bwd_o_f64(Q, K, V, NULL, dO, LSE, seg, dQ, dK, dV, D_out, rowsum_dS, S, H,
+                               KV, d, scale, nthreads);
 }
 
 /* ------------------------------------------------------------------ */
@@ -368,30 +388,39 @@ int oracle_attn_fwd(const float *Q, const float *K, const float *V, const uint32
   return rc;
 }
 
-/* fp32 inputs; dQ, dK, dV are accumulated: out = fp32(fp64(out) + gradient). */
-int oracle_attn_bwd(const float *Q, const float *K, const float *V, const float *dO,
-                    const float *LSE, const uint32_t *seg, float *dQ, float *dK, float *dV, int S,
-                    int H, int KV, int d, float scale, int nthreads) {
+/* fp32 inputs; dQ, dK, dV are accumulated: out = fp32(fp64(out) + gradient).
+ * O (may be NULL) is the forward output: when given, D = dO . O. */
+int oracle_attn_bwd_o(const float *Q, const float *K, const float *V, const float *O,
+                      const float *dO, const float *LSE, const uint32_t *seg, float *dQ,
+                      float *dK, float *dV, int S, int H, int KV, int d, float scale,
+                      int nthreads) {
   if (check_dims(S, H, KV, d)) return 1;
   if (S == 0) return 0;
   size_t nq = (size_t)S * H * d, nk = (size_t)S * KV * d, nr = (size_t)S * H;
   double *q = widen(Q, nq), *k = widen(K, nk), *v = widen(V, nk), *g = widen(dO, nq);
   double *l = widen(LSE, nr);
+  double *o = O ? widen(O, nq) : NULL;
   double *gq = (double *)malloc(sizeof(double) * nq);
   double *gk = (double *)malloc(sizeof(double) * nk);
   double *gv = (double *)malloc(sizeof(double) * nk);
   int rc = 2;
-  if (q && k && v && g && l && gq && gk && gv) {
-    rc = oracle_attn_bwd_f64(q, k, v, g, l, seg, gq, gk, gv, NULL, NULL, S, H, KV, d,
-                             (double)scale, nthreads);
+  if (q && k && v && g && l && gq && gk && gv && (o || !O)) {
+    rc = oracle_attn_bwd_o_f64(q, k, v, o, g, l, seg, gq, gk, gv, NULL, NULL, S, H, KV, d,
+                               (double)scale, nthreads);
     for (size_t i = 0; i < nq; ++i) dQ[i] = (float)((double)dQ[i] + gq[i]);
     for (size_t i = 0; i < nk; ++i) {
       dK[i] = (float)((double)dK[i] + gk[i]);
       dV[i] = (float)((double)dV[i] + gv[i]);
     }
   }
-  free(q); free(k); free(v); free(g); free(l); free(gq); free(gk); free(gv);
+  free(q); free(k); free(v); free(g); free(l); free(o); free(gq); free(gk); free(gv);
   return rc;
+}
+
+int oracle_attn_bwd(const float *Q, const float *K, const float *V, const float *dO,
+                    const float *LSE, const uint32_t *seg, float *dQ, float *dK, float *dV, int S,
+                    int H, int KV, int d, float scale, int nthreads) {
+  return oracle_attn_bwd_o(Q, K, V, NULL, dO, LSE, seg, dQ, dK, dV, S, H, KV, d, scale, nthreads);
 }
 
 /* Selected rows only, for checks at sizes where the full backward is slow:
@@ -399,11 +428,11 @@ int oracle_attn_bwd(const float *Q, const float *K, const float *V, const float 
  * k_rows[0..nk) -> dK_sel, dV_sel [nk, KV, d].  Outputs are the fp64
  * gradients of this call (no accumulation).  D is computed only for the rows
  * the selection needs. */
-int oracle_attn_bwd_rows(const float *Q, const float *K, const float *V, const float *dO,
-                         const float *LSE, const uint32_t *seg, const int32_t *q_rows, int nq,
-                         const int32_t *k_rows, int nk, double *dQ_sel, double *dK_sel,
-                         double *dV_sel, int S, int H, int KV, int d, float scale,
-                         int nthreads) {
+int oracle_attn_bwd_rows_o(const float *Q, const float *K, const float *V, const float *O,
+                           const float *dO, const float *LSE, const uint32_t *seg,
+                           const int32_t *q_rows, int nq, const int32_t *k_rows, int nk,
+                           double *dQ_sel, double *dK_sel, double *dV_sel, int S, int H, int KV,
+                           int d, float scale, int nthreads) {
   if (check_dims(S, H, KV, d) || nq < 0 || nk < 0) return 1;
   for (int i = 0; i < nq; ++i)
     if (q_rows[i] < 0 || q_rows[i] >= S) return 1;
@@ -413,6 +442,7 @@ int oracle_attn_bwd_rows(const float *Q, const float *K, const float *V, const f
   size_t n_q = (size_t)S * H * d, n_k = (size_t)S * KV * d, nr = (size_t)S * H;
   double *q = widen(Q, n_q), *k = widen(K, n_k), *v = widen(V, n_k), *g = widen(dO, n_q);
   double *l = widen(LSE, nr);
+  double *o = O ? widen(O, n_q) : NULL;
   double *D = (double *)calloc(nr, sizeof(double));
   double *gq = (double *)calloc(n_q, sizeof(double));
   double *gk = (double *)calloc(n_k, sizeof(double));
@@ -421,8 +451,9 @@ int oracle_attn_bwd_rows(const float *Q, const float *K, const float *V, const f
   unsigned char *dq_needed = (unsigned char *)calloc((size_t)S, 1);
   unsigned char *key_needed = (unsigned char *)calloc((size_t)S, 1);
   int rc = 2;
-  if (q && k && v && g && l && D && gq && gk && gv && row_needed && dq_needed && key_needed) {
-    problem_t p = {q, k, v, g, l, seg, S, H, KV, d, (double)scale};
+  if (q && k && v && g && l && D && gq && gk && gv && row_needed && dq_needed && key_needed &&
+      (o || !O)) {
+    problem_t p = {q, k, v, g, l, seg, S, H, KV, d, (double)scale, o};
     for (int i = 0; i < nq; ++i) row_needed[q_rows[i]] = dq_needed[q_rows[i]] = 1;
     for (int i = 0; i < nk; ++i) {
       long j = k_rows[i];
@@ -443,7 +474,16 @@ int oracle_attn_bwd_rows(const float *Q, const float *K, const float *V, const f
     }
     rc = 0;
   }
-  free(q); free(k); free(v); free(g); free(l); free(D); free(gq); free(gk); free(gv);
+  free(q); free(k); free(v); free(g); free(l); free(o); free(D); free(gq); free(gk); free(gv);
   free(row_needed); free(dq_needed); free(key_needed);
   return rc;
+}
+
+int oracle_attn_bwd_rows(const float *Q, const float *K, const float *V, const float *dO,
+                         const float *LSE, const uint32_t *seg, const int32_t *q_rows, int nq,
+                         const int32_t *k_rows, int nk, double *dQ_sel, double *dK_sel,
+                         double *dV_sel, int S, int H, int KV, int d, float scale,
+                         int nthreads) {
+  return oracle_attn_bwd_rows_o(Q, K, V, NULL, dO, LSE, seg, q_rows, nq, k_rows, nk, dQ_sel,
+                                dK_sel, dV_sel, S, H, KV, d, scale, nthreads);
 }
