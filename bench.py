@@ -111,6 +111,8 @@ def main():
                     help="KV groups in the oracle's timed sample (0: skip the CPU baseline)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--o-entry", action="store_true",
+                    help="time attn_bwd_o (row term read off the forward output O) instead")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
@@ -132,7 +134,8 @@ def main():
     seg = None if not np.any(seg_np) else torch.from_numpy(seg_np.astype(np.int32)).to(dev)
     scale = float(x["scale"])
     lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
-    binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, None, lse, scale)
+    O = torch.empty_like(t["Q"]) if args.o_entry else None
+    binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, O, lse, scale)
     ws_bytes, stored = binding.bwd_plan(w.S, w.H, w.KV, w.d)
     log(f"bench: workspace {ws_bytes / 2**30:.2f} GiB, "
         f"{'stored' if stored else 'recomputed'} probability tiles")
@@ -142,7 +145,10 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], lse, seg, dQ, dK, dV, scale)
+        if args.o_entry:
+            binding.attn_bwd_o(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
+        else:
+            binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], lse, seg, dQ, dK, dV, scale)
 
     for _ in range(args.warmup):
         step()
@@ -177,6 +183,8 @@ def main():
     # (2*d per contraction): with stored tiles k_dq forms S = Q.K^T and
     # dP = dO.V^T, k_dkdv_p P^T.dO and dS^T.Q, k_dqs dS.K; recomputing, k_dq
     # forms Q.K^T, dO.V^T and dS.K (with the row term), k_dkdv all four
+    # (the O entry's row-term kernel, k_rowdot, runs before the first pass and
+    # is in ms_per_step only)
     if stored:
         passes = [("k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0), ("k_dqs", ms_s, 2.0)]
     else:
@@ -222,6 +230,7 @@ def main():
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
                    "head_dim": w.d, "mask": "causal" if seg is None else "documents",
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
+                   "entry": "attn_bwd_o" if args.o_entry else "attn_bwd",
                    "stored_tiles": stored,
                    "workspace_bytes": ws_bytes,
                    "kernel_ms": kernel_ms},

@@ -13,7 +13,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_bwd_plan", "attn_fwd_lse", "attn_last_error",
+EXPORTED = ("attn_bwd", "attn_bwd_o", "attn_bwd_plan", "attn_fwd_lse", "attn_last_error",
             "attn_profile_begin", "attn_profile_end")
 
 _lib = None
@@ -37,6 +37,8 @@ def load():
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd.restype = I
+    lib.attn_bwd_o.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_bwd_o.restype = I
     lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                   ctypes.POINTER(ctypes.c_int)]
     lib.attn_bwd_plan.restype = I
@@ -94,28 +96,46 @@ def _dims(Q, K):
     return S, H, K.shape[1], d
 
 
+def _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV):
+    import torch
+    S, H, KV, d = _dims(Q, K)
+    f32 = (torch.float32,)
+    _check_tensors([("Q", Q, f32), ("K", K, f32), ("V", V, f32), ("O", O, f32), ("dO", dO, f32),
+                    ("LSE", LSE, f32), ("seg", seg, (torch.int32, torch.uint32)),
+                    ("dQ", dQ, f32), ("dK", dK, f32), ("dV", dV, f32)], Q.device)
+    for name, t, shape in (("V", V, K.shape), ("O", O, Q.shape), ("dO", dO, Q.shape),
+                           ("LSE", LSE, (S, H)), ("dQ", dQ, Q.shape), ("dK", dK, K.shape),
+                           ("dV", dV, K.shape)):
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if seg is not None and tuple(seg.shape) != (S,):
+        raise ValueError(f"seg has shape {tuple(seg.shape)}, expected ({S},)")
+    return S, H, KV, d
+
+
 def attn_bwd(Q, K, V, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
     """dQ += ..., dK += ..., dV += ... (the C ABI's attn_bwd) on torch device tensors.
 
     Q, dO, dQ [S,H,d]; K, V, dK, dV [S,KV,d]; LSE [S,H] float32; seg [S]
     int32/uint32 document starts or None (plain causal).
     """
-    import torch
-    S, H, KV, d = _dims(Q, K)
-    f32 = (torch.float32,)
-    _check_tensors([("Q", Q, f32), ("K", K, f32), ("V", V, f32), ("dO", dO, f32),
-                    ("LSE", LSE, f32), ("seg", seg, (torch.int32, torch.uint32)),
-                    ("dQ", dQ, f32), ("dK", dK, f32), ("dV", dV, f32)], Q.device)
-    for name, t, shape in (("V", V, K.shape), ("dO", dO, Q.shape), ("LSE", LSE, (S, H)),
-                           ("dQ", dQ, Q.shape), ("dK", dK, K.shape), ("dV", dV, K.shape)):
-        if tuple(t.shape) != tuple(shape):
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if seg is not None and tuple(seg.shape) != (S,):
-        raise ValueError(f"seg has shape {tuple(seg.shape)}, expected ({S},)")
+    S, H, KV, d = _bwd_args(Q, K, V, None, dO, LSE, seg, dQ, dK, dV)
     st = load().attn_bwd(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(seg),
                          _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                          _stream(stream))
     _raise_on(st, "attn_bwd")
+
+
+def attn_bwd_o(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
+    """attn_bwd with the forward output O [S,H,d] given (the C ABI's attn_bwd_o):
+    the row term is read off it, D = dO . O."""
+    if O is None:
+        raise ValueError("attn_bwd_o needs the forward output O")
+    S, H, KV, d = _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV)
+    st = load().attn_bwd_o(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(seg),
+                           _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
+                           _stream(stream))
+    _raise_on(st, "attn_bwd_o")
 
 
 def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):

@@ -468,6 +468,36 @@ __global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint3
   if (t == 0) slot_off[nblk] = carry;
 }
 
+// ---------------------------------------------------------------------------
+// k_rowdot: the row term read off the forward output, D[s, h] = dO[s, h, :] .
+// O[s, h, :] (rows s*H + h of the [S, H, d] tensors).  A group of TPR lanes
+// (a power of two covering the row's d/4 float4s) takes one row; a wave takes
+// 64/TPR rows per step of a grid-stride loop whose trip count is the same for
+// every lane of a wave (the group sums are shuffles).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rowdot(const float* __restrict__ O,
+                                                const float* __restrict__ dO, float* D,
+                                                long long rows, int d) {
+  const int lane = threadIdx.x & 63;
+  const int nf4 = d / 4;
+  int tpr = 1;
+  while (tpr < nf4) tpr <<= 1;
+  const int rpw = 64 / tpr, sub = lane / tpr, part = lane % tpr;
+  const long long wave = ((long long)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const long long nwaves = (long long)gridDim.x * (blockDim.x / 64);
+  for (long long r0 = wave * rpw; r0 < rows; r0 += nwaves * rpw) {
+    const long long row = r0 + sub;
+    float acc = 0.f;
+    if (row < rows && part < nf4) {
+      const float4 x = reinterpret_cast<const float4*>(O + row * d)[part];
+      const float4 y = reinterpret_cast<const float4*>(dO + row * d)[part];
+      acc = x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+    }
+    for (int o = tpr / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+    if (row < rows && part == 0) D[row] = acc;
+  }
+}
+
 // The P / P*dP scratch holds, per slot and head, two 32x32 tiles (P, then
 // P*dP) of one (query block, key block) pair, stored in the register layout
 // of the key-major kernel: element R*64 + L is what its lane L holds in
@@ -483,8 +513,11 @@ __global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint3
 //   ACC = true:  D and dQ (A, B accumulated as above, dQ = scale*(A - D*B)).
 //   ACC = false: D, and the P and P*dP tiles of every visible pair stored for
 //                the key-major kernel (which then forms dS; k_dqs adds dS*K).
+//   DK = true:   D is given (in a.Dws, from the forward output), so dS/scale =
+//                P*(dP - D) is formed here: ACC accumulates dQ = scale*sum dS K
+//                alone (3 contractions), !ACC stores dS/scale in place of P*dP.
 // ---------------------------------------------------------------------------
-template <int DP, bool ACC>
+template <int DP, bool ACC, bool DK>
 __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   using PG = Pair<DP>;
   constexpr int QB = PG::ROLE ? 2 : 4, BR = 32 * QB, BC = 32;
@@ -525,6 +558,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   }
   pin_agpr<PG::TH>(qr);
   const float lse2 = q_ok ? a.LSE[(size_t)q * H + h] * ATTN_LOG2E : 0.f;
+  const float Dk = (DK && q_ok) ? a.Dws[(size_t)q * H + h] : 0.f;  // given row term
   const uint32_t sq = (q_ok && a.seg) ? a.seg[q] : 0u;
 
   // smallest document start of the tile bounds the key sweep; the largest one
@@ -553,10 +587,13 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   const int last_q = min(i0 + BR, S) - 1;
   const int kt_lo = (int)(min(tmin, (uint32_t)last_q) / BC), kt_hi = last_q / BC;
 
-  f32x16 accA[ACC ? PG::NB : 1], accB[ACC ? PG::NB : 1];
+  f32x16 accA[ACC ? PG::NB : 1], accB[ACC && !DK ? PG::NB : 1];
   if constexpr (ACC) {
 #pragma unroll
-    for (int nb = 0; nb < PG::NB; ++nb) { accA[nb] = zero16(); accB[nb] = zero16(); }
+    for (int nb = 0; nb < PG::NB; ++nb) {
+      accA[nb] = zero16();
+      if constexpr (!DK) accB[nb] = zero16();
+    }
   }
   float Dp = 0.f;
   const int dcol0 = role * PG::DW;
@@ -633,13 +670,13 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       score_pair<DP>(sK, sV, l32, hf, qr, gr, st, dpt, spread);
     }
 
-    // P and P*dP in place; this lane's query, key = j0 + crow(r, hf)
+    // P and P*dP (DK: P*(dP - D)) in place; this lane's query, key = j0 + crow(r, hf)
     if (full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[r], sc2, -lse2));
-        const float pdp = p * dpt[r];
-        Dp += pdp;
+        const float pdp = p * (DK ? dpt[r] - Dk : dpt[r]);
+        if constexpr (!DK) Dp += pdp;
         st[r] = p;
         dpt[r] = pdp;
       }
@@ -650,8 +687,8 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
         const bool vis = q_ok && key <= q && (uint32_t)key >= sq;
         const float e = __builtin_amdgcn_exp2f(fmaf(st[r], sc2, -lse2));
         const float p = vis ? e : 0.f;
-        const float pdp = vis ? p * dpt[r] : 0.f;
-        Dp += pdp;
+        const float pdp = vis ? p * (DK ? dpt[r] - Dk : dpt[r]) : 0.f;
+        if constexpr (!DK) Dp += pdp;
         st[r] = p;
         dpt[r] = pdp;
       }
@@ -663,13 +700,13 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     pend_at = pend ? a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base : nullptr;
     pst = st;
     pdt = dpt;
-    // A += (P.dP) K,  B += P K over the 32 keys
+    // A += (P.dP) K,  B += P K over the 32 keys (DK: A += (dS/scale) K only)
     if constexpr (ACC) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
 #pragma unroll
         for (int nb = 0; nb < PG::NB; ++nb) {
-          accB[nb] = mfma32(st[r], kv[r][nb], accB[nb]);
+          if constexpr (!DK) accB[nb] = mfma32(st[r], kv[r][nb], accB[nb]);
           accA[nb] = mfma32(dpt[r], kv[r][nb], accA[nb]);
         }
       }
@@ -680,9 +717,11 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   flush();
 
   // D of this lane's query: the two half-waves saw disjoint keys
-  const float Dq = Dp + __shfl_xor(Dp, 32);
-  if (ACC && hf == 0) sD[wave * 32 + l32] = Dq;
-  if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * H + h] = Dq;
+  if constexpr (!DK) {
+    const float Dq = Dp + __shfl_xor(Dp, 32);
+    if (ACC && hf == 0) sD[wave * 32 + l32] = Dq;
+    if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * H + h] = Dq;
+  }
   if constexpr (ACC) {
     __syncthreads();
     // dQ += scale * (A - D B): all old values are read first, then all written
@@ -704,9 +743,13 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int m = crow(r, hf);
         const int row = i0 + qb * 32 + m;
-        if (row < S && col < d)
-          dQh[(size_t)row * qstride + col] =
-              old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
+        if (row < S && col < d) {
+          if constexpr (DK)
+            dQh[(size_t)row * qstride + col] = old[nb][r] + a.scale * accA[nb][r];
+          else
+            dQh[(size_t)row * qstride + col] =
+                old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
+        }
       }
     }
   }
@@ -995,9 +1038,10 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 // products are not recomputed: per (query block, key block, head) the wave
 // loads the two stored tiles (prefetched one item ahead into registers),
 // forms dS/scale = P*dP - P*D (written back over P*dP for k_dqs) and runs
-// the two accumulations dV += P^T dO and dK += (dS/scale)^T Q.  Above 128
-// columns the two waves of a key block split the output columns instead of
-// the query rows.
+// the two accumulations dV += P^T dO and dK += (dS/scale)^T Q.  With a given
+// row term (DK) the second tile already holds dS/scale.  Above 128 columns
+// the two waves of a key block split the output columns instead of the query
+// rows.
 //
 // Output columns are permuted: lane l's accumulator block nb holds column
 // dcol0 + NB*(l%32) + nb, so that the NB operands a lane needs per step are
@@ -1009,7 +1053,7 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 // wave's block pair.  The walk over a segment is scalar bit arithmetic, so no
 // memory read sits between an item and the next one's prefetch.
 // ---------------------------------------------------------------------------
-template <int DP>
+template <int DP, bool DK>
 __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   constexpr bool DSPLIT = DP > 128;
   constexpr int KB = 2, QS = DSPLIT ? 1 : 2, BC = 32 * KB, BR = 32 * QS;
@@ -1124,7 +1168,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
     const i32x4 rg = ld.rsrc(a.dO + (size_t)(head0 + hh) * d, t * BR, S, qstride, d, true);
     ld.load_all(rq, lds_qg, wave);
     ld.load_all(rg, lds_qg + TILE * 4, wave);
-    dma4(row_rsrc(t, hh, true), row_off, lds_row);
+    if constexpr (!DK) dma4(row_rsrc(t, hh, true), row_off, lds_row);
     cslot = item_slot(li, hh);
     fetch_tiles(cslot);
   }
@@ -1156,9 +1200,9 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
     auto issue = [&](int j) {
       if (j < CPW) ld.load(j, rq, nxt, wave);
       else if (j < 2 * CPW) ld.load(j - CPW, rg, nxt + TILE * 4, wave);
-      else dma4(rr, row_off, nrow);
+      else if constexpr (!DK) dma4(rr, row_off, nrow);
     };
-    constexpr int NLOAD = 2 * CPW + 1;
+    constexpr int NLOAD = 2 * CPW + (DK ? 0 : 1);
 
     if (vis) {
       // dO operands of all 16 steps, then dS/scale = P*dP - P*D
@@ -1169,11 +1213,14 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) gv[r][nb] = row[nb];
       }
+      if constexpr (!DK) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pd[r] = fmaf(-p[r], Dv[8 * (r >> 2) + (r & 3)], pd[r]);
+        for (int r = 0; r < 16; ++r) pd[r] = fmaf(-p[r], Dv[8 * (r >> 2) + (r & 3)], pd[r]);
+      }
       // dS/scale replaces P*dP in the scratch for k_dqs (all waves read this
-      // item's tiles before the barrier above; one writer per tile)
-      if (!DSPLIT || (wave & 1) == 0) {
+      // item's tiles before the barrier above; one writer per tile).  With a
+      // given row term (DK) the tile already holds dS/scale.
+      if (!DK && (!DSPLIT || (wave & 1) == 0)) {
         float* t = a.scratch + (size_t)cslot * ATTN_TILE_FLOATS + 1024 + lane;
 #pragma unroll
         for (int r = 0; r < 16; ++r) t[64 * r] = pd[r];
@@ -1634,23 +1681,25 @@ static attn_status_t hip_check(hipError_t e, const char* what) {
 
 // With stored tiles (a.scratch set): k_dq storing P and P*dP and emitting D,
 // k_dkdv_p (dK, dV, and dS over P*dP), then k_dqs (dQ).  Without: k_dq
-// accumulating dQ and emitting D, then k_dkdv recomputing the scores.
-template <int DP>
+// accumulating dQ and emitting D, then k_dkdv recomputing the scores.  DK:
+// D was computed beforehand (from the forward output); k_dq then stores
+// dS/scale in place of P*dP, or accumulates dQ from dS alone.
+template <int DP, bool DK>
 static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   const int BRq = Pair<DP>::ROLE ? 64 : 128;
   const int nqt = (a.S + BRq - 1) / BRq;
   attn_status_t rc = profile_mark(st, true);
   if (rc != ATTN_OK) return rc;
   if (a.scratch)
-    hipLaunchKernelGGL((k_dq<DP, false>), dim3(nqt * a.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_dq<DP, false, DK>), dim3(nqt * a.H), dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((k_dq<DP, true>), dim3(nqt * a.H), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_dq<DP, true, DK>), dim3(nqt * a.H), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching k_dq");
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
   const int nkt = (a.S + 63) / 64;
   if (a.scratch)
-    hipLaunchKernelGGL(k_dkdv_p<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_dkdv_p<DP, DK>), dim3(nkt * a.KV), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching the dK/dV kernel");
@@ -1663,14 +1712,15 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   return rc;
 }
 
+template <bool DK>
 static attn_status_t launch_bwd(const BwdArgs& a, int dp, hipStream_t st) {
   switch (dp) {
-    case 32: return launch_dqkv<32>(a, st);
-    case 64: return launch_dqkv<64>(a, st);
-    case 96: return launch_dqkv<96>(a, st);
-    case 128: return launch_dqkv<128>(a, st);
-    case 192: return launch_dqkv<192>(a, st);
-    default: return launch_dqkv<256>(a, st);
+    case 32: return launch_dqkv<32, DK>(a, st);
+    case 64: return launch_dqkv<64, DK>(a, st);
+    case 96: return launch_dqkv<96, DK>(a, st);
+    case 128: return launch_dqkv<128, DK>(a, st);
+    case 192: return launch_dqkv<192, DK>(a, st);
+    default: return launch_dqkv<256, DK>(a, st);
   }
 }
 
@@ -1767,16 +1817,15 @@ static attn_status_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   return hip_check(hipGetLastError(), "launching k_fwd");
 }
 
-extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V, const float* dO,
-                                  const float* LSE, const uint32_t* seg, float* dQ, float* dK,
-                                  float* dV, int seq_len, int n_heads, int n_kv_heads,
-                                  int head_dim, float scale, void* stream) {
-  g_err[0] = 0;
-  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
-    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+// The backward, with D computed by the kernels (O == NULL) or read off the
+// forward output O.
+static attn_status_t run_bwd(const float* Q, const float* K, const float* V, const float* O,
+                             const float* dO, const float* LSE, const uint32_t* seg, float* dQ,
+                             float* dK, float* dV, int seq_len, int n_heads, int n_kv_heads,
+                             int head_dim, float scale, void* stream) {
   attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, scale);
   if (rc != ATTN_OK) return rc;
-  const void* ptrs[] = {Q, K, V, dO, LSE, seg, dQ, dK, dV};
+  const void* ptrs[] = {Q, K, V, O, dO, LSE, seg, dQ, dK, dV};
   for (const void* p : ptrs)
     if (misaligned(p)) return fail(ATTN_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
   if (seq_len == 0) return ATTN_OK;
@@ -1805,9 +1854,41 @@ extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, st, seg, seq_len, a.blk_min, a.blk_max, a.slot_off);
   rc = hip_check(hipGetLastError(), "launching k_prep");
-  if (rc == ATTN_OK) rc = launch_bwd(a, dp, st);
+  if (rc == ATTN_OK && O) {
+    const long long rows = (long long)seq_len * n_heads;
+    int tpr = 1;
+    while (tpr < head_dim / 4) tpr <<= 1;
+    const long long waves = (rows * tpr + 63) / 64;
+    const int blocks = (int)std::min<long long>((waves + 3) / 4, 4096);
+    hipLaunchKernelGGL(k_rowdot, dim3(blocks), dim3(256), 0, st, O, dO, a.Dws, rows, head_dim);
+    rc = hip_check(hipGetLastError(), "launching k_rowdot");
+  }
+  if (rc == ATTN_OK) rc = O ? launch_bwd<true>(a, dp, st) : launch_bwd<false>(a, dp, st);
   attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");
   return rc != ATTN_OK ? rc : rc2;
+}
+
+extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V, const float* dO,
+                                  const float* LSE, const uint32_t* seg, float* dQ, float* dK,
+                                  float* dV, int seq_len, int n_heads, int n_kv_heads,
+                                  int head_dim, float scale, void* stream) {
+  g_err[0] = 0;
+  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  return run_bwd(Q, K, V, nullptr, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads,
+                 head_dim, scale, stream);
+}
+
+extern "C" attn_status_t attn_bwd_o(const float* Q, const float* K, const float* V,
+                                    const float* O, const float* dO, const float* LSE,
+                                    const uint32_t* seg, float* dQ, float* dK, float* dV,
+                                    int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                                    float scale, void* stream) {
+  g_err[0] = 0;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  return run_bwd(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
+                 scale, stream);
 }
 
 extern "C" attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V,

@@ -100,8 +100,26 @@ attn_status_t attn_bwd(const float* Q, const float* K, const float* V, const flo
                        void* stream);
 
 /*
+ * attn_bwd_o -- attn_bwd for callers that kept the forward output O [S, H, d]
+ * (fp32, same layout as Q; attn_fwd_lse produces it).  The row term is read
+ * off it, D[s,h] = dO[s,h,:] . O[s,h,:], which equals sum_j P*dP when O and
+ * LSE come from the same forward: summing P_j (dO . v_j) over the visible
+ * keys gives dO . (sum_j P_j v_j), and that sum is the forward's output (page
+ * "tang 0.2.0 -- src/gpu/llm.rs", causal_attention_fused: the
+ * probability-weighted sum of V).  With D known up front the first pass
+ * forms dS directly; otherwise as attn_bwd (arguments, layouts, +=
+ * semantics, errors, workspace).  O is read only; NULL O is
+ * ATTN_ERR_INVALID_ARG.
+ */
+attn_status_t attn_bwd_o(const float* Q, const float* K, const float* V, const float* O,
+                         const float* dO, const float* LSE, const uint32_t* seg,
+                         float* dQ, float* dK, float* dV,
+                         int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                         void* stream);
+
+/*
  * attn_bwd_plan -- host-side query (no GPU work): the workspace bytes one
- * attn_bwd call of this size takes, and whether its key-major pass reads
+ * attn_bwd (or attn_bwd_o) call of this size takes, and whether its key-major pass reads
  * stored probability tiles (1) or recomputes them (0).  Either output pointer
  * may be NULL.  Same argument checks as attn_bwd.
  */

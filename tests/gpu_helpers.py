@@ -20,16 +20,21 @@ def seg_dev(seg):
     return None if seg is None else to_dev(np.asarray(seg, np.uint32).astype(np.int32))
 
 
-def gpu_bwd(p, lse, init=None, seg=None, use_seg=True):
-    """Run attn_bwd on the GPU.  Returns numpy (dQ, dK, dV)."""
+def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None):
+    """Run attn_bwd (attn_bwd_o when the forward output O is given) on the GPU.
+    Returns numpy (dQ, dK, dV)."""
     t = {k: to_dev(p[k]) for k in ("Q", "K", "V", "dO")}
     if init is None:
         out = [torch.zeros_like(t["Q"]), torch.zeros_like(t["K"]), torch.zeros_like(t["V"])]
     else:
         out = [to_dev(x.copy()) for x in init]
     s = seg_dev(p["seg"] if seg is None else seg) if use_seg else None
-    binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], to_dev(lse.astype(np.float32)), s, *out,
-                     float(p["scale"]))
+    L = to_dev(lse.astype(np.float32))
+    if O is None:
+        binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], L, s, *out, float(p["scale"]))
+    else:
+        binding.attn_bwd_o(t["Q"], t["K"], t["V"], to_dev(O.astype(np.float32)), t["dO"], L, s,
+                           *out, float(p["scale"]))
     torch.cuda.synchronize()
     return [o.cpu().numpy() for o in out]
 
