@@ -6,21 +6,28 @@
 // comment and kernel attention_backward (Pass A: P, dP, D and dV; Pass B: dS,
 // dQ and dK; Final: owned += of dQ).  The page's design (one workgroup per
 // (query, head), CAS-atomic dK/dV scatter) was made for WebGPU on Apple GPUs;
-// here the same sums are re-tiled for 64-wide wavefronts and MFMA:
+// here the same sums are re-tiled for 64-wide wavefronts and MFMA.
 //
-//   k_dq   query-block-major.  One workgroup per (query tile, head).  Sweeps
-//          the visible key tiles once and accumulates, per query row,
-//             A = sum_j P*dP*k_j     B = sum_j P*k_j     D = sum_j P*dP
-//          so dQ = scale*(A - D*B) (= sum_j dS*k_j), and D is emitted for k_dkdv.
-//          4 MFMA contractions per visible pair: K.Q^T, V.dO^T, (P.dP).K, P.K.
-//   k_dkdv key-block-major.  One workgroup per (key tile, KV head).  Owns its
-//          dK/dV rows, sums the GQA group inside the workgroup (the key-major,
-//          atomic-free idea of the page's attention_backward_short_dKdV
-//          kernel), sweeps the query tiles that can see its keys.
-//          4 MFMA contractions per visible pair: Q.K^T, dO.V^T, P^T.dO, dS^T.Q.
-//   k_fwd  forward producing LSE (and optionally O) for the backward's input
-//          (page "tang 0.2.0 -- src/gpu/llm.rs", causal_attention_fused: row
-//          max, exp-sum, weighted V; plus the document mask and the LSE output).
+// Default path (the probability tiles fit the scratch budget), per call:
+//   k_prep    per 32-row query block: seg min/max and scratch slot offsets.
+//   k_dq      query-major, one workgroup per (query tile, head): S and dP
+//             (2 MFMA contractions per visible pair), P, P*dP and
+//             D = sum_j P*dP; stores the P and P*dP tiles.
+//   k_dkdv_p  key-major, one workgroup per (key tile, KV head): owns its
+//             dK/dV rows and sums the GQA group inside the workgroup (the
+//             key-major, atomic-free idea of the page's
+//             attention_backward_short_dKdV kernel); reads the tiles, forms
+//             dS, runs P^T.dO and dS^T.Q (2 contractions), leaves dS.
+//   k_dqs     query-major: dQ += dS.K from the dS tiles (1 contraction).
+// Recompute path (over budget): k_dq accumulates A = sum_j P*dP*k_j and
+//   B = sum_j P*k_j, so dQ = scale*(A - D*B) (4 contractions), then k_dkdv
+//   recomputes S and dP per pair (4 contractions).
+// attn_bwd_o: k_rowdot first computes D = dO.O from the forward output; the
+//   same kernels then run in their D-known mode (dS formed by k_dq).
+// k_fwd       the forward producing LSE (and optionally O) for the backward's
+//             input, in one sweep with a running max (page "tang 0.2.0 --
+//             src/gpu/llm.rs", causal_attention_fused; plus the document mask
+//             and the LSE output).
 //
 // MFMA v_mfma_f32_32x32x2_f32 (C[32x32] += A[32x2] * B[2x32]) lane layout,
 // checked on the device: lane l supplies A[l%32][l/32] and B[l/32][l%32]; it
@@ -70,20 +77,6 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Geometry shared by the kernels for a padded head dimension DP (a multiple of
-// 32; head_dim is zero-padded up to it).  Above 128 columns the contraction
-// over d is split between a pair of waves (DSPL = 2) that exchange partial
-// score tiles through LDS, so that each wave keeps DP/2 columns in registers.
-template <int DP>
-struct Geo {
-  static constexpr int DSPL = DP > 128 ? 2 : 1;
-  static constexpr int DW = DP / DSPL;  // columns owned by one wave
-  static constexpr int TH = DW / 2;     // contraction steps per half-wave
-  static constexpr int NB = DW / 32;    // 32-column output blocks per wave
-  static constexpr int LDR = DP + 4;    // LDS row stride in floats (b128 reads conflict-free)
-  static_assert(DW % 32 == 0, "a wave owns whole 32-column blocks");
-};
-
 struct BwdArgs {
   const float *Q, *K, *V, *dO, *LSE;
   const uint32_t* seg;  // NULL = all zeros
@@ -124,60 +117,6 @@ template <int N>
 __device__ __forceinline__ void pin_agpr(float* v) {
 #pragma unroll
   for (int i = 0; i < N; ++i) asm volatile("" : "+a"(v[i]));
-}
-
-// Cooperative load of ROWS x DP floats of two row-major matrices that share
-// addressing (K and V, or Q and dO) into registers, one float4 per step.
-template <int ROWS, int DP>
-struct TilePair {
-  static constexpr int F4 = ROWS * DP / 4 / 256;
-  static_assert(F4 * 256 * 4 == ROWS * DP, "tile must split evenly over 256 threads");
-  float4 a[F4], b[F4];
-
-  __device__ __forceinline__ void fetch(const float* A, const float* B, int r0, int S,
-                                        size_t row_stride, size_t col0, int d, int tid) {
-#pragma unroll
-    for (int i = 0; i < F4; ++i) {
-      const int f = tid + 256 * i;
-      const int row = f / (DP / 4), col = (f % (DP / 4)) * 4;
-      a[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-      b[i] = a[i];
-      if (r0 + row < S && col < d) {
-        const size_t off = (size_t)(r0 + row) * row_stride + col0 + col;
-        a[i] = *reinterpret_cast<const float4*>(A + off);
-        b[i] = *reinterpret_cast<const float4*>(B + off);
-      }
-    }
-  }
-  __device__ __forceinline__ void stash(float* sA, float* sB, int tid) const {
-    constexpr int LDR = DP + 4;
-#pragma unroll
-    for (int i = 0; i < F4; ++i) {
-      const int f = tid + 256 * i;
-      const int row = f / (DP / 4), col = (f % (DP / 4)) * 4;
-      *reinterpret_cast<float4*>(sA + row * LDR + col) = a[i];
-      *reinterpret_cast<float4*>(sB + row * LDR + col) = b[i];
-    }
-  }
-};
-
-// Exchange of partial score tiles between the two waves of a d-split pair:
-// each adds its partner's partial sums (a + b in one wave, b + a in the other,
-// so both hold bitwise identical tiles).
-__device__ __forceinline__ void pair_exchange(float* sX, int wave, int lane, f32x16& x, f32x16& y) {
-  float* mine = sX + (wave * 32) * 64 + lane;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    mine[r * 64] = x[r];
-    mine[(16 + r) * 64] = y[r];
-  }
-  __syncthreads();
-  const float* other = sX + ((wave ^ 1) * 32) * 64 + lane;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    x[r] += other[r * 64];
-    y[r] += other[(16 + r) * 64];
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1454,35 +1393,50 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_fwd: LSE (pass 1, running max and sum per query) and O (pass 2, with the
-// final LSE, no rescaling).  Same tiling as k_dq.
+// k_fwd: the forward that produces the backward's inputs, LSE and (WANT_O) O,
+// in one sweep with a running max (page "tang 0.2.0 -- src/gpu/llm.rs",
+// causal_attention_fused: row max, exp-sum, probability-weighted V; here
+// with the document mask, the log-sum-exp output, and the max carried across
+// key tiles, O being rescaled when it moves).  One workgroup per (query tile
+// of 128 rows, head); wave w owns query block w (32 queries) and all DP
+// columns.  K/V tiles of 32 keys are streamed through LDS as in k_dq.
+//   S^T = K Q^T  (lane <-> query, register r <-> key crow(r, hf)),
+//   m' = max(m, max over the tile), alpha = 2^(m - m'), p = 2^(x - m'),
+//   l = alpha*l + sum p,  O = alpha*O + P V   (log2 domain, x = scale*s*log2e).
+// O's rows sit in register r (query crow(r, hf)), so each row's alpha and
+// final 1/l come from the lane holding that query (a shuffle).  O's columns
+// are permuted (lane l, block nb <-> column NB*(l%32) + nb) so a step's V
+// operands are one wide LDS read.
 // ---------------------------------------------------------------------------
-template <int DP>
+template <int DP, bool WANT_O>
 __global__ __launch_bounds__(256) void k_fwd(FwdArgs a) {
-  using G = Geo<DP>;
-  constexpr int QB = 4 / G::DSPL, BR = 32 * QB, BC = 32;
-  __shared__ __attribute__((aligned(16))) float sK[BC * G::LDR];
-  __shared__ __attribute__((aligned(16))) float sV[BC * G::LDR];
-  __shared__ __attribute__((aligned(16))) float sX[G::DSPL > 1 ? 4 * 32 * 64 : 4];
+  constexpr int QB = 4, BR = 32 * QB, BC = 32;
+  constexpr int LDR = DP + 4, TH = DP / 2, NB = DP / 32;
+  constexpr int TILE = PadTile<BC, DP>::FLOATS;
+  constexpr int CPW = PadTile<BC, DP>::CPW;
+  __shared__ __attribute__((aligned(1024))) float sKV[2][2 * TILE];
   __shared__ uint32_t sMin[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
-  const int ds = wave % G::DSPL, qb = wave / G::DSPL;
   const int S = a.S, H = a.H, d = a.d;
   const int g = H / a.KV;
-  const int nqt = (S + BR - 1) / BR;
-  const int qt = nqt - 1 - (int)(blockIdx.x / H);
-  const int h = blockIdx.x % H, kvh = h / g;
+  const int qt_hi = (S - 1) / BR;
+  const int qt = qt_hi - (int)(blockIdx.x / H);  // longest rows first
+  const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
   const int i0 = qt * BR;
-  const int q = i0 + qb * 32 + l32;
+  const int q = i0 + wave * 32 + l32;
   const bool q_ok = q < S;
-  const int cb = ds * G::DW + hf * G::TH;
   const size_t qstride = (size_t)H * d, kstride = (size_t)a.KV * d;
   const float sc2 = a.scale * ATTN_LOG2E;
+  const float* Kh = a.K + (size_t)kvh * d;
+  const float* Vh = a.V + (size_t)kvh * d;
 
-  float qr[G::TH];
-  load_row<G::TH>(a.Q + (size_t)q * qstride + (size_t)h * d, cb, d, q_ok, qr);
+  // B operand of the score block: this lane's query row, half-wave hf's columns
+  float qr[TH];
+  load_row<TH>(a.Q + (size_t)q * qstride + (size_t)h * d, hf * TH, d, q_ok, qr);
+  pin_agpr<TH>(qr);
   const uint32_t sq = (q_ok && a.seg) ? a.seg[q] : 0u;
   uint32_t mn = q_ok ? sq : 0xffffffffu;
 #pragma unroll
@@ -1495,83 +1449,104 @@ __global__ __launch_bounds__(256) void k_fwd(FwdArgs a) {
   const int last_q = min(i0 + BR, S) - 1;
   const int kt_lo = (int)(min(tmin, (uint32_t)last_q) / BC), kt_hi = last_q / BC;
 
-  float m = -INFINITY, l = 0.f;  // running max / sum (log2 domain) over this half's keys
-  float lse2 = -INFINITY;
-  f32x16 accO[G::NB];
+  float m = -INFINITY, l = 0.f;  // this lane's query: running max, this half's running sum
+  f32x16 accO[WANT_O ? NB : 1];
+  if constexpr (WANT_O) {
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) accO[nb] = zero16();
-
-  for (int pass = 0; pass < (a.O ? 2 : 1); ++pass) {
-    for (int kt = kt_lo; kt <= kt_hi; ++kt) {
-      const int j0 = kt * BC;
-      TilePair<BC, DP> t;
-      t.fetch(a.K, a.V, j0, S, kstride, (size_t)kvh * d, d, tid);
-      t.stash(sK, sV, tid);
-      __syncthreads();
-      f32x16 st = zero16(), unused = zero16();
-      const float* kp = sK + l32 * G::LDR + cb;
-#pragma unroll
-      for (int t4 = 0; t4 < G::TH; t4 += 4) {
-        const float4 k4 = *reinterpret_cast<const float4*>(kp + t4);
-        st = mfma32(k4.x, qr[t4], st);
-        st = mfma32(k4.y, qr[t4 + 1], st);
-        st = mfma32(k4.z, qr[t4 + 2], st);
-        st = mfma32(k4.w, qr[t4 + 3], st);
-      }
-      if constexpr (G::DSPL > 1) pair_exchange(sX, wave, lane, st, unused);
-      if (pass == 0) {
-        float x[16], mloc = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + crow(r, hf);
-          const bool vis = q_ok && key <= q && (uint32_t)key >= sq;
-          x[r] = vis ? st[r] * sc2 : -INFINITY;
-          mloc = fmaxf(mloc, x[r]);
-        }
-        const float mnew = fmaxf(m, mloc);
-        if (mnew != -INFINITY) {
-          float acc = (m == -INFINITY) ? 0.f : l * exp2f(m - mnew);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc += (x[r] == -INFINITY) ? 0.f : exp2f(x[r] - mnew);
-          l = acc;
-          m = mnew;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j0 + crow(r, hf);
-          const bool vis = q_ok && key <= q && (uint32_t)key >= sq;
-          const float e = exp2f(fmaf(st[r], sc2, -lse2));
-          st[r] = vis ? e : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float* vrow = sV + crow(r, hf) * G::LDR + ds * G::DW + l32;
-#pragma unroll
-          for (int nb = 0; nb < G::NB; ++nb) accO[nb] = mfma32(st[r], vrow[nb * 32], accO[nb]);
-        }
-      }
-      __syncthreads();
-    }
-    if (pass == 0) {
-      const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
-      const float M = fmaxf(m, m2);
-      if (M != -INFINITY) {
-        const float L = ((m == -INFINITY) ? 0.f : l * exp2f(m - M)) +
-                        ((m2 == -INFINITY) ? 0.f : l2 * exp2f(m2 - M));
-        lse2 = M + log2f(L);
-      }
-      if (q_ok && hf == 0 && ds == 0) a.LSE[(size_t)q * H + h] = lse2 * ATTN_LN2;
-    }
+    for (int nb = 0; nb < NB; ++nb) accO[nb] = zero16();
   }
-  if (!a.O) return;
-#pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) {
-    const int col = ds * G::DW + nb * 32 + l32;
+
+  TileLoader<BC, DP> ld;
+  ld.init(kstride, d, wave, lane);
+  const uint32_t lds_kv = lds_addr(&sKV[0][0]);
+  {
+    ld.load_all(ld.rsrc(Kh, kt_lo * BC, S, kstride, d, true), lds_kv, wave);
+    if constexpr (WANT_O) ld.load_all(ld.rsrc(Vh, kt_lo * BC, S, kstride, d, true), lds_kv + TILE * 4, wave);
+  }
+  constexpr int NLOAD = (WANT_O ? 2 : 1) * CPW;
+  const int ob = (4 * hf) * LDR + NB * l32;  // this lane's V operands (row 4*hf + step row)
+  int buf = 0;
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    tile_barrier();  // tile kt resident; everyone done with tile kt-1
+    const float* sK = &sKV[buf][0];
+    const float* sV = &sKV[buf][TILE];
+    const uint32_t nxt = lds_kv + (buf ^ 1) * (2 * TILE * 4);
+    const int j0 = kt * BC;
+    const bool more = kt < kt_hi;
+    const i32x4 rk = ld.rsrc(Kh, (kt + 1) * BC, S, kstride, d, more);
+    const i32x4 rv = ld.rsrc(Vh, (kt + 1) * BC, S, kstride, d, more && WANT_O);
+    auto issue = [&](int j) {
+      if (j < CPW) ld.load(j, rk, nxt, wave);
+      else ld.load(j - CPW, rv, nxt + TILE * 4, wave);
+    };
+    const SpreadLoads<NLOAD, TH / 4, decltype(issue)> spread{issue};
+    const f32x16 st = score_block<DP>(sK, l32, hf, qr, spread);
+
+    // running max over this tile's visible keys (both half-waves hold the query)
+    float x[16], mloc = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = i0 + qb * 32 + crow(r, hf);
-      if (row < S && col < d) a.O[(size_t)row * qstride + (size_t)h * d + col] = accO[nb][r];
+      const int key = j0 + crow(r, hf);
+      const bool vis = q_ok && key <= q && (uint32_t)key >= sq;
+      x[r] = vis ? st[r] * sc2 : -INFINITY;
+      mloc = fmaxf(mloc, x[r]);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float mnew = fmaxf(m, mloc);
+    // alpha rescales what was summed under the old max (nothing yet: 0)
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+    float p[16], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = (x[r] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[r] - mnew);
+      psum += p[r];
+    }
+    if (mnew != -INFINITY) {
+      l = l * alpha + psum;
+      m = mnew;
+    }
+    if constexpr (WANT_O) {
+      // rescale O's rows when some query's max moved (alpha != 1)
+      const bool moved = mnew != -INFINITY && alpha != 1.f;
+      if (__ballot(moved)) {
+        const float am = moved ? alpha : 1.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float ar = __shfl(am, crow(r, hf));
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) accO[nb][r] *= ar;
+        }
+      }
+      // O += P V over the 32 keys
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float* vrow = sV + ob + (8 * (r >> 2) + (r & 3)) * LDR;
+        float vv[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vv[nb] = vrow[nb];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) accO[nb] = mfma32(p[r], vv[nb], accO[nb]);
+      }
+    }
+    buf ^= 1;
+  }
+  tile_barrier();  // the last (empty) loads have landed before the LDS is released
+
+  // LSE = ln(sum) = (m + log2 L) * ln 2, L summed over both half-waves
+  const float L = l + __shfl_xor(l, 32);
+  const float lse2 = (m == -INFINITY || !(L > 0.f)) ? -INFINITY : m + log2f(L);
+  if (q_ok && hf == 0) a.LSE[(size_t)q * H + h] = lse2 * ATTN_LN2;
+  if constexpr (WANT_O) {
+    const float inv = (lse2 == -INFINITY) ? 0.f : 1.f / L;
+    float* __restrict__ Oh = a.O + (size_t)h * d;
+    const int col0 = NB * l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float ir = __shfl(inv, crow(r, hf));
+      const int row = i0 + wave * 32 + crow(r, hf);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        if (row < S && col0 + nb < d) Oh[(size_t)row * qstride + col0 + nb] = accO[nb][r] * ir;
     }
   }
 }
@@ -1811,9 +1786,11 @@ extern "C" attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads,
 
 template <int DP>
 static attn_status_t launch_fwd(const FwdArgs& a, hipStream_t st) {
-  const int BRq = 32 * (4 / Geo<DP>::DSPL);
-  const int nqt = (a.S + BRq - 1) / BRq;
-  hipLaunchKernelGGL(k_fwd<DP>, dim3(nqt * a.H), dim3(256), 0, st, a);
+  const int nqt = (a.S + 127) / 128;
+  if (a.O)
+    hipLaunchKernelGGL((k_fwd<DP, true>), dim3(nqt * a.H), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_fwd<DP, false>), dim3(nqt * a.H), dim3(256), 0, st, a);
   return hip_check(hipGetLastError(), "launching k_fwd");
 }
 
