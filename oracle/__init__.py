@@ -59,9 +59,13 @@ def _load():
     lib.oracle_attn_bwd_rows_o.argtypes = [P, P, P, P, P, P, P, P, I, P, I, P, P, P, I, I, I, I,
                                            ctypes.c_float, I]
     lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I, ctypes.c_float, I]
+    lib.oracle_rope_f64.argtypes = [P, I, I, I, ctypes.c_double, ctypes.c_long, I]
+    lib.oracle_attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_float,
+                                         ctypes.c_double, ctypes.c_long, I]
     for f in (lib.oracle_attn_fwd_f64, lib.oracle_attn_bwd_f64, lib.oracle_attn_bwd_o_f64,
               lib.oracle_attn_fwd, lib.oracle_attn_bwd, lib.oracle_attn_bwd_o,
-              lib.oracle_attn_bwd_rows, lib.oracle_attn_bwd_rows_o, lib.oracle_attn_fwd_rows):
+              lib.oracle_attn_bwd_rows, lib.oracle_attn_bwd_rows_o, lib.oracle_attn_fwd_rows,
+              lib.oracle_rope_f64, lib.oracle_attn_bwd_rope):
         f.restype = I
     _lib = lib
     return lib
@@ -167,11 +171,24 @@ def attn_fwd(Q, K, V, seg, scale, nthreads=0, want_o=True):
     return O, LSE
 
 
-def attn_bwd(Q, K, V, dO, LSE, seg, scale, dQ=None, dK=None, dV=None, nthreads=0, O=None):
+def rope_f64(X, base, pos_offset, backward):
+    """The page's RoPE rotation of interleaved column pairs of X [S, NH, d]
+    (forward, or its transpose when ``backward``); returns a new float64 array."""
+    X = np.array(X, dtype=np.float64, order="C")
+    S, NH, d = X.shape
+    _check(_load().oracle_rope_f64(_ptr(X), S, NH, d, float(base), int(pos_offset),
+                                   1 if backward else 0), "rope_f64")
+    return X
+
+
+def attn_bwd(Q, K, V, dO, LSE, seg, scale, dQ=None, dK=None, dV=None, nthreads=0, O=None,
+             rope=None):
     """fp32 backward with "+=" semantics on dQ, dK, dV (zeros when not given).
 
-    With ``O`` (the forward output) the row term is D = dO . O.  Returns the
-    (updated) float32 arrays (dQ, dK, dV).
+    With ``O`` (the forward output) the row term is D = dO . O.  With ``rope``
+    = (base, pos_offset) the page's RoPE backward then rotates dQ and dK in
+    place (Q, K are the rotated inputs).  Returns the (updated) float32
+    arrays (dQ, dK, dV).
     """
     Q, K, V, dO, LSE = (np.ascontiguousarray(x, dtype=np.float32) for x in (Q, K, V, dO, LSE))
     O = None if O is None else np.ascontiguousarray(O, dtype=np.float32)
@@ -182,6 +199,12 @@ def attn_bwd(Q, K, V, dO, LSE, seg, scale, dQ=None, dK=None, dV=None, nthreads=0
     dV = np.zeros((S, KV, d), np.float32) if dV is None else np.array(dV, np.float32, order="C")
     if O is not None:
         assert O.shape == Q.shape
+    if rope is not None:
+        _check(_load().oracle_attn_bwd_rope(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO),
+                                            _ptr(LSE), _ptr(seg), _ptr(dQ), _ptr(dK), _ptr(dV),
+                                            S, H, KV, d, np.float32(scale), float(rope[0]),
+                                            int(rope[1]), nthreads), "attn_bwd_rope")
+        return dQ, dK, dV
     _check(_load().oracle_attn_bwd_o(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
                                      _ptr(seg), _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
                                      np.float32(scale), nthreads), "attn_bwd")

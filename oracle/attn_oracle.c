@@ -423,6 +423,72 @@ int oracle_attn_bwd(const float *Q, const float *K, const float *V, const float 
   return oracle_attn_bwd_o(Q, K, V, NULL, dO, LSE, seg, dQ, dK, dV, S, H, KV, d, scale, nthreads);
 }
 
+/* ------------------------------------------------------------------ */
+/* rotary position embedding (RoPE) of interleaved column pairs         */
+/* ------------------------------------------------------------------ */
+/* Page "llm.istanbul -- 10_backward_attention.wgsl", kernels rope_q_backward
+ * and rope_k_backward: for position s, head h and column pair (2p, 2p+1) of
+ * X [S, NH, d], angle = (s + pos_offset) * base^(-2p/d).  The forward
+ * rotation maps (x0, x1) to (x0 c - x1 s, x0 s + x1 c); the backward applies
+ * its transpose, (g0, g1) -> (g0 c + g1 s, -g0 s + g1 c).  In place, fp64. */
+int oracle_rope_f64(double *X, int S, int NH, int d, double base, long pos_offset, int backward) {
+  if (S < 0 || NH < 1 || d < 2 || (d & 1) || !(base > 0.0)) return 1;
+  for (long t = 0; t < S; ++t)
+    for (int h = 0; h < NH; ++h)
+      for (int pr = 0; pr < d / 2; ++pr) {
+        double freq = pow(base, -2.0 * pr / (double)d);
+        double ang = (double)(t + pos_offset) * freq;
+        double c = cos(ang), sn = sin(ang);
+        double *x = X + ((size_t)t * NH + h) * d + 2 * pr;
+        double x0 = x[0], x1 = x[1];
+        if (backward) {
+          x[0] = x0 * c + x1 * sn;
+          x[1] = -x0 * sn + x1 * c;
+        } else {
+          x[0] = x0 * c - x1 * sn;
+          x[1] = x0 * sn + x1 * c;
+        }
+      }
+  return 0;
+}
+
+/* The backward followed by the page's RoPE backward on dQ (n_heads) and dK
+ * (n_kv_heads), in place: dQ = fp32(R^T(fp64(dQ) + gradient)), the same for
+ * dK, and dV = fp32(fp64(dV) + gradient).  O may be NULL (see
+ * oracle_attn_bwd_o).  Q and K are the rotated inputs the forward used. */
+int oracle_attn_bwd_rope(const float *Q, const float *K, const float *V, const float *O,
+                         const float *dO, const float *LSE, const uint32_t *seg, float *dQ,
+                         float *dK, float *dV, int S, int H, int KV, int d, float scale,
+                         double rope_base, long pos_offset, int nthreads) {
+  if (check_dims(S, H, KV, d) || (d & 1) || !(rope_base > 0.0)) return 1;
+  if (S == 0) return 0;
+  size_t nq = (size_t)S * H * d, nk = (size_t)S * KV * d, nr = (size_t)S * H;
+  double *q = widen(Q, nq), *k = widen(K, nk), *v = widen(V, nk), *g = widen(dO, nq);
+  double *l = widen(LSE, nr);
+  double *o = O ? widen(O, nq) : NULL;
+  double *gq = (double *)malloc(sizeof(double) * nq);
+  double *gk = (double *)malloc(sizeof(double) * nk);
+  double *gv = (double *)malloc(sizeof(double) * nk);
+  int rc = 2;
+  if (q && k && v && g && l && gq && gk && gv && (o || !O)) {
+    rc = oracle_attn_bwd_o_f64(q, k, v, o, g, l, seg, gq, gk, gv, NULL, NULL, S, H, KV, d,
+                               (double)scale, nthreads);
+    if (rc == 0) {
+      for (size_t i = 0; i < nq; ++i) gq[i] += (double)dQ[i];
+      for (size_t i = 0; i < nk; ++i) gk[i] += (double)dK[i];
+      oracle_rope_f64(gq, S, H, d, rope_base, pos_offset, 1);
+      oracle_rope_f64(gk, S, KV, d, rope_base, pos_offset, 1);
+      for (size_t i = 0; i < nq; ++i) dQ[i] = (float)gq[i];
+      for (size_t i = 0; i < nk; ++i) {
+        dK[i] = (float)gk[i];
+        dV[i] = (float)((double)dV[i] + gv[i]);
+      }
+    }
+  }
+  free(q); free(k); free(v); free(g); free(l); free(o); free(gq); free(gk); free(gv);
+  return rc;
+}
+
 /* Selected rows only, for checks at sizes where the full backward is slow:
  * dQ for query rows q_rows[0..nq) -> dQ_sel [nq, H, d]; dK and dV for key rows
  * k_rows[0..nk) -> dK_sel, dV_sel [nk, KV, d].  Outputs are the fp64
