@@ -113,6 +113,8 @@ def main():
                     help="also run one device copy of this many MiB (counter calibration)")
     ap.add_argument("--o-entry", action="store_true",
                     help="time attn_bwd_o (row term read off the forward output O) instead")
+    ap.add_argument("--rope", action="store_true",
+                    help="time attn_bwd_rope (RoPE backward fused into the write-back, base 1e4)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
@@ -145,7 +147,10 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        if args.o_entry:
+        if args.rope:
+            binding.attn_bwd_rope(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale,
+                                  10000.0, 0)
+        elif args.o_entry:
             binding.attn_bwd_o(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
         else:
             binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], lse, seg, dQ, dK, dV, scale)
@@ -230,7 +235,8 @@ def main():
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
                    "head_dim": w.d, "mask": "causal" if seg is None else "documents",
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
-                   "entry": "attn_bwd_o" if args.o_entry else "attn_bwd",
+                   "entry": ("attn_bwd_rope" if args.rope else
+                             "attn_bwd_o" if args.o_entry else "attn_bwd"),
                    "stored_tiles": stored,
                    "workspace_bytes": ws_bytes,
                    "kernel_ms": kernel_ms},

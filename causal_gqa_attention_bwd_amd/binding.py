@@ -13,8 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_bwd_o", "attn_bwd_plan", "attn_fwd_lse", "attn_last_error",
-            "attn_profile_begin", "attn_profile_end")
+EXPORTED = ("attn_bwd", "attn_bwd_o", "attn_bwd_plan", "attn_bwd_rope", "attn_fwd_lse",
+            "attn_last_error", "attn_profile_begin", "attn_profile_end")
 
 _lib = None
 
@@ -39,6 +39,8 @@ def load():
     lib.attn_bwd.restype = I
     lib.attn_bwd_o.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_o.restype = I
+    lib.attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, F, I, P]
+    lib.attn_bwd_rope.restype = I
     lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                   ctypes.POINTER(ctypes.c_int)]
     lib.attn_bwd_plan.restype = I
@@ -136,6 +138,17 @@ def attn_bwd_o(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
                            _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                            _stream(stream))
     _raise_on(st, "attn_bwd_o")
+
+
+def attn_bwd_rope(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, rope_base, pos_offset,
+                  stream=None):
+    """attn_bwd (O None) or attn_bwd_o (O given), then the RoPE backward on dQ and
+    dK fused into the write-back (the C ABI's attn_bwd_rope): dQ <- R^T(dQ + g)."""
+    S, H, KV, d = _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV)
+    st = load().attn_bwd_rope(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(seg),
+                              _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
+                              float(rope_base), int(pos_offset), _stream(stream))
+    _raise_on(st, "attn_bwd_rope")
 
 
 def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):

@@ -88,6 +88,9 @@ struct BwdArgs {
   float* scratch;        // P and P*dP tiles of every visible pair, or NULL
   int S, H, KV, d;
   float scale;
+  int rope;              // 1: rotate dQ, dK back by RoPE after the += (rope_bwd)
+  int rope_pos;          // position of row 0 (the page's pos_offset)
+  double rope_base;      // frequency base
 };
 
 struct FwdArgs {
@@ -362,6 +365,45 @@ struct SpreadLoads {
 __device__ __forceinline__ int xcd_head(int r, int H) {
   if (H % 8 != 0) return r;
   return (r % 8) * (H / 8) + r / 8;
+}
+
+// ---------------------------------------------------------------------------
+// RoPE backward in the epilogues (page "llm.istanbul --
+// 10_backward_attention.wgsl", kernels rope_q_backward / rope_k_backward):
+// the pair of columns (2p, 2p+1) of a row at position pos turns back by
+// angle = pos * base^(-2p/d): (g0, g1) -> (g0 c + g1 s, -g0 s + g1 c).  The
+// angle and its sine and cosine are taken in fp64 (positions reach 2^31; an
+// fp32 angle would be off by ~1e-3 rad at a few thousand).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double rope_freq(int col, int d, double base) {
+  return pow(base, -2.0 * (double)(col >> 1) / (double)d);
+}
+// This column's value after the backward rotation, from its own value and its
+// pair partner's.
+__device__ __forceinline__ float rope_back(float mine, float partner, int col, long long pos,
+                                           double freq) {
+  double sn, cs;
+  sincos((double)pos * freq, &sn, &cs);
+  return (col & 1) ? (float)(-(double)partner * sn + (double)mine * cs)
+                   : (float)((double)mine * cs + (double)partner * sn);
+}
+// Pair partners of a lane's NB values in the permuted column layout
+// (value nb of lane l sits in column c0 + NB*(l%32) + nb, c0 even): the other
+// column of a pair is in the same lane or, for odd NB, in lane l +- 1.
+template <int NB>
+__device__ __forceinline__ void rope_partners_perm(const float (&v)[NB], int l32, float (&pv)[NB]) {
+  if constexpr (NB % 2 == 0) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pv[nb] = v[nb ^ 1];
+  } else if constexpr (NB == 1) {
+    pv[0] = __shfl_xor(v[0], 1);
+  } else {
+    static_assert(NB == 3, "odd column counts per lane are 1 or 3");
+    const float up = __shfl_down(v[0], 1);  // lane + 1, first column
+    const float dn = __shfl_up(v[2], 1);    // lane - 1, last column
+    if ((l32 & 1) == 0) { pv[0] = v[1]; pv[1] = v[0]; pv[2] = up; }
+    else { pv[0] = dn; pv[1] = v[2]; pv[2] = v[1]; }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -678,17 +720,19 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 #pragma unroll
     for (int nb = 0; nb < PG::NB; ++nb) {
       const int col = dcol0 + nb * 32 + l32;
+      const double fq = a.rope ? rope_freq(col, d, a.rope_base) : 0.0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int m = crow(r, hf);
         const int row = i0 + qb * 32 + m;
-        if (row < S && col < d) {
-          if constexpr (DK)
-            dQh[(size_t)row * qstride + col] = old[nb][r] + a.scale * accA[nb][r];
-          else
-            dQh[(size_t)row * qstride + col] =
-                old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
-        }
+        float v;
+        if constexpr (DK)
+          v = old[nb][r] + a.scale * accA[nb][r];
+        else
+          v = old[nb][r] + a.scale * (accA[nb][r] - sD[wave * 32 + m] * accB[nb][r]);
+        // dQ = R^T (dQ + sum dS K); the pair partner column sits in lane l ^ 1
+        if (a.rope) v = rope_back(v, __shfl_xor(v, 1), col, (long long)row + a.rope_pos, fq);
+        if (row < S && col < d) dQh[(size_t)row * qstride + col] = v;
       }
     }
   }
@@ -958,12 +1002,16 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < PG::NB; ++nb) {
     const int col = dcol0 + nb * 32 + l32;
+    const double fq = a.rope ? rope_freq(col, d, a.rope_base) : 0.0;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = j0 + kb * 32 + crow(r, hf);
+      float vk = oldK[nb][r] + a.scale * accK[nb][r];
+      // dK = R^T (dK + sum dS^T Q); the pair partner column sits in lane l ^ 1
+      if (a.rope) vk = rope_back(vk, __shfl_xor(vk, 1), col, (long long)row + a.rope_pos, fq);
       if (row < S && col < d) {
         const size_t off = (size_t)row * kstride + col;
-        dKh[off] = oldK[nb][r] + a.scale * accK[nb][r];
+        dKh[off] = vk;
         dVh[off] = oldV[nb][r] + accV[nb][r];
       }
     }
@@ -1234,14 +1282,27 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
       oldV[r][nb] = ok ? dVh[off] : 0.f;
     }
   }
+  double fq[NB];  // RoPE frequency of each of this lane's columns
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) fq[nb] = a.rope ? rope_freq(col0 + nb, d, a.rope_base) : 0.0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = j0 + kb * 32 + crow(r, hf);
+    float vk[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) vk[nb] = oldK[r][nb] + a.scale * accK[nb][r];
+    if (a.rope) {  // dK = R^T (dK + sum dS^T Q)
+      float pv[NB];
+      rope_partners_perm<NB>(vk, l32, pv);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        vk[nb] = rope_back(vk[nb], pv[nb], col0 + nb, (long long)row + a.rope_pos, fq[nb]);
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (row < S && col0 + nb < d) {
         const size_t off = (size_t)row * kstride + col0 + nb;
-        dKh[off] = oldK[r][nb] + a.scale * accK[nb][r];
+        dKh[off] = vk[nb];
         dVh[off] = oldV[r][nb] + accV[nb][r];
       }
     }
@@ -1382,13 +1443,25 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
     for (int nb = 0; nb < NB; ++nb)
       old[r][nb] = (row < S && col0 + nb < d) ? dQh[(size_t)row * qstride + col0 + nb] : 0.f;
   }
+  double fq[NB];  // RoPE frequency of each of this lane's columns
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) fq[nb] = a.rope ? rope_freq(col0 + nb, d, a.rope_base) : 0.0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = i0 + qb * 32 + crow(r, hf);
+    float v[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) v[nb] = old[r][nb] + a.scale * acc[nb][r];
+    if (a.rope) {  // dQ = R^T (dQ + sum dS K)
+      float pv[NB];
+      rope_partners_perm<NB>(v, l32, pv);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        v[nb] = rope_back(v[nb], pv[nb], col0 + nb, (long long)row + a.rope_pos, fq[nb]);
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      if (row < S && col0 + nb < d)
-        dQh[(size_t)row * qstride + col0 + nb] = old[r][nb] + a.scale * acc[nb][r];
+      if (row < S && col0 + nb < d) dQh[(size_t)row * qstride + col0 + nb] = v[nb];
   }
 }
 
@@ -1795,11 +1868,12 @@ static attn_status_t launch_fwd(const FwdArgs& a, hipStream_t st) {
 }
 
 // The backward, with D computed by the kernels (O == NULL) or read off the
-// forward output O.
+// forward output O; rope: dQ and dK rotated back afterwards (rope_bwd).
 static attn_status_t run_bwd(const float* Q, const float* K, const float* V, const float* O,
                              const float* dO, const float* LSE, const uint32_t* seg, float* dQ,
                              float* dK, float* dV, int seq_len, int n_heads, int n_kv_heads,
-                             int head_dim, float scale, void* stream) {
+                             int head_dim, float scale, void* stream, int rope = 0,
+                             float rope_base = 0.f, int pos_offset = 0) {
   attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, scale);
   if (rc != ATTN_OK) return rc;
   const void* ptrs[] = {Q, K, V, O, dO, LSE, seg, dQ, dK, dV};
@@ -1828,6 +1902,9 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   a.slot_off = reinterpret_cast<long long*>(wsb + pl.off_slot);
   a.scratch = pl.stored ? reinterpret_cast<float*>(wsb + pl.off_scr) : nullptr;
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim; a.scale = scale;
+  a.rope = rope;
+  a.rope_pos = pos_offset;
+  a.rope_base = (double)rope_base;
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, st, seg, seq_len, a.blk_min, a.blk_max, a.slot_off);
   rc = hip_check(hipGetLastError(), "launching k_prep");
@@ -1866,6 +1943,24 @@ extern "C" attn_status_t attn_bwd_o(const float* Q, const float* K, const float*
     return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
   return run_bwd(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
                  scale, stream);
+}
+
+extern "C" attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V,
+                                       const float* O, const float* dO, const float* LSE,
+                                       const uint32_t* seg, float* dQ, float* dK, float* dV,
+                                       int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                                       float scale, float rope_base, int pos_offset,
+                                       void* stream) {
+  g_err[0] = 0;
+  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  if (!(rope_base > 0.f) || !isfinite(rope_base))
+    return fail(ATTN_ERR_INVALID_ARG, "rope_base must be positive and finite (got %g)", (double)rope_base);
+  if (pos_offset < 0) return fail(ATTN_ERR_INVALID_ARG, "pos_offset must be >= 0 (got %d)", pos_offset);
+  if (seq_len > 0 && (long long)pos_offset + seq_len - 1 > 0x7fffffffll)
+    return fail(ATTN_ERR_INVALID_ARG, "pos_offset + seq_len exceeds 2^31");
+  return run_bwd(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
+                 scale, stream, 1, rope_base, pos_offset);
 }
 
 extern "C" attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V,

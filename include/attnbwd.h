@@ -118,8 +118,29 @@ attn_status_t attn_bwd_o(const float* Q, const float* K, const float* V, const f
                          void* stream);
 
 /*
+ * attn_bwd_rope -- attn_bwd (O == NULL) or attn_bwd_o (O given) followed by
+ * the RoPE backward of page "llm.istanbul -- 10_backward_attention.wgsl"
+ * (kernels rope_q_backward, rope_k_backward) applied in place to dQ and dK,
+ * fused into the kernels' write-back: for row s, head h and column pair
+ * (2p, 2p+1), angle = (s + pos_offset) * rope_base^(-2p/head_dim) and
+ * (g0, g1) -> (g0 cos + g1 sin, -g0 sin + g1 cos), the transpose of the
+ * forward rotation (q0 cos - q1 sin, q0 sin + q1 cos).  So
+ *   dQ <- R^T (dQ + attention gradient),  dK <- R^T (dK + attention gradient),
+ *   dV <- dV + attention gradient,
+ * exactly what the unfused sequence leaves.  Q and K are the rotated tensors
+ * the forward used.  The angle is computed in double precision.
+ * Errors as attn_bwd, plus ATTN_ERR_INVALID_ARG for rope_base <= 0 or not
+ * finite, pos_offset < 0, or pos_offset + seq_len > 2^31.
+ */
+attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, const float* O,
+                            const float* dO, const float* LSE, const uint32_t* seg,
+                            float* dQ, float* dK, float* dV,
+                            int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                            float rope_base, int pos_offset, void* stream);
+
+/*
  * attn_bwd_plan -- host-side query (no GPU work): the workspace bytes one
- * attn_bwd (or attn_bwd_o) call of this size takes, and whether its key-major pass reads
+ * attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes, and whether its key-major pass reads
  * stored probability tiles (1) or recomputes them (0).  Either output pointer
  * may be NULL.  Same argument checks as attn_bwd.
  */

@@ -20,9 +20,9 @@ def seg_dev(seg):
     return None if seg is None else to_dev(np.asarray(seg, np.uint32).astype(np.int32))
 
 
-def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None):
-    """Run attn_bwd (attn_bwd_o when the forward output O is given) on the GPU.
-    Returns numpy (dQ, dK, dV)."""
+def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None, rope=None):
+    """Run attn_bwd (attn_bwd_o when the forward output O is given; attn_bwd_rope
+    when rope = (base, pos_offset)) on the GPU.  Returns numpy (dQ, dK, dV)."""
     t = {k: to_dev(p[k]) for k in ("Q", "K", "V", "dO")}
     if init is None:
         out = [torch.zeros_like(t["Q"]), torch.zeros_like(t["K"]), torch.zeros_like(t["V"])]
@@ -30,7 +30,11 @@ def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None):
         out = [to_dev(x.copy()) for x in init]
     s = seg_dev(p["seg"] if seg is None else seg) if use_seg else None
     L = to_dev(lse.astype(np.float32))
-    if O is None:
+    if rope is not None:
+        binding.attn_bwd_rope(t["Q"], t["K"], t["V"],
+                              None if O is None else to_dev(O.astype(np.float32)), t["dO"], L, s,
+                              *out, float(p["scale"]), float(rope[0]), int(rope[1]))
+    elif O is None:
         binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], L, s, *out, float(p["scale"]))
     else:
         binding.attn_bwd_o(t["Q"], t["K"], t["V"], to_dev(O.astype(np.float32)), t["dO"], L, s,

@@ -15,23 +15,24 @@ def say(msg):
     print(msg, flush=True)
 
 
-def check_full(p, tag, init=None, with_o=False, o_shift=None):
+def check_full(p, tag, init=None, with_o=False, o_shift=None, rope=None):
     """GPU vs oracle on the whole problem.  with_o: through attn_bwd_o with the
-    oracle's forward output (plus o_shift, if given) on both sides."""
+    oracle's forward output (plus o_shift, if given) on both sides.  rope =
+    (base, pos_offset): through attn_bwd_rope."""
     O, lse = oracle.attn_fwd(p["Q"], p["K"], p["V"], p["seg"], p["scale"], want_o=with_o)
     if with_o and o_shift is not None:
         O = (O + o_shift).astype(np.float32)
     ref = oracle.attn_bwd(p["Q"], p["K"], p["V"], p["dO"], lse, p["seg"], p["scale"],
-                          *(init if init is not None else ()), O=O if with_o else None)
+                          *(init if init is not None else ()), O=O if with_o else None, rope=rope)
     say(f"[gpu] {tag}: attn_bwd{'_o' if with_o else ''} S={p['Q'].shape[0]} H={p['Q'].shape[1]} "
         f"KV={p['K'].shape[1]} d={p['Q'].shape[2]}")
-    got = gpu_bwd(p, lse, init=init, O=O if with_o else None)
+    got = gpu_bwd(p, lse, init=init, O=O if with_o else None, rope=rope)
     errs = {}
     pairs = []
     for name, g, w, i0 in zip(("dQ", "dK", "dV"), got, ref,
                               init if init is not None else (None,) * 3):
         g, w = g.astype(np.float64), w.astype(np.float64)
-        if i0 is not None:   # compare the accumulated gradients
+        if i0 is not None and rope is None:   # compare the accumulated gradients
             g, w = g - i0, w - i0
         assert np.all(np.isfinite(g)), f"{tag}: {name} has non-finite values"
         pairs.append((name, g, w))
