@@ -88,6 +88,7 @@ struct BwdArgs {
   float* scratch;        // P and P*dP tiles of every visible pair, or NULL
   int S, H, KV, d;
   float scale;
+  int pair;              // 1: block p serves tiles p and n-1-p (equal causal work)
   int rope;              // 1: rotate dQ, dK back by RoPE after the += (rope_bwd)
   int rope_pos;          // position of row 0 (the page's pos_offset)
   double rope_base;      // frequency base
@@ -406,6 +407,14 @@ __device__ __forceinline__ void rope_partners_perm(const float (&v)[NB], int l32
   }
 }
 
+// The mirror n - 1 - first of tile `first` among n tiles, which a paired block
+// serves after `first`, or -1 (unpaired, or the middle tile of an odd n).  A
+// tile and its mirror together carry the same causal work for every first.
+__device__ __forceinline__ int mirror_tile(int first, int n, int pair) {
+  const int mirror = n - 1 - first;
+  return (pair && mirror != first) ? mirror : -1;
+}
+
 // ---------------------------------------------------------------------------
 // k_prep: per 32-row query block, the smallest and largest document start,
 // and the slot offsets of the P / P*dP tile scratch.  A query block qb can see
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   const int S = a.S, H = a.H, d = a.d;
   const int g = H / a.KV;
   const int qt_hi = (S - 1) / BR;
-  const int qt = qt_hi - (int)(blockIdx.x / H);  // longest rows first
+  auto tile = [&](const int qt) __attribute__((always_inline)) {
   const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
   const int i0 = qt * BR;
   const int q = i0 + qb * 32 + l32;
@@ -736,6 +745,14 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       }
     }
   }
+  };
+  // longest rows first; paired: then the mirror tile
+  const int first = qt_hi - (int)(blockIdx.x / H), second = mirror_tile(first, qt_hi + 1, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // the first tile is done with the LDS
+    tile(second);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -769,7 +786,8 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   const int role = PG::ROLE ? (wave & 1) : 0;
   const int S = a.S, H = a.H, KV = a.KV, d = a.d;
   const int g = H / KV;
-  const int kt = blockIdx.x / KV, kvh = blockIdx.x % KV;  // low key tiles (most queries) first
+  const int kvh = blockIdx.x % KV;
+  auto tile = [&](const int kt) __attribute__((always_inline)) {
   const int j0 = kt * BC;
   const int key = j0 + kb * 32 + l32;
   const bool key_ok = key < S;
@@ -974,7 +992,7 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
         }
     }
     __syncthreads();
-    if (qs == 1) return;
+    if (qs == 0) {
 #pragma unroll
     for (int nb = 0; nb < PG::NB; ++nb)
 #pragma unroll
@@ -982,7 +1000,9 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
         accK[nb][r] += red[((0 * PG::NB + nb) * 16 + r) * 64];
         accV[nb][r] += red[((1 * PG::NB + nb) * 16 + r) * 64];
       }
+    }
   }
+  if (qs == 0) {  // the other query block's waves only contributed partial sums
   // dK += scale * accK, dV += accV: all old values are read first, then all written
   float* __restrict__ dKh = a.dK + (size_t)kvh * d;
   float* __restrict__ dVh = a.dV + (size_t)kvh * d;
@@ -1015,6 +1035,15 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
         dVh[off] = oldV[nb][r] + accV[nb][r];
       }
     }
+  }
+  }  // qs == 0
+  };
+  // low key tiles (most queries) first; paired: then the mirror tile
+  const int first = (int)(blockIdx.x / KV), second = mirror_tile(first, (S + BC - 1) / BC, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // the first tile is done with the LDS
+    tile(second);
   }
 }
 
@@ -1060,7 +1089,8 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   const int dcol0 = DSPLIT ? (wave & 1) * DW : 0;
   const int S = a.S, H = a.H, KV = a.KV, d = a.d;
   const int g = H / KV;
-  const int kt = blockIdx.x / KV, kvh = blockIdx.x % KV;  // low key tiles (most queries) first
+  const int kvh = blockIdx.x % KV;
+  auto tile = [&](const int kt) __attribute__((always_inline)) {
   const int j0 = kt * BC;
   const int kblk = kt * KB + kb;  // this wave's key block
   const int head0 = kvh * g;
@@ -1257,7 +1287,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
         }
     }
     __syncthreads();
-    if (qs == 1) return;
+    if (qs == 0) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -1265,7 +1295,9 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
         accK[nb][r] += red[((0 * NB + nb) * 16 + r) * 64];
         accV[nb][r] += red[((1 * NB + nb) * 16 + r) * 64];
       }
+    }
   }
+  if (qs == 0) {  // the other query block's waves only contributed partial sums
   // dK += scale * accK, dV += accV: all old values are read first, then all written
   float* __restrict__ dKh = a.dK + (size_t)kvh * d;
   float* __restrict__ dVh = a.dV + (size_t)kvh * d;
@@ -1307,6 +1339,15 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
       }
     }
   }
+  }  // qs == 0
+  };
+  // low key tiles (most queries) first; paired: then the mirror tile
+  const int first = (int)(blockIdx.x / KV), second = mirror_tile(first, (S + BC - 1) / BC, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // the first tile is done with the LDS
+    tile(second);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1339,7 +1380,7 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
   const int S = a.S, H = a.H, d = a.d;
   const int g = H / a.KV;
   const int qt_hi = (S - 1) / BR;
-  const int qt = qt_hi - (int)(blockIdx.x / H);  // longest rows first
+  auto tile = [&](const int qt) __attribute__((always_inline)) {
   const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
   const int i0 = qt * BR;
   const int nblk = (S + 31) / 32;
@@ -1462,6 +1503,14 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       if (row < S && col0 + nb < d) dQh[(size_t)row * qstride + col0 + nb] = v[nb];
+  }
+  };
+  // longest rows first; paired: then the mirror tile
+  const int first = qt_hi - (int)(blockIdx.x / H), second = mirror_tile(first, qt_hi + 1, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // the first tile is done with the LDS
+    tile(second);
   }
 }
 
@@ -1734,8 +1783,10 @@ static attn_status_t hip_check(hipError_t e, const char* what) {
 // dS/scale in place of P*dP, or accumulates dQ from dS alone.
 template <int DP, bool DK>
 static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
+  // paired (plain causal): block p serves tile p and its mirror, so each grid halves
+  auto blocks = [&](int ntiles) { return a.pair ? (ntiles + 1) / 2 : ntiles; };
   const int BRq = Pair<DP>::ROLE ? 64 : 128;
-  const int nqt = (a.S + BRq - 1) / BRq;
+  const int nqt = blocks((a.S + BRq - 1) / BRq);
   attn_status_t rc = profile_mark(st, true);
   if (rc != ATTN_OK) return rc;
   if (a.scratch)
@@ -1745,7 +1796,7 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   rc = hip_check(hipGetLastError(), "launching k_dq");
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
-  const int nkt = (a.S + 63) / 64;
+  const int nkt = blocks((a.S + 63) / 64);
   if (a.scratch)
     hipLaunchKernelGGL((k_dkdv_p<DP, DK>), dim3(nkt * a.KV), dim3(256), 0, st, a);
   else
@@ -1754,7 +1805,7 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK || !a.scratch) return rc;
   const int BRs = DP > 128 ? 64 : 128;
-  hipLaunchKernelGGL(k_dqs<DP>, dim3((a.S + BRs - 1) / BRs * a.H), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_dqs<DP>, dim3(blocks((a.S + BRs - 1) / BRs) * a.H), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching k_dqs");
   if (rc == ATTN_OK) rc = profile_mark(st);
   return rc;
@@ -1867,6 +1918,13 @@ static attn_status_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   return hip_check(hipGetLastError(), "launching k_fwd");
 }
 
+// ATTNBWD_PAIR=0 serves every tile from its own block even for plain causal
+// calls; anything else (or unset) pairs them.
+static bool pairing_enabled() {
+  const char* e = getenv("ATTNBWD_PAIR");
+  return !(e && e[0] == '0' && e[1] == 0);
+}
+
 // The backward, with D computed by the kernels (O == NULL) or read off the
 // forward output O; rope: dQ and dK rotated back afterwards (rope_bwd).
 static attn_status_t run_bwd(const float* Q, const float* K, const float* V, const float* O,
@@ -1902,6 +1960,9 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   a.slot_off = reinterpret_cast<long long*>(wsb + pl.off_slot);
   a.scratch = pl.stored ? reinterpret_cast<float*>(wsb + pl.off_scr) : nullptr;
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim; a.scale = scale;
+  // plain causal: every tile's work falls linearly with its index, so a tile
+  // and its mirror sum to the same work (ATTNBWD_PAIR=0 turns this off)
+  a.pair = seg == nullptr && pairing_enabled();
   a.rope = rope;
   a.rope_pos = pos_offset;
   a.rope_base = (double)rope_base;

@@ -66,7 +66,8 @@ def test_fullsize_sampled_parity(wid):
     rq, rk, rv = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], x["dO"], lse, x["seg"], x["scale"],
                                       q_rows, k_rows)
     say(f"[gpu] workload {wid}: attn_bwd S={w.S} H={w.H} KV={w.KV} d={w.d}")
-    dQ, dK, dV = gpu_bwd(x, lse)
+    # a plain causal mask goes in as a NULL seg, as bench.py passes it
+    dQ, dK, dV = gpu_bwd(x, lse, use_seg=bool(np.any(x["seg"])))
     errs = {}
     for name, got, ref in (("dQ", dQ[q_rows], rq), ("dK", dK[k_rows], rk), ("dV", dV[k_rows], rv)):
         assert np.all(np.isfinite(got))
@@ -97,7 +98,7 @@ def test_fullsize_document_invariants(wid):
     w = x["workload"]
     g = w.H // w.KV
     t = {k: to_dev(x[k]) for k in ("Q", "K", "V", "dO")}
-    seg = seg_dev(x["seg"])
+    seg = seg_dev(x["seg"]) if np.any(x["seg"]) else None
     lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev())
     say(f"[gpu] workload {wid}: forward + backward for the invariants")
     binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, None, lse, float(x["scale"]))

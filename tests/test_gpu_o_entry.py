@@ -82,7 +82,7 @@ def test_o_entry_fullsize_sampled(wid):
     rq, rk, rv = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], x["dO"], lse, x["seg"], x["scale"],
                                       q_rows, k_rows, O=O)
     say(f"[gpu] workload {wid}: attn_bwd_o S={w.S} H={w.H} KV={w.KV} d={w.d}")
-    dQ, dK, dV = gpu_bwd(x, lse, O=O)
+    dQ, dK, dV = gpu_bwd(x, lse, O=O, use_seg=bool(np.any(x["seg"])))
     for name, got, ref in (("dQ", dQ[q_rows], rq), ("dK", dK[k_rows], rk), ("dV", dV[k_rows], rv)):
         assert np.all(np.isfinite(got))
         e = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
