@@ -27,7 +27,8 @@ sys.path.insert(0, ROOT)
 PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16/bf16 matrix
 PEAK_HBM = 8.0           # TB/s
-KERNEL_SRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc", "attnbwd.hip")
+CSRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc")
+F16_KERNELS = ("k_cvt16", "k_kv16", "k_q16")
 
 
 def log(*a):
@@ -40,9 +41,14 @@ def valid_pairs(seg):
     return int(np.sum(np.maximum(s - np.asarray(seg, np.int64) + 1, 0)))
 
 
-def source_sha():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(kname):
+    """Hash of the source file holding kernel `kname` and the shared header."""
+    src = "attnbwd_f16.hip" if kname.split("<")[0] in F16_KERNELS else "attnbwd.hip"
+    h = hashlib.sha256()
+    for name in (src, "common.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic(kname, workload):
@@ -58,7 +64,7 @@ def read_traffic(kname, workload):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != source_sha():
+    if vals.get("kernel_source_sha256_16") != source_sha(kname):
         log(f"traffic: {path} was taken on another kernel source; reporting null")
         return None
     try:
@@ -115,6 +121,9 @@ def main():
                     help="time attn_bwd_o (row term read off the forward output O) instead")
     ap.add_argument("--rope", action="store_true",
                     help="time attn_bwd_rope (RoPE backward fused into the write-back, base 1e4)")
+    ap.add_argument("--f16", action="store_true",
+                    help="time attn_bwd_f16 (fp16 matrix-core operands, fp32 accumulation; with "
+                         "--o-entry the forward output is passed)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
@@ -139,15 +148,22 @@ def main():
     O = torch.empty_like(t["Q"]) if args.o_entry else None
     binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, O, lse, scale)
     ws_bytes, stored = binding.bwd_plan(w.S, w.H, w.KV, w.d)
-    log(f"bench: workspace {ws_bytes / 2**30:.2f} GiB, "
-        f"{'stored' if stored else 'recomputed'} probability tiles")
+    dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
+    f16_ws = (4 * w.H + 3 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + w.S * w.H * 4
+    if args.f16:
+        log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
+    else:
+        log(f"bench: workspace {ws_bytes / 2**30:.2f} GiB, "
+            f"{'stored' if stored else 'recomputed'} probability tiles")
     dQ = torch.zeros_like(t["Q"])
     dK = torch.zeros_like(t["K"])
     dV = torch.zeros_like(t["V"])
     torch.cuda.synchronize()
 
     def step():
-        if args.rope:
+        if args.f16:
+            binding.attn_bwd_f16(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
+        elif args.rope:
             binding.attn_bwd_rope(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale,
                                   10000.0, 0)
         elif args.o_entry:
@@ -190,7 +206,13 @@ def main():
     # forms Q.K^T, dO.V^T and dS.K (with the row term), k_dkdv all four
     # (the O entry's row-term kernel, k_rowdot, runs before the first pass and
     # is in ms_per_step only)
-    if stored:
+    # attn_bwd_f16: the fp16 copies plus the row term (S and dP once more when
+    # no forward output is given), k_kv16 (S, dP, P^T.dO, dS^T.Q) and k_q16
+    # (S, dP, dS.K)
+    if args.f16:
+        passes = [("k_cvt16", ms_q, 0.0 if args.o_entry else 4.0), ("k_kv16", ms_k, 8.0),
+                  ("k_q16", ms_s, 6.0)]
+    elif stored:
         passes = [("k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0), ("k_dqs", ms_s, 2.0)]
     else:
         passes = [("k_dq", ms_q, 6.0), ("k_dkdv", ms_k, 8.0)]
@@ -204,8 +226,9 @@ def main():
     kflops = per_pair * w.d * w.H * npairs
     traffic = read_traffic(kname, w.name)
     kach = kflops / (kms * 1e-3) / 1e12
+    peak = PEAK_FP16_MFMA if args.f16 else PEAK_FP32_MFMA
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
-                "peak": PEAK_FP32_MFMA, "unit": "TFLOP/s", "frac": round(kach / PEAK_FP32_MFMA, 4),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(kach / peak, 4),
                 "traffic": traffic, "avg_launch_ms": round(kms, 4)}
 
     cpu = None
@@ -228,17 +251,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16" if args.f16 else "f32",
         "data": "synthetic",
         "pct_of_peak_fp32_matrix": round(100.0 * tflops / PEAK_FP32_MFMA, 2),
         "pct_of_peak_fp16_matrix": round(100.0 * tflops / PEAK_FP16_MFMA, 3),
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
                    "head_dim": w.d, "mask": "causal" if seg is None else "documents",
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
-                   "entry": ("attn_bwd_rope" if args.rope else
+                   "entry": ("attn_bwd_f16" if args.f16 else "attn_bwd_rope" if args.rope else
                              "attn_bwd_o" if args.o_entry else "attn_bwd"),
-                   "stored_tiles": stored,
-                   "workspace_bytes": ws_bytes,
+                   "operands": ("fp16, fp32 accumulation" if args.f16 else "fp32"),
+                   "forward_output_given": bool(args.o_entry),
+                   "stored_tiles": None if args.f16 else stored,
+                   "workspace_bytes": f16_ws if args.f16 else ws_bytes,
                    "kernel_ms": kernel_ms},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -13,8 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_bwd_o", "attn_bwd_plan", "attn_bwd_rope", "attn_fwd_lse",
-            "attn_last_error", "attn_profile_begin", "attn_profile_end")
+EXPORTED = ("attn_bwd", "attn_bwd_f16", "attn_bwd_o", "attn_bwd_plan", "attn_bwd_rope",
+            "attn_fwd_lse", "attn_last_error", "attn_profile_begin", "attn_profile_end")
 
 _lib = None
 
@@ -41,6 +41,8 @@ def load():
     lib.attn_bwd_o.restype = I
     lib.attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, F, I, P]
     lib.attn_bwd_rope.restype = I
+    lib.attn_bwd_f16.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_bwd_f16.restype = I
     lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                   ctypes.POINTER(ctypes.c_int)]
     lib.attn_bwd_plan.restype = I
@@ -149,6 +151,16 @@ def attn_bwd_rope(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, rope_base, pos_of
                               _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                               float(rope_base), int(pos_offset), _stream(stream))
     _raise_on(st, "attn_bwd_rope")
+
+
+def attn_bwd_f16(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
+    """The backward with fp16 matrix-core operands and fp32 accumulation (the C
+    ABI's attn_bwd_f16); O is the forward output or None (row term computed)."""
+    S, H, KV, d = _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV)
+    st = load().attn_bwd_f16(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(seg),
+                             _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
+                             _stream(stream))
+    _raise_on(st, "attn_bwd_f16")
 
 
 def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "attnbwd.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("attnbwd.hip", "attnbwd_f16.hip")]
 LIB = os.path.join(HERE, "libattnbwd.so")
 INCLUDE = os.path.join(ROOT, "include")
 
@@ -22,7 +22,7 @@ HIPCC_FLAGS = [
 def build(verbose: bool = False, extra: list | None = None) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), file=sys.stderr)
     res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)

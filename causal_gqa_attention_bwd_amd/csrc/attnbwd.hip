@@ -56,26 +56,7 @@
 #include <mutex>
 #include <vector>
 
-#include "attnbwd.h"
-
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-#define ATTN_LOG2E 1.4426950408889634f
-#define ATTN_LN2 0.6931471805599453f
-
-__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
-// row of a 32x32 accumulator tile held in register r by half-wave hf
-__device__ __forceinline__ int crow(int r, int hf) { return 8 * (r >> 2) + 4 * hf + (r & 3); }
-
-__device__ __forceinline__ f32x16 zero16() {
-  f32x16 z;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) z[i] = 0.f;
-  return z;
-}
+#include "common.h"
 
 struct BwdArgs {
   const float *Q, *K, *V, *dO, *LSE;
@@ -139,63 +120,6 @@ __device__ __forceinline__ void pin_agpr(float* v) {
 // on a pad granule or past head_dim carry an offset beyond any range, so all
 // of them deposit zeros without touching memory.
 // ---------------------------------------------------------------------------
-#define ATTN_BUF_OOB 0x80000000u        // beyond every buffer range used here
-#define ATTN_BUF_WORD3 0x00020000       // raw buffer, 32-bit data format
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Buffer resource of `nbytes` bytes at `base` (nbytes = 0: every load reads zeros).
-__device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t nbytes) {
-  const uint64_t p = (uint64_t)base;
-  i32x4 r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(p >> 32));  // stride 0
-  r.z = __builtin_amdgcn_readfirstlane((int)nbytes);
-  r.w = ATTN_BUF_WORD3;
-  return r;
-}
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Direct buffer->LDS loads (16 or 4 bytes per lane; lane i's data lands at
-// lds + i * size).  Issued from inline assembly so that the compiler does not
-// treat every later LDS read as possibly overlapping these writes and wait for
-// them: ordering is explicit instead -- every reader of a tile passes a
-// tile_barrier (s_waitcnt vmcnt(0) + s_barrier) issued after the tile's loads,
-// and no buffer is refilled before all waves have passed a barrier after
-// their last read of it.  M0 carries the LDS address and is restored.
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, uint32_t lds_byte) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(r)
-      : "memory");
-}
-__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, uint32_t lds_byte) {
-  int saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "buffer_load_dword %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(r)
-      : "memory");
-}
-__device__ __forceinline__ void dma16(const i32x4& r, uint32_t voff, const void* lds) {
-  dma16(r, voff, lds_addr(lds));
-}
-__device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, const void* lds) {
-  dma4(r, voff, lds_addr(lds));
-}
-
 // Padded ROWS x DP tile filled by 1 KiB chunks.
 template <int ROWS, int DP>
 struct PadTile {
@@ -251,23 +175,6 @@ struct TileLoader {
     for (int i = 0; i < T::CPW; ++i) load(i, r, lds_byte, wave_u);
   }
 };
-
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations,
-// then s_barrier.  Unlike __syncthreads it does not wait for outstanding global
-// loads, so direct-to-LDS loads of the next tile stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// Wait for all of this wave's outstanding memory operations (the current
-// tile's direct-to-LDS loads among them), then a workgroup barrier: the tile is
-// complete in LDS and every wave has finished with the previous tile.  The
-// wait is the compiler's own s_waitcnt, so it also knows that every load it
-// issued before has landed and adds no later waits for them.
-__device__ __forceinline__ void tile_barrier() {
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt and lgkmcnt all zero
-  asm volatile("s_barrier" ::: "memory");
-}
 
 // Above 128 columns a pair of waves shares one 32x32 score block by role:
 // role 0 forms the Q.K product, role 1 the dO.V product, over all DP columns,
@@ -359,15 +266,6 @@ struct SpreadLoads {
   }
 };
 
-// Head served by block b of a (tile, head) grid, grouping the heads of one KV
-// group on one XCD: workgroups are dispatched round-robin over the 8 XCDs, so
-// blocks b, b+8, b+16, ... share an L2; when H is a multiple of 8 they get
-// heads x*(H/8) .. x*(H/8) + H/8 - 1 of XCD slot x = b % 8, i.e. whole groups.
-__device__ __forceinline__ int xcd_head(int r, int H) {
-  if (H % 8 != 0) return r;
-  return (r % 8) * (H / 8) + r / 8;
-}
-
 // ---------------------------------------------------------------------------
 // RoPE backward in the epilogues (page "llm.istanbul --
 // 10_backward_attention.wgsl", kernels rope_q_backward / rope_k_backward):
@@ -405,14 +303,6 @@ __device__ __forceinline__ void rope_partners_perm(const float (&v)[NB], int l32
     if ((l32 & 1) == 0) { pv[0] = v[1]; pv[1] = v[0]; pv[2] = up; }
     else { pv[0] = dn; pv[1] = v[2]; pv[2] = v[1]; }
   }
-}
-
-// The mirror n - 1 - first of tile `first` among n tiles, which a paired block
-// serves after `first`, or -1 (unpaired, or the middle tile of an odd n).  A
-// tile and its mirror together carry the same causal work for every first.
-__device__ __forceinline__ int mirror_tile(int first, int n, int pair) {
-  const int mirror = n - 1 - first;
-  return (pair && mirror != first) ? mirror : -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -1678,13 +1568,15 @@ __global__ __launch_bounds__(256) void k_fwd(FwdArgs a) {
 // ---------------------------------------------------------------------------
 static thread_local char g_err[512];
 
-static attn_status_t fail(attn_status_t st, const char* fmt, ...) {
+attn_status_t fail(attn_status_t st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
   vsnprintf(g_err, sizeof(g_err), fmt, ap);
   va_end(ap);
   return st;
 }
+
+void clear_error() { g_err[0] = 0; }
 
 extern "C" const char* attn_last_error(void) { return g_err; }
 
@@ -1733,7 +1625,7 @@ extern "C" attn_status_t attn_profile_end(double* ms, int* n_calls) {
 
 // Record one profile event on `st` if the measurement hooks are on; `first`
 // opens the record of a new call.
-static attn_status_t profile_mark(hipStream_t st, bool first = false) {
+attn_status_t profile_mark(hipStream_t st, bool first) {
   if (!g_prof.on) return ATTN_OK;
   hipEvent_t e;
   hipError_t err = hipEventCreate(&e);
@@ -1744,7 +1636,7 @@ static attn_status_t profile_mark(hipStream_t st, bool first = false) {
   return ATTN_OK;
 }
 
-static int padded_dim(int d) {
+int padded_dim(int d) {
   if (d <= 32) return 32;
   if (d <= 64) return 64;
   if (d <= 96) return 96;
@@ -1753,9 +1645,9 @@ static int padded_dim(int d) {
   return 256;
 }
 
-static bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u); }
 
-static attn_status_t check_common(int S, int H, int KV, int d, float scale) {
+attn_status_t check_common(int S, int H, int KV, int d, float scale) {
   if (S < 0) return fail(ATTN_ERR_INVALID_ARG, "seq_len = %d is negative", S);
   if (H < 1 || KV < 1) return fail(ATTN_ERR_INVALID_ARG, "n_heads = %d, n_kv_heads = %d", H, KV);
   if (H % KV != 0)
@@ -1771,7 +1663,7 @@ static attn_status_t check_common(int S, int H, int KV, int d, float scale) {
   return ATTN_OK;
 }
 
-static attn_status_t hip_check(hipError_t e, const char* what) {
+attn_status_t hip_check(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ATTN_OK;
 }
@@ -1829,7 +1721,7 @@ static attn_status_t launch_bwd(const BwdArgs& a, int dp, hipStream_t st) {
 static std::mutex g_pool_mu;
 static std::map<int, hipMemPool_t> g_pools;
 
-static attn_status_t device_pool(hipMemPool_t* out) {
+attn_status_t device_pool(hipMemPool_t* out) {
   int dev = 0;
   attn_status_t rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
   if (rc != ATTN_OK) return rc;
@@ -1918,9 +1810,25 @@ static attn_status_t launch_fwd(const FwdArgs& a, hipStream_t st) {
   return hip_check(hipGetLastError(), "launching k_fwd");
 }
 
+attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* blk_min, uint32_t* blk_max,
+                          long long* slot_off, hipStream_t st) {
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, st, seg, S, blk_min, blk_max, slot_off);
+  return hip_check(hipGetLastError(), "launching k_prep");
+}
+
+attn_status_t launch_rowdot(const float* O, const float* dO, float* D, long long rows, int d,
+                            hipStream_t st) {
+  int tpr = 1;
+  while (tpr < d / 4) tpr <<= 1;
+  const long long waves = (rows * tpr + 63) / 64;
+  const int blocks = (int)std::min<long long>((waves + 3) / 4, 4096);
+  hipLaunchKernelGGL(k_rowdot, dim3(blocks), dim3(256), 0, st, O, dO, D, rows, d);
+  return hip_check(hipGetLastError(), "launching k_rowdot");
+}
+
 // ATTNBWD_PAIR=0 serves every tile from its own block even for plain causal
 // calls; anything else (or unset) pairs them.
-static bool pairing_enabled() {
+bool pairing_enabled() {
   const char* e = getenv("ATTNBWD_PAIR");
   return !(e && e[0] == '0' && e[1] == 0);
 }
@@ -1967,17 +1875,8 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   a.rope_pos = pos_offset;
   a.rope_base = (double)rope_base;
 
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, st, seg, seq_len, a.blk_min, a.blk_max, a.slot_off);
-  rc = hip_check(hipGetLastError(), "launching k_prep");
-  if (rc == ATTN_OK && O) {
-    const long long rows = (long long)seq_len * n_heads;
-    int tpr = 1;
-    while (tpr < head_dim / 4) tpr <<= 1;
-    const long long waves = (rows * tpr + 63) / 64;
-    const int blocks = (int)std::min<long long>((waves + 3) / 4, 4096);
-    hipLaunchKernelGGL(k_rowdot, dim3(blocks), dim3(256), 0, st, O, dO, a.Dws, rows, head_dim);
-    rc = hip_check(hipGetLastError(), "launching k_rowdot");
-  }
+  rc = launch_prep(seg, seq_len, a.blk_min, a.blk_max, a.slot_off, st);
+  if (rc == ATTN_OK && O) rc = launch_rowdot(O, dO, a.Dws, (long long)seq_len * n_heads, head_dim, st);
   if (rc == ATTN_OK) rc = O ? launch_bwd<true>(a, dp, st) : launch_bwd<false>(a, dp, st);
   attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");
   return rc != ATTN_OK ? rc : rc2;

@@ -1,0 +1,748 @@
+// attnbwd_f16.hip -- the attention backward with 16-bit matrix-core operands
+// (attn_bwd_f16): the gradients of page "llm.istanbul --
+// 10_backward_attention.wgsl" (kernel attention_backward: P, dP, D, dS, then
+// dV = P^T dO, dK = dS^T Q, dQ = dS K, all +=), with every product operand --
+// Q, K, V, dO, the probabilities P and the score gradients scale*dS -- rounded
+// to fp16 (round to nearest even) and every sum accumulated in fp32.  Inputs,
+// outputs, LSE, the row term D, the exponent and the masks stay fp32.  The
+// pages compute in fp32 throughout; this is the reduced-precision variant of
+// the same sums, at 16 times the fp32 matrix rate of the hardware.
+//
+// Per call:
+//   k_prep    per 32-row query block seg min / max (shared with attn_bwd).
+//   k_cvt16   fp16 copies of Q, dO, K, V as head-major row tiles [head][Sp][DP],
+//             and d-major copies of Q, dO, K [head][DP][Sp] for the products
+//             that contract over rows.  Sp = S rounded up to 128, DP = head_dim
+//             rounded up to a tile width; padding is zero.
+//   D         k_rowdot (D = dO . O) when the forward output is given, else
+//             k_q16<D only>: S^T and dP^T of every visible pair, D = sum P dP.
+//   k_kv16    key-major, one workgroup per (64-key tile, KV head), owns its
+//             dK / dV rows and sums the group's heads; a wave pair per 32-key
+//             block: role 0 forms S = Q K^T, P, and dV += P^T dO; role 1 forms
+//             dP = dO V^T, dS from P (handed over through LDS), and
+//             dK += dS^T Q.  4 products per visible pair.
+//   k_q16     query-major, one workgroup per (128-query tile, head): S^T, dP^T,
+//             dS, dQ += dS K.  3 products per visible pair.
+// Executed products per visible pair: 7 with the forward output, 9 without
+// (the page's method credits 5).
+//
+// MFMA v_mfma_f32_32x32x16_f16 (C[32x32] += A[32x16] B[16x32]), lane layout
+// checked on the device: lane l supplies A[l%32][8(l/32) + j] and
+// B[8(l/32) + j][l%32] for j = 0..7 (16 bytes each) and holds C like the fp32
+// product (register r: row crow(r, l/32), column l%32).  Registers 8s..8s+7 of
+// an accumulator tile, rounded to fp16, are therefore the A operand of a
+// product that contracts over the tile's rows, taken in the row order
+// crow(8s + j, hf).  The d-major copies store every 16-row group in that order
+// (rows 4..7 and 8..11 swapped, tpos), so the matching B operand is one
+// 16-byte read per lane.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "common.h"
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma16(const h8& a, const h8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Registers 8s .. 8s+7 of accumulator tile c, rounded to fp16 (nearest even).
+__device__ __forceinline__ h8 pack8(const f32x16& c, int s) {
+  f32x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = c[8 * s + j];
+  return __builtin_convertvector(v, h8);
+}
+
+// Position of row q of a 32-row block inside the d-major copies (and the row
+// at position q): bits 2 and 3 swapped, so that positions 8hf + j of a 16-row
+// group hold rows crow(j, hf).
+__device__ __forceinline__ int tpos(int q) { return (q & ~12) | ((q & 4) << 1) | ((q >> 1) & 4); }
+
+// ---------------------------------------------------------------------------
+// fp16 tiles in LDS: ROWS x CH chunks of 16 bytes, unpadded; chunk c of row r
+// sits at chunk r*CH + (c ^ swz(r)).  The swizzle makes the 16-byte reads of
+// 8 (and of 16) consecutive rows at one chunk hit distinct banks for every CH
+// used here (4, 8, 12, 16, 24, 32), and keeps c ^ swz(r) below CH.
+// ---------------------------------------------------------------------------
+template <int CH>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CH % 8 != 0) return ((r >> 1) ^ (r >> 2)) & 3;
+  else if constexpr (CH % 16 != 0) return (r ^ (r >> 3)) & 7;
+  else return (r ^ (r >> 4)) & 15;
+}
+
+template <int ROWS, int CH>
+struct Tile16 {
+  static constexpr int CHUNKS = ROWS * CH;
+  // wave-wide 1 KiB loads per tile, a multiple of 4 so that every wave issues
+  // the same number (the surplus loads deposit zeros past the tile's chunks)
+  static constexpr int NCH = (CHUNKS + 255) / 256 * 4;
+  static constexpr int BYTES = NCH * 1024;
+  static constexpr int CPW = NCH / 4;              // loads per wave
+  // LDS byte offset of chunk c of row r
+  __device__ static __forceinline__ uint32_t at(int r, int c) {
+    return (uint32_t)(r * CH + (c ^ swz<CH>(r))) * 16u;
+  }
+};
+
+// Per-lane global byte offsets of the chunks this wave loads into a Tile16
+// whose rows are `gstride` bytes apart in memory: physical chunk p of the tile
+// takes logical chunk (p % CH) ^ swz(p / CH) of row p / CH.
+template <int ROWS, int CH>
+struct Loader16 {
+  using T = Tile16<ROWS, CH>;
+  uint32_t off[T::CPW];
+  __device__ __forceinline__ void init(uint32_t gstride, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < T::CPW; ++i) {
+      const int p = (wave + 4 * i) * 64 + lane;
+      const int r = p / CH, c = (p % CH) ^ swz<CH>(p / CH);
+      off[i] = p < T::CHUNKS ? (uint32_t)r * gstride + (uint32_t)c * 16u : ATTN_BUF_OOB;
+    }
+  }
+  __device__ __forceinline__ void load(const i32x4& rs, uint32_t lds_byte, int wave) const {
+#pragma unroll
+    for (int i = 0; i < T::CPW; ++i) dma16(rs, off[i], lds_byte + (wave + 4 * i) * 1024);
+  }
+};
+
+// Wait until at most N of this wave's vector-memory operations (its
+// direct-to-LDS loads among them) are outstanding; loads retire in issue
+// order, so everything issued before the last N has landed.  Other counters
+// are left alone.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+struct F16Args {
+  const _Float16 *Qh, *dOh, *Kh, *Vh;  // [heads][Sp][DP] row tiles
+  const _Float16 *QT, *dOT, *KT;       // [heads][DP][Sp], each 32-row block in tpos order
+  const float* LSE;                    // [S, H]
+  const uint32_t* seg;                 // [S], NULL = all zeros
+  float *dQ, *dK, *dV;
+  float* D;                            // [S, H] row term
+  const uint32_t* blk_min;             // [ceil(S/32)] min seg per 32-row query block
+  int S, Sp, H, KV, d;
+  float scale;
+  int pair;                            // 1: block p serves tiles p and n-1-p (plain causal)
+  int splits;                          // k_kv16: workgroups sharing one key tile's heads
+  float* part;                         // [2 * splits][S, KV, d] partial dK, dV (splits > 1)
+};
+
+struct CvtArgs {
+  const float *Q, *dO, *K, *V;
+  _Float16 *Qh, *dOh, *Kh, *Vh, *QT, *dOT, *KT;
+  int S, Sp, H, KV, d;
+};
+
+// ---------------------------------------------------------------------------
+// k_cvt16: one workgroup per (32-row block, head) of one tensor; blocks
+// [0, nb*H) convert Q, then dO, then K (nb*KV), then V.  Rows past S and
+// columns past head_dim become zeros.  V needs no d-major copy.
+// ---------------------------------------------------------------------------
+template <int DP>
+__global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
+  __shared__ _Float16 sT[DP][34];  // d-major staging of the block (positions tpos)
+  const int nb = a.Sp / 32;
+  const long long nq = (long long)nb * a.H, nk = (long long)nb * a.KV;
+  long long b = blockIdx.x;
+  int which;
+  if (b < nq) which = 0;
+  else if (b < 2 * nq) { which = 1; b -= nq; }
+  else if (b < 2 * nq + nk) { which = 2; b -= 2 * nq; }
+  else { which = 3; b -= 2 * nq + nk; }
+  const int heads = which < 2 ? a.H : a.KV;
+  const int head = (int)(b % heads);
+  const int r0 = (int)(b / heads) * 32;
+  const float* src = which == 0 ? a.Q : which == 1 ? a.dO : which == 2 ? a.K : a.V;
+  _Float16* dst = which == 0 ? a.Qh : which == 1 ? a.dOh : which == 2 ? a.Kh : a.Vh;
+  _Float16* dstT = which == 0 ? a.QT : which == 1 ? a.dOT : which == 2 ? a.KT : nullptr;
+  const size_t stride = (size_t)heads * a.d;
+  for (int i = threadIdx.x; i < 32 * (DP / 2); i += 256) {
+    const int r = i / (DP / 2), c = 2 * (i % (DP / 2));
+    const int s = r0 + r;
+    f32x2 v = {0.f, 0.f};
+    if (s < a.S && c < a.d)
+      v = *reinterpret_cast<const f32x2*>(src + (size_t)s * stride + (size_t)head * a.d + c);
+    const h2 hv = __builtin_convertvector(v, h2);
+    *reinterpret_cast<h2*>(dst + ((size_t)head * a.Sp + s) * DP + c) = hv;
+    if (dstT) {
+      sT[c][tpos(r)] = hv[0];
+      sT[c + 1][tpos(r)] = hv[1];
+    }
+  }
+  if (dstT) {  // the same for the whole workgroup
+    __syncthreads();
+    for (int i = threadIdx.x; i < DP * 16; i += 256) {
+      const int c = i / 16, p = 2 * (i % 16);
+      const h2 hv = {sT[c][p], sT[c][p + 1]};
+      *reinterpret_cast<h2*>(dstT + ((size_t)head * DP + c) * a.Sp + r0 + p) = hv;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_q16: query-major, one workgroup per (128-query tile, head).  Wave w owns
+// queries i0 + 32w + l%32 and keeps their Q and dO rows in registers as the B
+// operands of S^T = K Q^T and dP^T = V dO^T; 32-key blocks of K, V (row
+// tiles) and K^T stream through LDS, double-buffered.  The score tiles hold
+// key crow(r, hf) of query l%32, so each lane's LSE, D and seg are one value.
+//   DONLY: D[q] = sum_j P dP (the row term, for the key-major pass).
+//   else:  dQ += dS K with dS = scale P (dP - D), A operand straight from the
+//          dS registers, B from the K^T tile.  Above 128 columns the dQ
+//          columns come in two parts, one workgroup each (both form S and dP),
+//          so that a wave's accumulators fit the register file.
+// ---------------------------------------------------------------------------
+template <int DP, bool DONLY>
+struct QGeom {
+  static constexpr int NC = (DP > 128 && !DONLY) ? 2 : 1;  // dQ column parts
+  static constexpr int DW = DP / NC;
+};
+
+template <int DP, bool DONLY>
+__global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
+  constexpr int CH = DP / 8;   // 16-byte chunks per row
+  constexpr int NT = DP / 16;  // k-steps of the d-contractions
+  constexpr int NC = QGeom<DP, DONLY>::NC, DW = QGeom<DP, DONLY>::DW;
+  constexpr int NO = DW / 32;  // 32-column output tiles of the part
+  using RT = Tile16<32, CH>;
+  using TT = Tile16<DW, 4>;
+  constexpr int STAGE = 2 * RT::BYTES + (DONLY ? 0 : TT::BYTES);
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  __shared__ uint32_t sMin[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int S = a.S, H = a.H;
+  const int g = H / a.KV;
+  const int qt_hi = (S - 1) / 128;
+  const float sc2 = a.scale * ATTN_LOG2E;
+  const uint32_t smem0 = lds_addr(smem);
+  Loader16<32, CH> ldr;
+  ldr.init(DP * 2, wave, lane);
+  Loader16<DW, 4> ldt;
+  if constexpr (!DONLY) ldt.init((uint32_t)a.Sp * 2u, wave, lane);
+  const int cpart = (int)(blockIdx.x / H) % NC;
+
+  auto tile = [&](const int qt) __attribute__((always_inline)) {
+    const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
+    const int i0 = qt * 128;
+    const int q = i0 + 32 * wave + l32;  // < Sp: the copies hold zero rows up to Sp
+    const bool q_ok = q < S;
+    h8 qreg[NT], oreg[NT];
+    const _Float16* qrow = a.Qh + ((size_t)h * a.Sp + q) * DP + 8 * hf;
+    const _Float16* orow = a.dOh + ((size_t)h * a.Sp + q) * DP + 8 * hf;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      qreg[t] = *reinterpret_cast<const h8*>(qrow + 16 * t);
+      oreg[t] = *reinterpret_cast<const h8*>(orow + 16 * t);
+    }
+    const float lse2 = q_ok ? a.LSE[(size_t)q * H + h] * ATTN_LOG2E : 0.f;
+    const uint32_t sq = !q_ok ? 0xffffffffu : (a.seg ? a.seg[q] : 0u);
+    float Dq = 0.f;
+    if constexpr (!DONLY) Dq = q_ok ? a.D[(size_t)q * H + h] : 0.f;
+
+    // key blocks: from the smallest document start of the tile to the diagonal
+    const int nblk = (S + 31) / 32;
+    const int qb = (i0 >> 5) + wave;
+    const uint32_t lo = qb < nblk ? a.blk_min[qb] : 0xffffffffu;
+    if (lane == 0) sMin[wave] = lo;
+    __syncthreads();
+    const uint32_t lo_all = min(min(sMin[0], sMin[1]), min(sMin[2], sMin[3]));
+    const int kb_last = min(i0 + 127, S - 1) / 32;
+    const int kb_first = (int)min(lo_all / 32u, (uint32_t)kb_last + 1u);
+    // this wave's key blocks (a wave past S has lo = ~0 and sees none)
+    const int w_lo = (int)min(lo / 32u, 0x7fffffffu);
+    const int w_hi = min(i0 + 32 * wave + 31, S - 1) / 32;
+
+    auto issue = [&](int kb, int buf) {
+      const uint32_t st = smem0 + (uint32_t)(buf * STAGE);
+      const size_t roff = ((size_t)kvh * a.Sp + (size_t)kb * 32) * DP;
+      ldr.load(buf_rsrc(a.Kh + roff, 32 * DP * 2), st, wave);
+      ldr.load(buf_rsrc(a.Vh + roff, 32 * DP * 2), st + RT::BYTES, wave);
+      if constexpr (!DONLY)
+        ldt.load(buf_rsrc(a.KT + ((size_t)kvh * DP + (size_t)cpart * DW) * a.Sp + (size_t)kb * 32,
+                          (uint32_t)(((size_t)(DW - 1) * a.Sp + 32) * 2)),
+                 st + 2 * RT::BYTES, wave);
+    };
+
+    f32x16 acc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) acc[o] = zero16();
+    float Dacc = 0.f;
+    if (kb_first <= kb_last) {
+      issue(kb_first, 0);
+      tile_barrier();
+      for (int kb = kb_first; kb <= kb_last; ++kb) {
+        const int buf = (kb - kb_first) & 1;
+        if (kb < kb_last) issue(kb + 1, buf ^ 1);
+        if (kb >= w_lo && kb <= w_hi) {
+          const char* st = smem + buf * STAGE;
+          f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const h8 ka = *reinterpret_cast<const h8*>(st + RT::at(l32, 2 * t + hf));
+            const h8 va = *reinterpret_cast<const h8*>(st + RT::BYTES + RT::at(l32, 2 * t + hf));
+            s = mfma16(ka, qreg[t], s);
+            dp = mfma16(va, oreg[t], dp);
+          }
+          f32x16 ds;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kb * 32 + crow(r, hf);
+            const bool vis = key <= q && (uint32_t)key >= sq;
+            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2)) : 0.f;
+            if constexpr (DONLY) Dacc = fmaf(p, dp[r], Dacc);
+            else ds[r] = p * (dp[r] - Dq) * a.scale;
+          }
+          if constexpr (!DONLY) {
+            const h8 a0 = pack8(ds, 0), a1 = pack8(ds, 1);
+            const char* kt = st + 2 * RT::BYTES;
+#pragma unroll
+            for (int o = 0; o < NO; ++o) {
+              const int row = 32 * o + l32;
+              acc[o] = mfma16(a0, *reinterpret_cast<const h8*>(kt + TT::at(row, hf)), acc[o]);
+              acc[o] = mfma16(a1, *reinterpret_cast<const h8*>(kt + TT::at(row, 2 + hf)), acc[o]);
+            }
+          }
+        }
+        tile_barrier();  // next block resident; everyone done with this one
+      }
+    }
+    if constexpr (DONLY) {
+      const float Dt = Dacc + __shfl_xor(Dacc, 32);  // the half-waves saw disjoint keys
+      if (q_ok && hf == 0) a.D[(size_t)q * H + h] = Dt;
+    } else {
+      float* dQh = a.dQ + (size_t)h * a.d;
+      const size_t qstride = (size_t)H * a.d;
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        const int col = cpart * DW + 32 * o + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i0 + 32 * wave + crow(r, hf);
+          if (row < S && col < a.d) dQh[(size_t)row * qstride + col] += acc[o][r];
+        }
+      }
+    }
+  };
+  // longest rows first; paired: then the mirror tile
+  const int first = qt_hi - (int)(blockIdx.x / (H * NC));
+  const int second = mirror_tile(first, qt_hi + 1, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // the first tile is done with the LDS
+    tile(second);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_kv16: key-major, one workgroup per (128-key tile, KV head, head split,
+// column part).  Wave w owns key block w (keys j0 + 32w + l%32) and holds its
+// K and V rows in registers as the B operands of S = Q K^T and dP = dO V^T.
+// Per visible 32-row query block and head of the split's share of the group,
+// the Q and dO row tiles, the part's columns of their d-major tiles, and the
+// rows' LSE, D and seg stream through an LDS ring of NBUF stages (NBUF - 1
+// steps in flight), shared by the four waves.  Each wave forms P and
+// dS = scale P (dP - D) in registers and accumulates dV += P^T dO and
+// dK += dS^T Q over its part's output columns.  Above 128 columns the output
+// columns come in two parts, one workgroup each (both form S and dP), so that
+// a wave's accumulators fit the register file.  The visible query blocks of
+// the tile (blk_min <= last key, at or after the diagonal) come from 64-block
+// ballots, the same in every wave.
+// With one split the workgroup adds its sums into dK, dV; with several, each
+// split writes its partial sums to its own slice of `part`, and k_sumparts
+// adds the slices in split order (deterministic).
+// ---------------------------------------------------------------------------
+template <int DP>
+struct KvGeom {
+  static constexpr int NC = DP > 128 ? 2 : 1;  // output column parts
+  static constexpr int DW = DP / NC;           // output columns per part
+  static constexpr int NOW = DW / 32;          // 32-column output tiles per part
+  using RT = Tile16<32, DP / 8>;
+  using TT = Tile16<DW, 4>;
+  static constexpr int OFF_DO = RT::BYTES, OFF_QT = 2 * RT::BYTES;
+  static constexpr int OFF_DOT = 2 * RT::BYTES + TT::BYTES;
+  static constexpr int OFF_ROW = 2 * RT::BYTES + 2 * TT::BYTES;  // LSE, D, seg, spare (256 B each)
+  static constexpr int STAGE = OFF_ROW + 4 * 256;
+  static constexpr int NBUF = 4 * STAGE <= 150 * 1024 ? 4 : 3 * STAGE <= 150 * 1024 ? 3 : 2;
+  static constexpr int LPS = 2 * RT::CPW + 2 * TT::CPW + 1;  // loads per wave per step
+  static_assert(DW % 32 == 0, "whole output tiles per part");
+  static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
+};
+
+template <int DP>
+__global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
+  using G = KvGeom<DP>;
+  using RT = typename G::RT;
+  using TT = typename G::TT;
+  constexpr int NT = DP / 16, NOW = G::NOW, NBUF = G::NBUF, STAGE = G::STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int S = a.S, H = a.H, KV = a.KV;
+  const int g = H / KV, gs = g / a.splits;  // heads of the group per split
+  int b = (int)blockIdx.x;
+  const int kvh = b % KV;
+  b /= KV;
+  const int cpart = b % G::NC;
+  b /= G::NC;
+  const int split = b % a.splits;
+  const int nblk = (S + 31) / 32;
+  const float sc2 = a.scale * ATTN_LOG2E;
+  const uint32_t smem0 = lds_addr(smem);
+  Loader16<32, DP / 8> ldr;
+  ldr.init(DP * 2, wave, lane);
+  Loader16<G::DW, 4> ldt;
+  ldt.init((uint32_t)a.Sp * 2u, wave, lane);
+
+  auto tile = [&](const int kt) __attribute__((always_inline)) {
+    const int j0 = kt * 128;
+    const int key = j0 + 32 * wave + l32;  // < Sp: the copies hold zero rows up to Sp
+    h8 kreg[NT], vreg[NT];
+    const size_t boff = ((size_t)kvh * a.Sp + key) * DP + 8 * hf;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      kreg[t] = *reinterpret_cast<const h8*>(a.Kh + boff + 16 * t);
+      vreg[t] = *reinterpret_cast<const h8*>(a.Vh + boff + 16 * t);
+    }
+    f32x16 accK[NOW], accV[NOW];
+#pragma unroll
+    for (int o = 0; o < NOW; ++o) {
+      accK[o] = zero16();
+      accV[o] = zero16();
+    }
+
+    // visible query blocks: qb >= j0/32 whose smallest document start is at or
+    // before the tile's last key
+    const uint32_t khi = (uint32_t)min(j0 + 127, S - 1);
+    int segb = j0 >> 5;
+    auto seg_mask = [&](int bb) -> uint64_t {
+      const int qb = bb + lane;
+      return __ballot(qb < nblk && a.blk_min[qb] <= khi);
+    };
+    uint64_t mask = segb < nblk ? seg_mask(segb) : 0ull;
+    // smallest visible block after `prev` (-1 when none is left)
+    auto next_block = [&](int prev) -> int {
+      if (prev >= segb) {
+        const int sh = prev - segb + 1;
+        mask = sh >= 64 ? 0ull : (mask >> sh) << sh;
+      }
+      while (mask == 0ull) {
+        segb += 64;
+        if (segb >= nblk) return -1;
+        mask = seg_mask(segb);
+      }
+      return segb + (int)__builtin_ctzll(mask);
+    };
+    // the step after (qb, hh): the next head of the split, then the next block
+    auto next_step = [&](int& qb, int& hh) {
+      if (qb < 0) return;
+      if (++hh == gs) {
+        hh = 0;
+        qb = next_block(qb);
+      }
+    };
+
+    auto issue = [&](int qb, int hh, int buf) {
+      const int head = kvh * g + split * gs + hh;
+      const uint32_t st = smem0 + (uint32_t)(buf * STAGE);
+      const size_t roff = ((size_t)head * a.Sp + (size_t)qb * 32) * DP;
+      ldr.load(buf_rsrc(a.Qh + roff, 32 * DP * 2), st, wave);
+      ldr.load(buf_rsrc(a.dOh + roff, 32 * DP * 2), st + G::OFF_DO, wave);
+      const size_t toff = ((size_t)head * DP + (size_t)cpart * G::DW) * a.Sp + (size_t)qb * 32;
+      const uint32_t tbytes = (uint32_t)(((size_t)(G::DW - 1) * a.Sp + 32) * 2);
+      ldt.load(buf_rsrc(a.QT + toff, tbytes), st + G::OFF_QT, wave);
+      ldt.load(buf_rsrc(a.dOT + toff, tbytes), st + G::OFF_DOT, wave);
+      // LSE, D and seg of the block's rows (lanes 0..31; the rest, and wave 3's
+      // spare load, deposit zeros)
+      const int rows = min(32, S - qb * 32);
+      const bool rok = hf == 0 && l32 < rows;
+      const uint32_t roff4 = rok ? (uint32_t)(l32 * H + head) * 4u : ATTN_BUF_OOB;
+      const uint32_t rbytes = (uint32_t)(rows * H * 4);
+      if (wave == 0) dma4(buf_rsrc(a.LSE + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW);
+      else if (wave == 1) dma4(buf_rsrc(a.D + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW + 256);
+      else if (wave == 2)
+        dma4(buf_rsrc(a.seg ? (const void*)(a.seg + (size_t)qb * 32) : (const void*)a.LSE,
+                      a.seg ? (uint32_t)rows * 4u : 0u),
+             rok ? (uint32_t)l32 * 4u : ATTN_BUF_OOB, st + G::OFF_ROW + 512);
+      else dma4(buf_rsrc(a.LSE, 0u), ATTN_BUF_OOB, st + G::OFF_ROW + 768);
+    };
+
+    auto compute = [&](int qb, int buf) {
+      const int q0 = qb * 32;
+      if (j0 + 32 * wave > q0 + 31) return;  // every key of the block after every query
+      const char* st = smem + buf * STAGE;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        s = mfma16(*reinterpret_cast<const h8*>(st + RT::at(l32, 2 * t + hf)), kreg[t], s);
+        dp = mfma16(*reinterpret_cast<const h8*>(st + G::OFF_DO + RT::at(l32, 2 * t + hf)), vreg[t],
+                    dp);
+      }
+      const float* lse = reinterpret_cast<const float*>(st + G::OFF_ROW);
+      const float* Dv = reinterpret_cast<const float*>(st + G::OFF_ROW + 256);
+      const uint32_t* sg = reinterpret_cast<const uint32_t*>(st + G::OFF_ROW + 512);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qr = crow(r, hf), qq = q0 + qr;
+        const bool vis = qq < S && key <= qq && (uint32_t)key >= sg[qr];
+        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[qr] * ATTN_LOG2E)) : 0.f;
+        s[r] = p;
+        dp[r] = p * (dp[r] - Dv[qr]) * a.scale;
+      }
+      const h8 p0 = pack8(s, 0), p1 = pack8(s, 1), d0 = pack8(dp, 0), d1 = pack8(dp, 1);
+#pragma unroll
+      for (int o = 0; o < NOW; ++o) {
+        const int row = 32 * o + l32;
+        const uint32_t c0 = TT::at(row, hf), c1 = TT::at(row, 2 + hf);
+        accV[o] = mfma16(p0, *reinterpret_cast<const h8*>(st + G::OFF_DOT + c0), accV[o]);
+        accV[o] = mfma16(p1, *reinterpret_cast<const h8*>(st + G::OFF_DOT + c1), accV[o]);
+        accK[o] = mfma16(d0, *reinterpret_cast<const h8*>(st + G::OFF_QT + c0), accK[o]);
+        accK[o] = mfma16(d1, *reinterpret_cast<const h8*>(st + G::OFF_QT + c1), accK[o]);
+      }
+    };
+
+    // the ring: steps i .. i + NBUF - 2 issued ahead of the compute of step i
+    int rq[NBUF], rh[NBUF];  // issued steps, oldest first (rq = -1: none)
+    rq[0] = next_block(-1);
+    rh[0] = 0;
+#pragma unroll
+    for (int k = 1; k < NBUF; ++k) {
+      rq[k] = rq[k - 1];
+      rh[k] = rh[k - 1];
+      next_step(rq[k], rh[k]);
+    }
+    // rq[NBUF - 1] is the first step not yet issued
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (rq[k] >= 0) issue(rq[k], rh[k], k);
+    int buf = 0;
+    while (rq[0] >= 0) {
+      // this wave's loads of step i have landed once at most those of the
+      // later issued steps are outstanding
+      int ahead = 0;
+#pragma unroll
+      for (int k = 1; k < NBUF - 1; ++k) ahead += rq[k] >= 0;
+      if constexpr (NBUF >= 4) {
+        if (ahead >= 2) wait_vm<2 * G::LPS>();
+        else if (ahead == 1) wait_vm<G::LPS>();
+        else wait_vm<0>();
+      } else if constexpr (NBUF == 3) {
+        if (ahead >= 1) wait_vm<G::LPS>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+      // every wave: step i resident and done with step i - 1 (whose buffer the
+      // next issue refills)
+      asm volatile("s_barrier" ::: "memory");
+      if (rq[NBUF - 1] >= 0) issue(rq[NBUF - 1], rh[NBUF - 1], (buf + NBUF - 1) % NBUF);
+      compute(rq[0], buf);
+      // shift the ring
+      int nq = rq[NBUF - 1], nh = rh[NBUF - 1];
+      next_step(nq, nh);
+#pragma unroll
+      for (int k = 0; k < NBUF - 1; ++k) {
+        rq[k] = rq[k + 1];
+        rh[k] = rh[k + 1];
+      }
+      rq[NBUF - 1] = nq;
+      rh[NBUF - 1] = nh;
+      buf = (buf + 1) % NBUF;
+    }
+    __syncthreads();  // every wave done with the ring before it is reused
+
+    // rows key j0 + 32w + crow(r, hf), the part's columns: += into dK, dV (one
+    // split), or this split's partial sums into part (several)
+    const size_t kstride = (size_t)KV * a.d;
+    const size_t slice = (size_t)S * kstride;
+    float* outK = a.splits == 1 ? a.dK : a.part + (size_t)(2 * split) * slice;
+    float* outV = a.splits == 1 ? a.dV : a.part + (size_t)(2 * split + 1) * slice;
+    outK += (size_t)kvh * a.d;
+    outV += (size_t)kvh * a.d;
+#pragma unroll
+    for (int o = 0; o < NOW; ++o) {
+      const int col = cpart * G::DW + 32 * o + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = j0 + 32 * wave + crow(r, hf);
+        if (row < S && col < a.d) {
+          const size_t off = (size_t)row * kstride + col;
+          if (a.splits == 1) {
+            outK[off] += accK[o][r];
+            outV[off] += accV[o][r];
+          } else {
+            outK[off] = accK[o][r];
+            outV[off] = accV[o][r];
+          }
+        }
+      }
+    }
+  };
+  // low key tiles (most queries) first; paired: then the mirror tile
+  const int first = (int)(blockIdx.x / (KV * G::NC * a.splits));
+  const int second = mirror_tile(first, (S + 127) / 128, a.pair);
+  tile(first);
+  if (second >= 0) tile(second);
+}
+
+// k_sumparts: dK += sum over splits of part[2 split], dV += sum of
+// part[2 split + 1], split by split in order; n = S * KV * d floats per slice
+// (a multiple of 4: d is a multiple of 16).
+__global__ __launch_bounds__(256) void k_sumparts(const float* __restrict__ part, int splits,
+                                                  long long n, float* dK, float* dV) {
+  const long long n4 = n / 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    float4 k = reinterpret_cast<float4*>(dK)[i], v = reinterpret_cast<float4*>(dV)[i];
+    for (int s = 0; s < splits; ++s) {
+      const float4 pk = reinterpret_cast<const float4*>(part + (size_t)(2 * s) * n)[i];
+      const float4 pv = reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * n)[i];
+      k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
+      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+    }
+    reinterpret_cast<float4*>(dK)[i] = k;
+    reinterpret_cast<float4*>(dV)[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+template <int DP>
+static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float* O, const float* dO,
+                                hipStream_t st) {
+  auto blocks = [&](int ntiles) { return f.pair ? (ntiles + 1) / 2 : ntiles; };
+  const int nb = f.Sp / 32;
+  const long long ncvt = 2ll * nb * f.H + 2ll * nb * f.KV;
+  attn_status_t rc = profile_mark(st, true);
+  if (rc != ATTN_OK) return rc;
+  hipLaunchKernelGGL(k_cvt16<DP>, dim3((unsigned)ncvt), dim3(256), 0, st, c);
+  rc = hip_check(hipGetLastError(), "launching k_cvt16");
+  if (rc != ATTN_OK) return rc;
+  const int nqt = blocks((f.S + 127) / 128);
+  if (O) {
+    rc = launch_rowdot(O, dO, f.D, (long long)f.S * f.H, f.d, st);
+  } else {
+    hipLaunchKernelGGL((k_q16<DP, true>), dim3(nqt * f.H), dim3(256), 0, st, f);
+    rc = hip_check(hipGetLastError(), "launching k_q16 (row term)");
+  }
+  if (rc == ATTN_OK) rc = profile_mark(st);
+  if (rc != ATTN_OK) return rc;
+  hipLaunchKernelGGL(k_kv16<DP>, dim3(blocks((f.S + 127) / 128) * f.KV * KvGeom<DP>::NC * f.splits),
+                     dim3(256), 0, st, f);
+  rc = hip_check(hipGetLastError(), "launching k_kv16");
+  if (rc == ATTN_OK && f.splits > 1) {
+    const long long n = (long long)f.S * f.KV * f.d;
+    const int nb4 = (int)std::min<long long>((n / 4 + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_sumparts, dim3(nb4), dim3(256), 0, st, f.part, f.splits, n, f.dK, f.dV);
+    rc = hip_check(hipGetLastError(), "launching k_sumparts");
+  }
+  if (rc == ATTN_OK) rc = profile_mark(st);
+  if (rc != ATTN_OK) return rc;
+  hipLaunchKernelGGL((k_q16<DP, false>), dim3(nqt * f.H * QGeom<DP, false>::NC), dim3(256), 0, st, f);
+  rc = hip_check(hipGetLastError(), "launching k_q16");
+  if (rc == ATTN_OK) rc = profile_mark(st);
+  return rc;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
+                                      const float* dO, const float* LSE, const uint32_t* seg,
+                                      float* dQ, float* dK, float* dV, int seq_len, int n_heads,
+                                      int n_kv_heads, int head_dim, float scale, void* stream) {
+  clear_error();
+  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, scale);
+  if (rc != ATTN_OK) return rc;
+  const void* ptrs[] = {Q, K, V, O, dO, LSE, seg, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return fail(ATTN_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
+  if (seq_len == 0) return ATTN_OK;
+  const int dp = padded_dim(head_dim);
+  const long long Sp = ((long long)seq_len + 127) / 128 * 128;
+  // byte offsets inside one d-major tile must fit the 32-bit buffer offsets
+  if ((long long)dp * Sp * 2 >= (1ll << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "seq_len = %d is too long for head_dim = %d", seq_len, head_dim);
+
+  const long long nblk = ((long long)seq_len + 31) / 32;
+  const size_t qbytes = (size_t)n_heads * Sp * dp * 2, kbytes = (size_t)n_kv_heads * Sp * dp * 2;
+  size_t off = 0;
+  const size_t off_D = off; off += align256((size_t)seq_len * n_heads * 4);
+  const size_t off_min = off; off += align256((size_t)nblk * 4);
+  const size_t off_max = off; off += align256((size_t)nblk * 4);
+  const size_t off_slot = off; off += align256((size_t)(nblk + 1) * 8);
+  size_t off_x[7];  // Qh, dOh, QT, dOT, Kh, Vh, KT
+  for (int i = 0; i < 7; ++i) {
+    off_x[i] = off;
+    off += align256(i < 4 ? qbytes : kbytes);
+  }
+  // k_kv16 splits a group's heads over workgroups until the grid has ~1024 of
+  // them (or the group cannot be split further); several splits add their
+  // partial dK, dV through a workspace slice each
+  const bool pair = seg == nullptr && pairing_enabled();
+  const int g = n_heads / n_kv_heads;
+  const int nkt = (seq_len + 127) / 128;
+  const long long kv_blocks = (long long)(pair ? (nkt + 1) / 2 : nkt) * n_kv_heads;
+  int splits = 1;
+  while (kv_blocks * splits < 1024 && g % (2 * splits) == 0) splits *= 2;
+  const size_t off_part = off;
+  if (splits > 1) off += align256((size_t)2 * splits * seq_len * n_kv_heads * head_dim * 4);
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipMemPool_t pool;
+  rc = device_pool(&pool);
+  if (rc != ATTN_OK) return rc;
+  void* ws = nullptr;
+  rc = hip_check(hipMallocFromPoolAsync(&ws, off, pool, st), "hipMallocFromPoolAsync(workspace)");
+  if (rc != ATTN_OK) return rc;
+  char* w = static_cast<char*>(ws);
+  auto half_at = [&](int i) { return reinterpret_cast<_Float16*>(w + off_x[i]); };
+
+  F16Args f;
+  f.Qh = half_at(0); f.dOh = half_at(1); f.QT = half_at(2); f.dOT = half_at(3);
+  f.Kh = half_at(4); f.Vh = half_at(5); f.KT = half_at(6);
+  f.LSE = LSE; f.seg = seg; f.dQ = dQ; f.dK = dK; f.dV = dV;
+  f.D = reinterpret_cast<float*>(w + off_D);
+  f.blk_min = reinterpret_cast<const uint32_t*>(w + off_min);
+  f.S = seq_len; f.Sp = (int)Sp; f.H = n_heads; f.KV = n_kv_heads; f.d = head_dim; f.scale = scale;
+  f.pair = pair;
+  f.splits = splits;
+  f.part = splits > 1 ? reinterpret_cast<float*>(w + off_part) : nullptr;
+  CvtArgs c;
+  c.Q = Q; c.dO = dO; c.K = K; c.V = V;
+  c.Qh = half_at(0); c.dOh = half_at(1); c.QT = half_at(2); c.dOT = half_at(3);
+  c.Kh = half_at(4); c.Vh = half_at(5); c.KT = half_at(6);
+  c.S = seq_len; c.Sp = (int)Sp; c.H = n_heads; c.KV = n_kv_heads; c.d = head_dim;
+
+  rc = launch_prep(seg, seq_len, reinterpret_cast<uint32_t*>(w + off_min),
+                   reinterpret_cast<uint32_t*>(w + off_max), reinterpret_cast<long long*>(w + off_slot), st);
+  if (rc == ATTN_OK) {
+    switch (dp) {
+      case 32: rc = launch_f16<32>(f, c, O, dO, st); break;
+      case 64: rc = launch_f16<64>(f, c, O, dO, st); break;
+      case 96: rc = launch_f16<96>(f, c, O, dO, st); break;
+      case 128: rc = launch_f16<128>(f, c, O, dO, st); break;
+      case 192: rc = launch_f16<192>(f, c, O, dO, st); break;
+      default: rc = launch_f16<256>(f, c, O, dO, st); break;
+    }
+  }
+  attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");
+  return rc != ATTN_OK ? rc : rc2;
+}

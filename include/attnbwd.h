@@ -139,6 +139,38 @@ attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, cons
                             float rope_base, int pos_offset, void* stream);
 
 /*
+ * attn_bwd_f16 -- the same gradients with 16-bit matrix-core operands.
+ * Every operand of the page's products (Q, K, V, dO, and the probability and
+ * score-gradient tiles P and scale*dS of kernel attention_backward) is rounded
+ * to IEEE fp16 (round to nearest even) and every sum is accumulated in fp32;
+ * inputs, outputs, LSE, the row term and the masks stay fp32.  The pages
+ * compute in fp32 throughout: this is a reduced-precision variant of their
+ * sums (it runs the products at the fp16 matrix rate), meant for activations
+ * of ordinary magnitude -- inputs beyond the fp16 range (|x| > 65504)
+ * overflow to infinity.  Measured against the fp64 definition it stays
+ * within 1e-3 of the largest gradient on the workloads the tests cover.
+ *
+ * O is the forward output, as for attn_bwd_o, or NULL: the row term is then
+ * computed by an extra pass over the scores.  Arguments, layouts, +=
+ * semantics and errors as attn_bwd, plus ATTN_ERR_UNSUPPORTED when
+ * Sp * DP * 2 >= 2^31, with Sp = seq_len rounded up to 128 and DP = head_dim
+ * rounded up to 32, 64, 96, 128, 192 or 256.  Workspace (same private pool):
+ * fp16 copies of Q, dO and K in two layouts each and of V,
+ * (4 * n_heads + 3 * n_kv_heads) * Sp * DP * 2 bytes; the row term and block
+ * metadata; and, when the key-major pass splits each KV group's heads over
+ * `splits` workgroups (a power of two dividing n_heads / n_kv_heads, chosen
+ * to give about 1024 workgroups), 2 * splits * seq_len * n_kv_heads *
+ * head_dim * 4 bytes of partial dK, dV sums, added in split order (the result
+ * does not depend on the schedule).  0.29 GiB at seq_len 4096, 32 heads,
+ * 8 KV heads, head_dim 128 (4 splits).
+ */
+attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
+                           const float* dO, const float* LSE, const uint32_t* seg,
+                           float* dQ, float* dK, float* dV,
+                           int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                           void* stream);
+
+/*
  * attn_bwd_plan -- host-side query (no GPU work): the workspace bytes one
  * attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes, and whether its key-major pass reads
  * stored probability tiles (1) or recomputes them (0).  Either output pointer
@@ -167,7 +199,9 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
  * attn_profile_begin: from now on, on the calling thread, every attn_bwd call
  *   records HIP events on its stream before, between and after its passes:
  *   the query-major pass (row term D, and dQ or the stored tiles), the
- *   key-major pass (dK, dV), and -- with stored tiles -- the dQ pass.
+ *   key-major pass (dK, dV), and -- with stored tiles -- the dQ pass.  An
+ *   attn_bwd_f16 call records its three: the fp16 copies and the row term,
+ *   the key-major pass, the dQ pass.
  * attn_profile_end: waits for those events, writes into ms[0], ms[1], ms[2]
  *   the summed device time in milliseconds of each of the three passes over
  *   the recorded calls (ms[2] = 0 for calls without the dQ pass), into
