@@ -419,11 +419,17 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       kreg[t] = *reinterpret_cast<const h8*>(a.Kh + boff + 16 * t);
       vreg[t] = *reinterpret_cast<const h8*>(a.Vh + boff + 16 * t);
     }
+    // land them now, where the compiler sees it: otherwise it waits for them
+    // inside the step loop, on a counter that also counts the ring's loads
+    wait_vm<0>();
+    // the accumulators live in AGPRs for the whole tile (the matrix cores read
+    // and write them there; pinned so that no step copies them to VGPRs)
     f32x16 accK[NOW], accV[NOW];
 #pragma unroll
     for (int o = 0; o < NOW; ++o) {
       accK[o] = zero16();
       accV[o] = zero16();
+      asm volatile("" : "+a"(accK[o]), "+a"(accV[o]));
     }
 
     // visible query blocks: qb >= j0/32 whose smallest document start is at or
@@ -493,16 +499,28 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         dp = mfma16(*reinterpret_cast<const h8*>(st + G::OFF_DO + RT::at(l32, 2 * t + hf)), vreg[t],
                     dp);
       }
-      const float* lse = reinterpret_cast<const float*>(st + G::OFF_ROW);
-      const float* Dv = reinterpret_cast<const float*>(st + G::OFF_ROW + 256);
-      const uint32_t* sg = reinterpret_cast<const uint32_t*>(st + G::OFF_ROW + 512);
+      // LSE, D and seg of this lane's rows crow(r, hf): rows 8(r/4) + 4hf + r%4,
+      // four 16-byte reads each
+      float lse[16], dv[16];
+      uint32_t sg[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int row0 = 8 * a4 + 4 * hf;
+        const float4 l4 = *reinterpret_cast<const float4*>(st + G::OFF_ROW + 4 * row0);
+        const float4 d4 = *reinterpret_cast<const float4*>(st + G::OFF_ROW + 256 + 4 * row0);
+        const uint4 s4 = *reinterpret_cast<const uint4*>(st + G::OFF_ROW + 512 + 4 * row0);
+        lse[4 * a4] = l4.x; lse[4 * a4 + 1] = l4.y; lse[4 * a4 + 2] = l4.z; lse[4 * a4 + 3] = l4.w;
+        dv[4 * a4] = d4.x; dv[4 * a4 + 1] = d4.y; dv[4 * a4 + 2] = d4.z; dv[4 * a4 + 3] = d4.w;
+        sg[4 * a4] = s4.x; sg[4 * a4 + 1] = s4.y; sg[4 * a4 + 2] = s4.z; sg[4 * a4 + 3] = s4.w;
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qr = crow(r, hf), qq = q0 + qr;
-        const bool vis = qq < S && key <= qq && (uint32_t)key >= sg[qr];
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[qr] * ATTN_LOG2E)) : 0.f;
+        const int qq = q0 + crow(r, hf);
+        const bool vis = (qq < S) & (key <= qq) & ((uint32_t)key >= sg[r]);
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r] * ATTN_LOG2E));
+        const float p = vis ? e : 0.f;
         s[r] = p;
-        dp[r] = p * (dp[r] - Dv[qr]) * a.scale;
+        dp[r] = p * (dp[r] - dv[r]) * a.scale;
       }
       const h8 p0 = pack8(s, 0), p1 = pack8(s, 1), d0 = pack8(dp, 0), d1 = pack8(dp, 1);
 #pragma unroll
@@ -513,6 +531,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         accV[o] = mfma16(p1, *reinterpret_cast<const h8*>(st + G::OFF_DOT + c1), accV[o]);
         accK[o] = mfma16(d0, *reinterpret_cast<const h8*>(st + G::OFF_QT + c0), accK[o]);
         accK[o] = mfma16(d1, *reinterpret_cast<const h8*>(st + G::OFF_QT + c1), accK[o]);
+        asm volatile("" : "+a"(accK[o]), "+a"(accV[o]));
       }
     };
 
