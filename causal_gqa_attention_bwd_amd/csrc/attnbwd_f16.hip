@@ -195,30 +195,34 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
 // k_q16: query-major, one workgroup per (128-query tile, head).  Wave w owns
 // queries i0 + 32w + l%32 and keeps their Q and dO rows in registers as the B
 // operands of S^T = K Q^T and dP^T = V dO^T; 32-key blocks of K, V (row
-// tiles) and K^T stream through LDS, double-buffered.  The score tiles hold
-// key crow(r, hf) of query l%32, so each lane's LSE, D and seg are one value.
+// tiles) and K^T stream through an LDS ring of NBUF stages (NBUF - 1 blocks
+// in flight), shared by the four waves.  The score tiles hold key crow(r, hf)
+// of query l%32, so each lane's LSE, D and seg are one value.
 //   DONLY: D[q] = sum_j P dP (the row term, for the key-major pass).
 //   else:  dQ += dS K with dS = scale P (dP - D), A operand straight from the
-//          dS registers, B from the K^T tile.  Above 128 columns the dQ
-//          columns come in two parts, one workgroup each (both form S and dP),
-//          so that a wave's accumulators fit the register file.
+//          dS registers, B from the K^T tile; the accumulators stay in AGPRs.
 // ---------------------------------------------------------------------------
 template <int DP, bool DONLY>
 struct QGeom {
-  static constexpr int NC = (DP > 128 && !DONLY) ? 2 : 1;  // dQ column parts
-  static constexpr int DW = DP / NC;
+  using RT = Tile16<32, DP / 8>;
+  using TT = Tile16<DP, 4>;
+  static constexpr int STAGE = 2 * RT::BYTES + (DONLY ? 0 : TT::BYTES);
+  // two workgroups per CU up to 128 columns, one above
+  static constexpr int BUDGET = DP <= 128 ? 72 * 1024 : 150 * 1024;
+  static constexpr int NBUF = 4 * STAGE <= BUDGET ? 4 : 3 * STAGE <= BUDGET ? 3 : 2;
+  static constexpr int LPS = 2 * RT::CPW + (DONLY ? 0 : TT::CPW);  // loads per wave per block
+  static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
 
 template <int DP, bool DONLY>
 __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
-  constexpr int CH = DP / 8;   // 16-byte chunks per row
+  using G = QGeom<DP, DONLY>;
+  using RT = typename G::RT;
+  using TT = typename G::TT;
   constexpr int NT = DP / 16;  // k-steps of the d-contractions
-  constexpr int NC = QGeom<DP, DONLY>::NC, DW = QGeom<DP, DONLY>::DW;
-  constexpr int NO = DW / 32;  // 32-column output tiles of the part
-  using RT = Tile16<32, CH>;
-  using TT = Tile16<DW, 4>;
-  constexpr int STAGE = 2 * RT::BYTES + (DONLY ? 0 : TT::BYTES);
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  constexpr int NO = DP / 32;  // 32-column output tiles
+  constexpr int NBUF = G::NBUF, STAGE = G::STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
   __shared__ uint32_t sMin[4];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -229,11 +233,10 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
   const int qt_hi = (S - 1) / 128;
   const float sc2 = a.scale * ATTN_LOG2E;
   const uint32_t smem0 = lds_addr(smem);
-  Loader16<32, CH> ldr;
+  Loader16<32, DP / 8> ldr;
   ldr.init(DP * 2, wave, lane);
-  Loader16<DW, 4> ldt;
+  Loader16<DP, 4> ldt;
   if constexpr (!DONLY) ldt.init((uint32_t)a.Sp * 2u, wave, lane);
-  const int cpart = (int)(blockIdx.x / H) % NC;
 
   auto tile = [&](const int qt) __attribute__((always_inline)) {
     const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
@@ -258,10 +261,14 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
     const int qb = (i0 >> 5) + wave;
     const uint32_t lo = qb < nblk ? a.blk_min[qb] : 0xffffffffu;
     if (lane == 0) sMin[wave] = lo;
+    // the register loads above land here, where the compiler sees it (not
+    // inside the block loop, on a counter that also counts the ring's loads)
+    wait_vm<0>();
     __syncthreads();
     const uint32_t lo_all = min(min(sMin[0], sMin[1]), min(sMin[2], sMin[3]));
     const int kb_last = min(i0 + 127, S - 1) / 32;
     const int kb_first = (int)min(lo_all / 32u, (uint32_t)kb_last + 1u);
+    const int n = kb_last - kb_first + 1;  // blocks of the tile (0: none)
     // this wave's key blocks (a wave past S has lo = ~0 and sees none)
     const int w_lo = (int)min(lo / 32u, 0x7fffffffu);
     const int w_hi = min(i0 + 32 * wave + 31, S - 1) / 32;
@@ -272,54 +279,77 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
       ldr.load(buf_rsrc(a.Kh + roff, 32 * DP * 2), st, wave);
       ldr.load(buf_rsrc(a.Vh + roff, 32 * DP * 2), st + RT::BYTES, wave);
       if constexpr (!DONLY)
-        ldt.load(buf_rsrc(a.KT + ((size_t)kvh * DP + (size_t)cpart * DW) * a.Sp + (size_t)kb * 32,
-                          (uint32_t)(((size_t)(DW - 1) * a.Sp + 32) * 2)),
+        ldt.load(buf_rsrc(a.KT + (size_t)kvh * DP * a.Sp + (size_t)kb * 32,
+                          (uint32_t)(((size_t)(DP - 1) * a.Sp + 32) * 2)),
                  st + 2 * RT::BYTES, wave);
     };
 
     f32x16 acc[NO];
 #pragma unroll
-    for (int o = 0; o < NO; ++o) acc[o] = zero16();
-    float Dacc = 0.f;
-    if (kb_first <= kb_last) {
-      issue(kb_first, 0);
-      tile_barrier();
-      for (int kb = kb_first; kb <= kb_last; ++kb) {
-        const int buf = (kb - kb_first) & 1;
-        if (kb < kb_last) issue(kb + 1, buf ^ 1);
-        if (kb >= w_lo && kb <= w_hi) {
-          const char* st = smem + buf * STAGE;
-          f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const h8 ka = *reinterpret_cast<const h8*>(st + RT::at(l32, 2 * t + hf));
-            const h8 va = *reinterpret_cast<const h8*>(st + RT::BYTES + RT::at(l32, 2 * t + hf));
-            s = mfma16(ka, qreg[t], s);
-            dp = mfma16(va, oreg[t], dp);
-          }
-          f32x16 ds;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kb * 32 + crow(r, hf);
-            const bool vis = key <= q && (uint32_t)key >= sq;
-            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2)) : 0.f;
-            if constexpr (DONLY) Dacc = fmaf(p, dp[r], Dacc);
-            else ds[r] = p * (dp[r] - Dq) * a.scale;
-          }
-          if constexpr (!DONLY) {
-            const h8 a0 = pack8(ds, 0), a1 = pack8(ds, 1);
-            const char* kt = st + 2 * RT::BYTES;
-#pragma unroll
-            for (int o = 0; o < NO; ++o) {
-              const int row = 32 * o + l32;
-              acc[o] = mfma16(a0, *reinterpret_cast<const h8*>(kt + TT::at(row, hf)), acc[o]);
-              acc[o] = mfma16(a1, *reinterpret_cast<const h8*>(kt + TT::at(row, 2 + hf)), acc[o]);
-            }
-          }
-        }
-        tile_barrier();  // next block resident; everyone done with this one
-      }
+    for (int o = 0; o < NO; ++o) {
+      acc[o] = zero16();
+      if constexpr (!DONLY) asm volatile("" : "+a"(acc[o]));
     }
+    float Dacc = 0.f;
+
+    auto compute = [&](int kb, int buf) {
+      if (kb < w_lo || kb > w_hi) return;
+      const char* st = smem + buf * STAGE;
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const h8 ka = *reinterpret_cast<const h8*>(st + RT::at(l32, 2 * t + hf));
+        const h8 va = *reinterpret_cast<const h8*>(st + RT::BYTES + RT::at(l32, 2 * t + hf));
+        s = mfma16(ka, qreg[t], s);
+        dp = mfma16(va, oreg[t], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb * 32 + crow(r, hf);
+        const bool vis = (key <= q) & ((uint32_t)key >= sq);
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
+        const float p = vis ? e : 0.f;
+        if constexpr (DONLY) Dacc = fmaf(p, dp[r], Dacc);
+        else s[r] = p * (dp[r] - Dq) * a.scale;
+      }
+      if constexpr (!DONLY) {
+        const h8 a0 = pack8(s, 0), a1 = pack8(s, 1);
+        const char* kt = st + 2 * RT::BYTES;
+#pragma unroll
+        for (int o = 0; o < NO; ++o) {
+          const int row = 32 * o + l32;
+          acc[o] = mfma16(a0, *reinterpret_cast<const h8*>(kt + TT::at(row, hf)), acc[o]);
+          acc[o] = mfma16(a1, *reinterpret_cast<const h8*>(kt + TT::at(row, 2 + hf)), acc[o]);
+          asm volatile("" : "+a"(acc[o]));
+        }
+      }
+    };
+
+    // the ring: blocks i .. i + NBUF - 2 issued ahead of the compute of block i
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < n) issue(kb_first + k, k);
+    for (int i = 0; i < n; ++i) {
+      // this wave's loads of block i have landed once at most those of the
+      // later issued blocks are outstanding
+      const int ahead = min(NBUF - 2, n - 1 - i);
+      if constexpr (NBUF >= 4) {
+        if (ahead >= 2) wait_vm<2 * G::LPS>();
+        else if (ahead == 1) wait_vm<G::LPS>();
+        else wait_vm<0>();
+      } else if constexpr (NBUF == 3) {
+        if (ahead >= 1) wait_vm<G::LPS>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+      // every wave: block i resident and done with block i - 1 (whose buffer
+      // the next issue refills)
+      asm volatile("s_barrier" ::: "memory");
+      if (i + NBUF - 1 < n) issue(kb_first + i + NBUF - 1, (i + NBUF - 1) % NBUF);
+      compute(kb_first + i, i % NBUF);
+    }
+
     if constexpr (DONLY) {
       const float Dt = Dacc + __shfl_xor(Dacc, 32);  // the half-waves saw disjoint keys
       if (q_ok && hf == 0) a.D[(size_t)q * H + h] = Dt;
@@ -328,7 +358,7 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
       const size_t qstride = (size_t)H * a.d;
 #pragma unroll
       for (int o = 0; o < NO; ++o) {
-        const int col = cpart * DW + 32 * o + l32;
+        const int col = 32 * o + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i0 + 32 * wave + crow(r, hf);
@@ -338,11 +368,11 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
     }
   };
   // longest rows first; paired: then the mirror tile
-  const int first = qt_hi - (int)(blockIdx.x / (H * NC));
+  const int first = qt_hi - (int)(blockIdx.x / H);
   const int second = mirror_tile(first, qt_hi + 1, a.pair);
   tile(first);
   if (second >= 0) {
-    __syncthreads();  // the first tile is done with the LDS
+    __syncthreads();  // every wave done with the ring and sMin of the first tile
     tile(second);
   }
 }
@@ -673,7 +703,7 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
-  hipLaunchKernelGGL((k_q16<DP, false>), dim3(nqt * f.H * QGeom<DP, false>::NC), dim3(256), 0, st, f);
+  hipLaunchKernelGGL((k_q16<DP, false>), dim3(nqt * f.H), dim3(256), 0, st, f);
   rc = hip_check(hipGetLastError(), "launching k_q16");
   if (rc == ATTN_OK) rc = profile_mark(st);
   return rc;
