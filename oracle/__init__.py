@@ -60,6 +60,9 @@ def _load():
                                            ctypes.c_float, I]
     lib.oracle_attn_fwd_rows.argtypes = [P, P, P, P, P, I, P, P, I, I, I, I, ctypes.c_float, I]
     lib.oracle_rope_f64.argtypes = [P, I, I, I, ctypes.c_double, ctypes.c_long, I]
+    lib.oracle_attn_bwd_decode_f64.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I,
+                                               ctypes.c_double]
+    lib.oracle_attn_bwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_float]
     lib.oracle_attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, ctypes.c_float,
                                          ctypes.c_double, ctypes.c_long, I]
     for f in (lib.oracle_attn_fwd_f64, lib.oracle_attn_bwd_f64, lib.oracle_attn_bwd_o_f64,
@@ -209,6 +212,44 @@ def attn_bwd(Q, K, V, dO, LSE, seg, scale, dQ=None, dK=None, dV=None, nthreads=0
                                      _ptr(seg), _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
                                      np.float32(scale), nthreads), "attn_bwd")
     return dQ, dK, dV
+
+
+def _decode_dims(q, K, P):
+    H, d = q.shape
+    T, KV, d2 = K.shape
+    assert d == d2 and P.shape == (H, T), "q [H,d], K [T,KV,d], P [H,T] disagree"
+    return T, H, KV, d
+
+
+def attn_bwd_decode_f64(q, K, V, P, dO, scale, debug=False):
+    """Single-query backward over a KV history (page "rullama 0.5.0", pass 1
+    and 2 of 2), fp64, no accumulation: q, dO [H,d]; K, V [T,KV,d]; P the
+    forward's probabilities [H,T].  Returns (dq, dK, dV), plus the score
+    gradients dS [H,T] when ``debug``."""
+    q, K, V, P, dO = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, K, V, P, dO))
+    T, H, KV, d = _decode_dims(q, K, P)
+    dq = np.zeros((H, d), np.float64)
+    dK = np.zeros((T, KV, d), np.float64)
+    dV = np.zeros((T, KV, d), np.float64)
+    dS = np.zeros((H, T), np.float64)
+    _check(_load().oracle_attn_bwd_decode_f64(_ptr(q), _ptr(K), _ptr(V), _ptr(P), _ptr(dO),
+                                              _ptr(dq), _ptr(dK), _ptr(dV), _ptr(dS), T, H, KV,
+                                              d, float(scale)), "attn_bwd_decode_f64")
+    return (dq, dK, dV, dS) if debug else (dq, dK, dV)
+
+
+def attn_bwd_decode(q, K, V, P, dO, scale, dq=None, dK=None, dV=None):
+    """fp32 single-query backward with "+=" semantics (zeros when not given);
+    returns the (updated) float32 arrays (dq, dK, dV)."""
+    q, K, V, P, dO = (np.ascontiguousarray(x, dtype=np.float32) for x in (q, K, V, P, dO))
+    T, H, KV, d = _decode_dims(q, K, P)
+    dq = np.zeros((H, d), np.float32) if dq is None else np.array(dq, np.float32, order="C")
+    dK = np.zeros((T, KV, d), np.float32) if dK is None else np.array(dK, np.float32, order="C")
+    dV = np.zeros((T, KV, d), np.float32) if dV is None else np.array(dV, np.float32, order="C")
+    _check(_load().oracle_attn_bwd_decode(_ptr(q), _ptr(K), _ptr(V), _ptr(P), _ptr(dO), _ptr(dq),
+                                          _ptr(dK), _ptr(dV), T, H, KV, d, np.float32(scale)),
+           "attn_bwd_decode")
+    return dq, dK, dV
 
 
 def attn_bwd_rows(Q, K, V, dO, LSE, seg, scale, q_rows, k_rows, nthreads=0, O=None):

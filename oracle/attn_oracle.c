@@ -46,12 +46,19 @@
  * The _o entry points take the forward output O and read the row term off it
  * (D = dO . O, see bwd_row); the others compute D = sum_j P * dP.
  *
+ * The _decode entry points are the single-query backward over a KV history
+ * with stored probabilities (page "rullama 0.5.0", pass 1 and pass 2 of 2);
+ * see oracle_attn_bwd_decode_f64.
+ *
  * Parity status: every function here is pinned by the CPU tests (finite
  * differences, sum_j dS = 0, masked-key zeros, plain-causal equality with an
  * independent dense implementation, packed == per-document, GQA == replicated
  * MHA, closed forms, linearity / "+="; for the _o entry points: agreement with
  * D = sum_j P * dP at the exact forward output, and the closed-form effect of
- * a perturbed O on each gradient).
+ * a perturbed O on each gradient; for the _decode entry points: finite
+ * differences through the decode forward, equality with the backward above
+ * for the last row of a causal problem, the T = 1 closed form, the history
+ * sums of dK and dV).
  */
 #include <math.h>
 #include <pthread.h>
@@ -552,4 +559,99 @@ int oracle_attn_bwd_rows(const float *Q, const float *K, const float *V, const f
                          int nthreads) {
   return oracle_attn_bwd_rows_o(Q, K, V, NULL, dO, LSE, seg, q_rows, nq, k_rows, nk, dQ_sel,
                                 dK_sel, dV_sel, S, H, KV, d, scale, nthreads);
+}
+
+/* ------------------------------------------------------------------ */
+/* single-query backward over a KV history (one decode step)            */
+/* ------------------------------------------------------------------ */
+/* Page "rullama 0.5.0 -- src/backend/dispatch/training.rs",
+ * attention_backward_dq_chained and attention_backward_dkv_chained (pass 1
+ * and pass 2 of 2): one query per head attends to every one of the T keys of
+ * a KV history, and the forward's probabilities P[h][j] are given (the stored
+ * "probs"; nothing is recomputed).  Layouts: q, dO, dq [H, d]; P and the
+ * staged score gradients [H, T]; K, V, dK, dV [T, KV, d].  Per head h, with
+ * kv_h = h / (H/KV):
+ *   dP[j] = dO_h . v_j
+ *   D     = sum_j P[h][j] * dP[j]
+ *   dS[j] = P[h][j] * (dP[j] - D)             (pass 1's staged d_scores)
+ *   dq_h += scale * sum_j dS[j] * k_j          (pass 1)
+ *   dK_j += scale * sum_{h in group} dS[j] * q_h   (pass 2, key-major)
+ *   dV_j += sum_{h in group} P[h][j] * dO_h        (pass 2)
+ * Plain loops in a fixed order, fp64.  The _f64 entry writes the gradients
+ * (no accumulation) and optionally dS; the float entry adds into its outputs
+ * and rounds once: out = (float)((double)init + gradient). */
+int oracle_attn_bwd_decode_f64(const double *q, const double *K, const double *V,
+                               const double *P, const double *dO, double *dq, double *dK,
+                               double *dV, double *dS_out, int T, int H, int KV, int d,
+                               double scale) {
+  if (T < 0 || H < 1 || KV < 1 || d < 1 || H % KV != 0) return 1;
+  const int g = H / KV;
+  double *ds = (double *)malloc(sizeof(double) * ((size_t)H * T + 1));
+  if (!ds) return 2;
+  memset(dq, 0, sizeof(double) * (size_t)H * d);
+  memset(dK, 0, sizeof(double) * (size_t)T * KV * d);
+  memset(dV, 0, sizeof(double) * (size_t)T * KV * d);
+  /* pass 1: score gradients and dq, head by head */
+  for (int h = 0; h < H; ++h) {
+    const int kvh = h / g;
+    const double *doh = dO + (size_t)h * d;
+    double D = 0.0;
+    for (long j = 0; j < T; ++j) {
+      const double dp = dot(doh, V + ((size_t)j * KV + kvh) * d, d);
+      ds[(size_t)h * T + j] = dp; /* dP for now */
+      D += P[(size_t)h * T + j] * dp;
+    }
+    for (long j = 0; j < T; ++j) {
+      const size_t k = (size_t)h * T + j;
+      ds[k] = P[k] * (ds[k] - D);
+    }
+    for (long j = 0; j < T; ++j) {
+      const double *kj = K + ((size_t)j * KV + kvh) * d;
+      const double w = scale * ds[(size_t)h * T + j];
+      for (int c = 0; c < d; ++c) dq[(size_t)h * d + c] += w * kj[c];
+    }
+  }
+  /* pass 2: key-major dK and dV, the group's heads in order */
+  for (long j = 0; j < T; ++j)
+    for (int kvh = 0; kvh < KV; ++kvh) {
+      double *dk = dK + ((size_t)j * KV + kvh) * d;
+      double *dv = dV + ((size_t)j * KV + kvh) * d;
+      for (int hh = 0; hh < g; ++hh) {
+        const int h = kvh * g + hh;
+        const double wk = scale * ds[(size_t)h * T + j], wv = P[(size_t)h * T + j];
+        for (int c = 0; c < d; ++c) {
+          dk[c] += wk * q[(size_t)h * d + c];
+          dv[c] += wv * dO[(size_t)h * d + c];
+        }
+      }
+    }
+  if (dS_out) memcpy(dS_out, ds, sizeof(double) * (size_t)H * T);
+  free(ds);
+  return 0;
+}
+
+int oracle_attn_bwd_decode(const float *q, const float *K, const float *V, const float *P,
+                           const float *dO, float *dq, float *dK, float *dV, int T, int H, int KV,
+                           int d, float scale) {
+  if (T < 0 || H < 1 || KV < 1 || d < 1 || H % KV != 0) return 1;
+  const size_t nq = (size_t)H * d, nk = (size_t)T * KV * d, np_ = (size_t)H * T;
+  double *q64 = widen(q, nq), *K64 = widen(K, nk), *V64 = widen(V, nk), *P64 = widen(P, np_);
+  double *dO64 = widen(dO, nq);
+  double *gq = (double *)malloc(sizeof(double) * (nq + 1));
+  double *gk = (double *)malloc(sizeof(double) * (nk + 1));
+  double *gv = (double *)malloc(sizeof(double) * (nk + 1));
+  int rc = 2;
+  if (q64 && K64 && V64 && P64 && dO64 && gq && gk && gv) {
+    rc = oracle_attn_bwd_decode_f64(q64, K64, V64, P64, dO64, gq, gk, gv, NULL, T, H, KV, d,
+                                    (double)scale);
+    if (rc == 0) {
+      for (size_t i = 0; i < nq; ++i) dq[i] = (float)((double)dq[i] + gq[i]);
+      for (size_t i = 0; i < nk; ++i) {
+        dK[i] = (float)((double)dK[i] + gk[i]);
+        dV[i] = (float)((double)dV[i] + gv[i]);
+      }
+    }
+  }
+  free(q64); free(K64); free(V64); free(P64); free(dO64); free(gq); free(gk); free(gv);
+  return rc;
 }
