@@ -29,6 +29,7 @@ PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16/bf16 matrix
 PEAK_HBM = 8.0           # TB/s
 CSRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc")
 F16_KERNELS = ("k_cvt16", "k_kv16", "k_q16")
+DEC_KERNELS = ("k_dec_dp", "k_dec_kv", "k_dec_dq")
 
 
 def log(*a):
@@ -43,7 +44,9 @@ def valid_pairs(seg):
 
 def source_sha(kname):
     """Hash of the source file holding kernel `kname` and the shared header."""
-    src = "attnbwd_f16.hip" if kname.split("<")[0] in F16_KERNELS else "attnbwd.hip"
+    base = kname.split("<")[0]
+    src = ("attnbwd_f16.hip" if base in F16_KERNELS else
+           "attnbwd_decode.hip" if base in DEC_KERNELS else "attnbwd.hip")
     h = hashlib.sha256()
     for name in (src, "common.h"):
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -107,6 +110,93 @@ def cpu_baseline(x, groups):
             "seconds": dt}
 
 
+def bench_decode(args):
+    """attn_bwd_decode on the decode workload: HBM-bound, so the roofline is
+    bytes.  Algorithmic bytes per call: K and V read, dK and dV read and
+    written, P read (q, dO, dq are a few KB): 4 (6 T KV d + H T)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from causal_gqa_attention_bwd_amd import binding
+    from causal_gqa_attention_bwd_amd.workloads import DECODE_WORKLOAD, make_decode_inputs
+
+    wl = DECODE_WORKLOAD
+    T, H, KV, d = wl["T"], wl["H"], wl["KV"], wl["d"]
+    x = make_decode_inputs(T, H, KV, d)
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev) for k in ("q", "K", "V", "P", "dO")}
+    dq, dK, dV = torch.zeros_like(t["q"]), torch.zeros_like(t["K"]), torch.zeros_like(t["V"])
+    scale = float(x["scale"])
+    log(f"bench: decode workload {wl['name']}: T={T} H={H} KV={KV} d={d}")
+
+    def step():
+        binding.attn_bwd_decode(t["q"], t["K"], t["V"], t["P"], t["dO"], dq, dK, dV, scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    binding.profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms1, ms2, ms3, ncalls = binding.profile_end()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    assert ncalls == args.steps, (ncalls, args.steps)
+    if not (torch.isfinite(dq).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()):
+        raise RuntimeError("non-finite gradients")
+    kv_bytes = 4.0 * T * KV * d
+    total = 6 * kv_bytes + 4.0 * H * T
+    # per kernel: its share of the algorithmic bytes (k_dec_dp: V and P;
+    # k_dec_kv: K, dK and dV read and written, P; k_dec_dq: dq)
+    passes = [("k_dec_dp", ms1, kv_bytes + 4.0 * H * T), ("k_dec_kv", ms2, 5 * kv_bytes + 4.0 * H * T),
+              ("k_dec_dq", ms3, 8.0 * H * d)]
+    kernel_ms = {n: round(tt / ncalls, 4) for n, tt, _ in passes}
+    kname, kms_sum, kbytes = max(passes, key=lambda p: p[1])
+    kms = kms_sum / ncalls
+    kach = kbytes / (kms * 1e-3) / 1e9
+    value = total / (ms_step * 1e-3) / 1e9
+    log(f"bench: {ms_step:.4f} ms/step, " + ", ".join(f"{n} {v:.4f} ms" for n, v in kernel_ms.items())
+        + f", {value:.1f} GB/s algorithmic")
+    cpu = None
+    if args.cpu_groups > 0:
+        log("bench: timing the oracle on the host ...")
+        t0 = time.perf_counter()
+        oracle.attn_bwd_decode(x["q"], x["K"], x["V"], x["P"], x["dO"], x["scale"])
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(total / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle attn_bwd_decode (fp64 C, one thread) on the whole workload; "
+                         f"{dt:.2f} s wall"}
+    out = {
+        "metric": "single-query attention-backward HBM throughput (algorithmic bytes)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "history_len": T, "n_heads": H, "n_kv_heads": KV,
+                   "head_dim": d, "entry": "attn_bwd_decode", "algorithmic_bytes_per_step": total,
+                   "kernel_ms": kernel_ms},
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(kach, 1),
+                     "peak": PEAK_HBM * 1000.0, "unit": "GB/s",
+                     "frac": round(kach / (PEAK_HBM * 1000.0), 4),
+                     "traffic": read_traffic(kname, wl["name"]), "avg_launch_ms": round(kms, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +211,9 @@ def main():
                     help="time attn_bwd_o (row term read off the forward output O) instead")
     ap.add_argument("--rope", action="store_true",
                     help="time attn_bwd_rope (RoPE backward fused into the write-back, base 1e4)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time attn_bwd_decode (single-query backward over a 32768-key history, "
+                         "stored probabilities) instead; reported against HBM bandwidth")
     ap.add_argument("--f16", action="store_true",
                     help="time attn_bwd_f16 (fp16 matrix-core operands, fp32 accumulation; with "
                          "--o-entry the forward output is passed)")
@@ -129,6 +222,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
               "multi-GPU mode", file=sys.stderr)
         sys.exit(2)
+
+    if args.decode:
+        bench_decode(args)
+        return
 
     import numpy as np
     import torch

@@ -13,8 +13,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_bwd_f16", "attn_bwd_o", "attn_bwd_plan", "attn_bwd_rope",
-            "attn_fwd_lse", "attn_last_error", "attn_profile_begin", "attn_profile_end")
+EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_o", "attn_bwd_plan",
+            "attn_bwd_rope", "attn_fwd_lse", "attn_last_error", "attn_profile_begin",
+            "attn_profile_end")
 
 _lib = None
 
@@ -43,6 +44,8 @@ def load():
     lib.attn_bwd_rope.restype = I
     lib.attn_bwd_f16.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_f16.restype = I
+    lib.attn_bwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_bwd_decode.restype = I
     lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                   ctypes.POINTER(ctypes.c_int)]
     lib.attn_bwd_plan.restype = I
@@ -161,6 +164,27 @@ def attn_bwd_f16(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
                              _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                              _stream(stream))
     _raise_on(st, "attn_bwd_f16")
+
+
+def attn_bwd_decode(q, K, V, P, dO, dq, dK, dV, scale, stream=None):
+    """Single-query backward over a KV history (the C ABI's attn_bwd_decode):
+    q, dO, dq [H,d]; K, V, dK, dV [T,KV,d]; P [H,T] the forward's
+    probabilities; dq, dK, dV accumulate."""
+    import torch
+    H, d = q.shape
+    T, KV, d2 = K.shape
+    if d2 != d:
+        raise ValueError(f"q {tuple(q.shape)} and K {tuple(K.shape)} disagree")
+    f32 = (torch.float32,)
+    _check_tensors([("q", q, f32), ("K", K, f32), ("V", V, f32), ("P", P, f32), ("dO", dO, f32),
+                    ("dq", dq, f32), ("dK", dK, f32), ("dV", dV, f32)], q.device)
+    for name, t, shape in (("V", V, K.shape), ("P", P, (H, T)), ("dO", dO, q.shape),
+                           ("dq", dq, q.shape), ("dK", dK, K.shape), ("dV", dV, K.shape)):
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    st = load().attn_bwd_decode(_ptr(q), _ptr(K), _ptr(V), _ptr(P), _ptr(dO), _ptr(dq), _ptr(dK),
+                                _ptr(dV), T, H, KV, d, float(scale), _stream(stream))
+    _raise_on(st, "attn_bwd_decode")
 
 
 def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):

@@ -104,3 +104,25 @@ def random_problem(rng: np.random.Generator, S: int, H: int, KV: int, d: int,
     dO = rng.standard_normal((S, H, d)).astype(dtype)
     seg = np.zeros(S, np.uint32) if seg is None else np.asarray(seg, np.uint32)
     return dict(Q=Q, K=K, V=V, dO=dO, seg=seg, scale=np.float32(1.0 / np.sqrt(d)))
+
+
+# The single-query (decode-step) backward over a KV history: one query per head
+# and a history of T keys, with the forward's probabilities given.  Llama-like
+# heads (32 query heads in 8 KV groups of 128 columns) over a 32768-position
+# history.
+DECODE_WORKLOAD = dict(name="decode_t32768_h32_kv8_d128", T=32768, H=32, KV=8, d=128)
+
+
+def make_decode_inputs(T: int, H: int, KV: int, d: int, seed: int = 1100) -> dict:
+    """q, dO [H,d], K, V [T,KV,d] float32 standard normals (drawn in that order
+    from ``default_rng(seed)``), and probabilities P [H,T]: each row
+    normalises exp of standard-normal logits (the diffuse attention of an
+    untrained model), in float64 then rounded to float32.  scale = 1/sqrt(d)."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((H, d)).astype(np.float32)
+    K = rng.standard_normal((T, KV, d)).astype(np.float32)
+    V = rng.standard_normal((T, KV, d)).astype(np.float32)
+    dO = rng.standard_normal((H, d)).astype(np.float32)
+    e = np.exp(rng.standard_normal((H, T)))
+    P = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return dict(q=q, K=K, V=V, dO=dO, P=P, scale=np.float32(1.0 / np.sqrt(d)))

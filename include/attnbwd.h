@@ -171,6 +171,34 @@ attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const
                            void* stream);
 
 /*
+ * attn_bwd_decode -- the single-query backward over a KV history (one decode
+ * step) with the forward's probabilities stored: page "rullama 0.5.0 --
+ * src/backend/dispatch/training.rs", attention_backward_dq_chained and
+ * attention_backward_dkv_chained (pass 1: score gradients and dq; pass 2:
+ * key-major dK and dV).  The query of head h (kv_h = h / (n_heads /
+ * n_kv_heads)) sees every one of the history_len keys:
+ *   dP[h][j] = dO[h,:] . V[j,kv_h,:],  D[h] = sum_j P[h][j] dP[h][j],
+ *   dS[h][j] = P[h][j] (dP[h][j] - D[h]),
+ *   dq[h,:] += scale sum_j dS[h][j] K[j,kv_h,:],
+ *   dK[j,kv,:] += scale sum_{h in kv's group} dS[h][j] q[h,:],
+ *   dV[j,kv,:] += sum_{h in kv's group} P[h][j] dO[h,:].
+ * Layouts (fp32, contiguous, device pointers): q, dO, dq [n_heads, head_dim];
+ * P [n_heads, history_len]; K, V, dK, dV [history_len, n_kv_heads, head_dim]
+ * (the history's positions in order, like K and V above).  dq, dK, dV are
+ * ACCUMULATED.  scale multiplies the scores (the page's parameters carry
+ * none; a caller passes 1/sqrt(head_dim) for the usual attention).
+ * Deterministic (no atomics).  Workspace (same pool): (n_heads * history_len
+ * + n_heads * ceil(history_len/128) * (head_dim + 1)) * 4 bytes.
+ * Errors as attn_bwd (history_len in the place of seq_len).  history_len
+ * == 0 returns ATTN_OK and does nothing (K, V, P, dK and dV may then be
+ * NULL).
+ */
+attn_status_t attn_bwd_decode(const float* q, const float* K, const float* V, const float* P,
+                              const float* dO, float* dq, float* dK, float* dV,
+                              int history_len, int n_heads, int n_kv_heads, int head_dim,
+                              float scale, void* stream);
+
+/*
  * attn_bwd_plan -- host-side query (no GPU work): the workspace bytes one
  * attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes, and whether its key-major pass reads
  * stored probability tiles (1) or recomputes them (0).  Either output pointer
@@ -201,7 +229,8 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
  *   the query-major pass (row term D, and dQ or the stored tiles), the
  *   key-major pass (dK, dV), and -- with stored tiles -- the dQ pass.  An
  *   attn_bwd_f16 call records its three: the fp16 copies and the row term,
- *   the key-major pass, the dQ pass.
+ *   the key-major pass, the dQ pass; an attn_bwd_decode call its three:
+ *   the score-gradient pass, the dK/dV pass, the dq pass.
  * attn_profile_end: waits for those events, writes into ms[0], ms[1], ms[2]
  *   the summed device time in milliseconds of each of the three passes over
  *   the recorded calls (ms[2] = 0 for calls without the dQ pass), into
