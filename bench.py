@@ -110,6 +110,21 @@ def cpu_baseline(x, groups):
             "seconds": dt}
 
 
+def calibration_copy(mb, dev):
+    """One device copy of mb MiB (nothing when mb is 0): a kernel of known
+    traffic whose FETCH_SIZE and WRITE_SIZE counters scale those of the
+    backward kernels to bytes."""
+    import torch
+    if not mb:
+        return
+    n = mb * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"bench: calibration copy of {mb} MiB done")
+
+
 def bench_decode(args):
     """attn_bwd_decode on the decode workload: HBM-bound, so the roofline is
     bytes.  Algorithmic bytes per call: K and V read, dK and dV read and
@@ -136,6 +151,7 @@ def bench_decode(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    calibration_copy(args.calib_copy_mb, dev)
     binding.profile_begin()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -271,13 +287,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    if args.calib_copy_mb:
-        n = args.calib_copy_mb * (1 << 20) // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        log(f"bench: calibration copy of {args.calib_copy_mb} MiB done")
+    calibration_copy(args.calib_copy_mb, dev)
 
     binding.profile_begin()
     e0 = torch.cuda.Event(enable_timing=True)

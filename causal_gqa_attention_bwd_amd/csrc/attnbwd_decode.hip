@@ -30,6 +30,15 @@
 
 #define DEC_TB 128  // keys per chunk
 
+// A 16-byte load that is marked nontemporal: the history's K, V, dK and dV
+// rows are each read once per pass, so they are streamed past the caches
+// (measured faster than plain loads for both passes; stores stay plain).
+typedef float dec_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 stream_load(const float4* p) {
+  const dec_f4 v = __builtin_nontemporal_load(reinterpret_cast<const dec_f4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 struct DecArgs {
   const float *q, *K, *V, *P, *dO;  // [H, d], [T, KV, d] x 2, [H, T], [H, d]
   float *dq, *dK, *dV;              // [H, d], [T, KV, d] x 2 (accumulated)
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(256) void k_dec_dp(DecArgs a) {
         const int i = lane + 64 * u, kr = i / n4, c4 = i % n4;
         vb[u] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (i < DEC_KW * n4 && kb + kr < nj)
-          vb[u] = reinterpret_cast<const float4*>(a.V)[((size_t)(j0 + kb + kr) * a.KV + kvh) * n4 + c4];
+          vb[u] = stream_load(reinterpret_cast<const float4*>(a.V) + ((size_t)(j0 + kb + kr) * a.KV + kvh) * n4 + c4);
       }
       // the wave's LDS operations run in order: the previous step's reads of
       // the tile are done before these writes, and these before the reads
@@ -212,9 +221,9 @@ __global__ __launch_bounds__(256) void k_dec_kv(DecArgs a) {
           kc[u] = k0[u] = v0[u] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (jj < nj) {
             const size_t off = ((size_t)(j0 + jj) * a.KV + kvh) * n4 + c4;
-            kc[u] = reinterpret_cast<const float4*>(a.K)[off];
-            k0[u] = reinterpret_cast<const float4*>(a.dK)[off];
-            v0[u] = reinterpret_cast<const float4*>(a.dV)[off];
+            kc[u] = stream_load(reinterpret_cast<const float4*>(a.K) + off);
+            k0[u] = stream_load(reinterpret_cast<const float4*>(a.dK) + off);
+            v0[u] = stream_load(reinterpret_cast<const float4*>(a.dV) + off);
           }
         }
 #pragma unroll
