@@ -30,6 +30,7 @@ PEAK_HBM = 8.0           # TB/s
 CSRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc")
 F16_KERNELS = ("k_cvt16", "k_kv16", "k_q16")
 DEC_KERNELS = ("k_dec_dp", "k_dec_kv", "k_dec_dq")
+SHORT_KERNELS = ("k_short", "k_short_rowterm")
 
 
 def log(*a):
@@ -46,7 +47,8 @@ def source_sha(kname):
     """Hash of the source file holding kernel `kname` and the shared header."""
     base = kname.split("<")[0]
     src = ("attnbwd_f16.hip" if base in F16_KERNELS else
-           "attnbwd_decode.hip" if base in DEC_KERNELS else "attnbwd.hip")
+           "attnbwd_decode.hip" if base in DEC_KERNELS else
+           "attnbwd_short.hip" if base in SHORT_KERNELS else "attnbwd.hip")
     h = hashlib.sha256()
     for name in (src, "common.h"):
         with open(os.path.join(CSRC, name), "rb") as f:
@@ -230,6 +232,9 @@ def main():
     ap.add_argument("--decode", action="store_true",
                     help="time attn_bwd_decode (single-query backward over a 32768-key history, "
                          "stored probabilities) instead; reported against HBM bandwidth")
+    ap.add_argument("--short", action="store_true",
+                    help="time attn_bwd_short (the single-launch short-sequence backward, "
+                         "seq_len <= 1024; with --o-entry the forward output is passed)")
     ap.add_argument("--f16", action="store_true",
                     help="time attn_bwd_f16 (fp16 matrix-core operands, fp32 accumulation; with "
                          "--o-entry the forward output is passed)")
@@ -274,7 +279,9 @@ def main():
     torch.cuda.synchronize()
 
     def step():
-        if args.f16:
+        if args.short:
+            binding.attn_bwd_short(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
+        elif args.f16:
             binding.attn_bwd_f16(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
         elif args.rope:
             binding.attn_bwd_rope(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale,
@@ -316,7 +323,13 @@ def main():
     # attn_bwd_f16: the fp16 copies plus the row term (S and dP once more when
     # no forward output is given), k_kv16 (S, dP, P^T.dO, dS^T.Q) and k_q16
     # (S, dP, dS.K)
-    if args.f16:
+    # attn_bwd_short: one launch whose key-role workgroups form S, dP, P^T.dO,
+    # dS^T.Q and whose query-role workgroups form S, dP, dS.K (14 d per pair
+    # and head together), after a row-term launch (S, dP) when no O is given
+    if args.short:
+        passes = ([("k_short", ms_q, 14.0)] if args.o_entry else
+                  [("k_short_rowterm", ms_q, 4.0), ("k_short", ms_k, 14.0)])
+    elif args.f16:
         passes = [("k_cvt16", ms_q, 0.0 if args.o_entry else 4.0), ("k_kv16", ms_k, 8.0),
                   ("k_q16", ms_s, 6.0)]
     elif stored:
@@ -365,12 +378,15 @@ def main():
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
                    "head_dim": w.d, "mask": "causal" if seg is None else "documents",
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
-                   "entry": ("attn_bwd_f16" if args.f16 else "attn_bwd_rope" if args.rope else
+                   "entry": ("attn_bwd_short" if args.short else
+                             "attn_bwd_f16" if args.f16 else "attn_bwd_rope" if args.rope else
                              "attn_bwd_o" if args.o_entry else "attn_bwd"),
                    "operands": ("fp16, fp32 accumulation" if args.f16 else "fp32"),
                    "forward_output_given": bool(args.o_entry),
-                   "stored_tiles": None if args.f16 else stored,
-                   "workspace_bytes": f16_ws if args.f16 else ws_bytes,
+                   "stored_tiles": None if args.f16 or args.short else stored,
+                   "workspace_bytes": (0 if args.short and args.o_entry else
+                                       w.S * w.H * 4 if args.short else
+                                       f16_ws if args.f16 else ws_bytes),
                    "kernel_ms": kernel_ms},
         "roofline": roofline,
         "cpu_baseline": cpu,

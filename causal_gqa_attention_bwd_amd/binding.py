@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_o", "attn_bwd_plan",
-            "attn_bwd_rope", "attn_fwd_lse", "attn_last_error", "attn_profile_begin",
-            "attn_profile_end")
+            "attn_bwd_rope", "attn_bwd_short", "attn_fwd_lse", "attn_last_error",
+            "attn_profile_begin", "attn_profile_end")
 
 _lib = None
 
@@ -44,6 +44,8 @@ def load():
     lib.attn_bwd_rope.restype = I
     lib.attn_bwd_f16.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_f16.restype = I
+    lib.attn_bwd_short.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_bwd_short.restype = I
     lib.attn_bwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_decode.restype = I
     lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
@@ -164,6 +166,17 @@ def attn_bwd_f16(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
                              _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                              _stream(stream))
     _raise_on(st, "attn_bwd_f16")
+
+
+def attn_bwd_short(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
+    """The short-sequence backward (the C ABI's attn_bwd_short; seq_len <= 1024,
+    head_dim <= 64): one launch when O (the forward output) is given, two when
+    O is None."""
+    S, H, KV, d = _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV)
+    st = load().attn_bwd_short(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(seg),
+                               _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
+                               _stream(stream))
+    _raise_on(st, "attn_bwd_short")
 
 
 def attn_bwd_decode(q, K, V, P, dO, dq, dK, dV, scale, stream=None):

@@ -8,7 +8,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRCS = [os.path.join(HERE, "csrc", f)
-        for f in ("attnbwd.hip", "attnbwd_f16.hip", "attnbwd_decode.hip")]
+        for f in ("attnbwd.hip", "attnbwd_f16.hip", "attnbwd_decode.hip", "attnbwd_short.hip")]
 LIB = os.path.join(HERE, "libattnbwd.so")
 INCLUDE = os.path.join(ROOT, "include")
 

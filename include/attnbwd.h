@@ -171,6 +171,28 @@ attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const
                            void* stream);
 
 /*
+ * attn_bwd_short -- the backward for short sequences (seq_len <= 1024): page
+ * "llm.istanbul -- 10_backward_attention.wgsl", attention_backward_short and
+ * attention_backward_short_dKdV, the page's variant for sequences of at most
+ * 1024 positions.  The same sums, arguments, layouts, += semantics and mask
+ * as attn_bwd; O is the forward output (as for attn_bwd_o: D = dO . O) or
+ * NULL (D = sum_j P dP, computed by a first launch).  With O given the whole
+ * backward is ONE kernel launch and needs no workspace: workgroups that own
+ * 32 queries of one head (dQ) and workgroups that own 32 keys of one KV head
+ * (dK, dV) run side by side, each splitting its visible blocks over its four
+ * waves and adding the waves' partial sums in a fixed order (deterministic,
+ * no atomics).  Without O, a workspace of seq_len * n_heads * 4 bytes (same
+ * pool) holds D between the two launches.  Errors as attn_bwd, plus
+ * ATTN_ERR_UNSUPPORTED for seq_len > 1024 or head_dim > 64 (attn_bwd and
+ * attn_bwd_o take those).
+ */
+attn_status_t attn_bwd_short(const float* Q, const float* K, const float* V, const float* O,
+                             const float* dO, const float* LSE, const uint32_t* seg,
+                             float* dQ, float* dK, float* dV,
+                             int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                             void* stream);
+
+/*
  * attn_bwd_decode -- the single-query backward over a KV history (one decode
  * step) with the forward's probabilities stored: page "rullama 0.5.0 --
  * src/backend/dispatch/training.rs", attention_backward_dq_chained and
@@ -230,7 +252,9 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
  *   key-major pass (dK, dV), and -- with stored tiles -- the dQ pass.  An
  *   attn_bwd_f16 call records its three: the fp16 copies and the row term,
  *   the key-major pass, the dQ pass; an attn_bwd_decode call its three:
- *   the score-gradient pass, the dK/dV pass, the dq pass.
+ *   the score-gradient pass, the dK/dV pass, the dq pass; an attn_bwd_short
+ *   call its one (the whole backward; with O NULL two: the row term, then
+ *   the backward).
  * attn_profile_end: waits for those events, writes into ms[0], ms[1], ms[2]
  *   the summed device time in milliseconds of each of the three passes over
  *   the recorded calls (ms[2] = 0 for calls without the dQ pass), into

@@ -20,10 +20,12 @@ def seg_dev(seg):
     return None if seg is None else to_dev(np.asarray(seg, np.uint32).astype(np.int32))
 
 
-def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None, rope=None, f16=False):
+def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None, rope=None, f16=False,
+            short=False):
     """Run attn_bwd (attn_bwd_o when the forward output O is given; attn_bwd_rope
-    when rope = (base, pos_offset); attn_bwd_f16, with or without O, when f16)
-    on the GPU.  Returns numpy (dQ, dK, dV)."""
+    when rope = (base, pos_offset); attn_bwd_f16, with or without O, when f16;
+    attn_bwd_short, with or without O, when short) on the GPU.  Returns numpy
+    (dQ, dK, dV)."""
     t = {k: to_dev(p[k]) for k in ("Q", "K", "V", "dO")}
     if init is None:
         out = [torch.zeros_like(t["Q"]), torch.zeros_like(t["K"]), torch.zeros_like(t["V"])]
@@ -31,7 +33,11 @@ def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None, rope=None, f16=Fa
         out = [to_dev(x.copy()) for x in init]
     s = seg_dev(p["seg"] if seg is None else seg) if use_seg else None
     L = to_dev(lse.astype(np.float32))
-    if f16:
+    if short:
+        binding.attn_bwd_short(t["Q"], t["K"], t["V"],
+                               None if O is None else to_dev(O.astype(np.float32)), t["dO"], L, s,
+                               *out, float(p["scale"]))
+    elif f16:
         binding.attn_bwd_f16(t["Q"], t["K"], t["V"],
                              None if O is None else to_dev(O.astype(np.float32)), t["dO"], L, s,
                              *out, float(p["scale"]))

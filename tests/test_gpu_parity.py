@@ -15,20 +15,22 @@ def say(msg):
     print(msg, flush=True)
 
 
-def check_full(p, tag, init=None, with_o=False, o_shift=None, rope=None, f16=False, tol=TOL):
+def check_full(p, tag, init=None, with_o=False, o_shift=None, rope=None, f16=False, tol=TOL,
+               short=False):
     """GPU vs oracle on the whole problem.  with_o: through attn_bwd_o with the
     oracle's forward output (plus o_shift, if given) on both sides.  rope =
     (base, pos_offset): through attn_bwd_rope.  f16: through attn_bwd_f16 (with
-    the forward output when with_o)."""
+    the forward output when with_o).  short: through attn_bwd_short (likewise)."""
     O, lse = oracle.attn_fwd(p["Q"], p["K"], p["V"], p["seg"], p["scale"], want_o=with_o)
     if with_o and o_shift is not None:
         O = (O + o_shift).astype(np.float32)
     ref = oracle.attn_bwd(p["Q"], p["K"], p["V"], p["dO"], lse, p["seg"], p["scale"],
                           *(init if init is not None else ()), O=O if with_o else None, rope=rope)
-    entry = "attn_bwd_f16" if f16 else "attn_bwd_o" if with_o else "attn_bwd"
+    entry = ("attn_bwd_short" if short else "attn_bwd_f16" if f16 else
+             "attn_bwd_o" if with_o else "attn_bwd")
     say(f"[gpu] {tag}: {entry} S={p['Q'].shape[0]} H={p['Q'].shape[1]} "
         f"KV={p['K'].shape[1]} d={p['Q'].shape[2]}")
-    got = gpu_bwd(p, lse, init=init, O=O if with_o else None, rope=rope, f16=f16)
+    got = gpu_bwd(p, lse, init=init, O=O if with_o else None, rope=rope, f16=f16, short=short)
     errs = {}
     pairs = []
     for name, g, w, i0 in zip(("dQ", "dK", "dV"), got, ref,
