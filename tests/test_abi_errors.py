@@ -1,0 +1,91 @@
+"""Argument errors of every backward entry point are status codes returned on
+the host before any HIP call, so they are checked here without a GPU.  The
+tensor pointers are placeholders that no failing (or empty) call reads: an
+aligned non-NULL address, NULL, or a misaligned one."""
+import math
+
+import pytest
+
+from causal_gqa_attention_bwd_amd import binding
+
+OK, INVALID, UNSUPPORTED = binding.ATTN_OK, binding.ATTN_ERR_INVALID_ARG, binding.ATTN_ERR_UNSUPPORTED
+A = 0x10000        # an aligned placeholder address
+MIS = 0x10004      # a misaligned one
+
+
+def bwd_args(S=8, H=2, KV=1, d=64, scale=0.125, null=None, mis=None, with_o=True):
+    """Q, K, V, O, dO, LSE, seg, dQ, dK, dV, S, H, KV, d, scale, stream."""
+    names = ["Q", "K", "V", "O", "dO", "LSE", "seg", "dQ", "dK", "dV"]
+    ptrs = {n: A for n in names}
+    if not with_o:
+        ptrs["O"] = None
+    if null:
+        ptrs[null] = None
+    if mis:
+        ptrs[mis] = MIS
+    return [ptrs[n] for n in names] + [S, H, KV, d, scale, None]
+
+
+def decode_args(T=8, H=2, KV=1, d=64, scale=0.125, null=(), mis=None):
+    """q, K, V, P, dO, dq, dK, dV, T, H, KV, d, scale, stream."""
+    names = ["q", "K", "V", "P", "dO", "dq", "dK", "dV"]
+    ptrs = {n: A for n in names}
+    for n in null:
+        ptrs[n] = None
+    if mis:
+        ptrs[mis] = MIS
+    return [ptrs[n] for n in names] + [T, H, KV, d, scale, None]
+
+
+CASES = [
+    # attn_bwd_short
+    ("attn_bwd_short", bwd_args(null="Q"), INVALID, "NULL"),
+    ("attn_bwd_short", bwd_args(H=3, KV=2), INVALID, "multiple"),
+    ("attn_bwd_short", bwd_args(scale=math.inf), INVALID, "scale"),
+    ("attn_bwd_short", bwd_args(S=1025), UNSUPPORTED, "1024"),
+    ("attn_bwd_short", bwd_args(d=80), UNSUPPORTED, "64"),
+    ("attn_bwd_short", bwd_args(d=24), UNSUPPORTED, "head_dim"),
+    ("attn_bwd_short", bwd_args(mis="dK"), UNSUPPORTED, "aligned"),
+    ("attn_bwd_short", bwd_args(S=1024, H=16384, KV=1, d=64), UNSUPPORTED, "2^31"),
+    ("attn_bwd_short", bwd_args(S=0), OK, ""),
+    ("attn_bwd_short", bwd_args(S=0, with_o=False), OK, ""),
+    # attn_bwd_decode
+    ("attn_bwd_decode", decode_args(null=("q",)), INVALID, "NULL"),
+    ("attn_bwd_decode", decode_args(null=("K",)), INVALID, "NULL"),
+    ("attn_bwd_decode", decode_args(T=-1), INVALID, "negative"),
+    ("attn_bwd_decode", decode_args(H=4, KV=3), INVALID, "multiple"),
+    ("attn_bwd_decode", decode_args(d=250), UNSUPPORTED, "head_dim"),
+    ("attn_bwd_decode", decode_args(mis="P"), UNSUPPORTED, "aligned"),
+    ("attn_bwd_decode", decode_args(T=0, null=("K", "V", "P", "dK", "dV")), OK, ""),
+    # attn_bwd_f16
+    ("attn_bwd_f16", bwd_args(null="dV"), INVALID, "NULL"),
+    ("attn_bwd_f16", bwd_args(d=8), UNSUPPORTED, "head_dim"),
+    ("attn_bwd_f16", bwd_args(mis="seg"), UNSUPPORTED, "aligned"),
+    ("attn_bwd_f16", bwd_args(S=0, with_o=False), OK, ""),
+    # attn_bwd_o
+    ("attn_bwd_o", bwd_args(null="O"), INVALID, "NULL"),
+    ("attn_bwd_o", bwd_args(S=-4), INVALID, "negative"),
+    ("attn_bwd_o", bwd_args(S=0), OK, ""),
+]
+
+
+@pytest.mark.parametrize("entry,args,status,text", CASES,
+                         ids=[f"{c[0]}-{i}" for i, c in enumerate(CASES)])
+def test_entry_rejects_bad_arguments_on_the_host(entry, args, status, text):
+    lib = binding.load()
+    st = getattr(lib, entry)(*args)
+    assert st == status, (st, binding.last_error())
+    if status != OK:
+        assert text in binding.last_error(), binding.last_error()
+    else:
+        assert binding.last_error() == ""
+
+
+@pytest.mark.parametrize("base,pos,text", [(0.0, 0, "rope_base"), (math.nan, 0, "rope_base"),
+                                           (1e4, -1, "pos_offset"), (1e4, 2**31 - 4, "pos_offset")])
+def test_rope_entry_rejects_bad_rotation_arguments(base, pos, text):
+    lib = binding.load()
+    args = bwd_args(S=8)[:-1] + [base, pos, None]
+    st = lib.attn_bwd_rope(*args)
+    assert st == INVALID, (st, binding.last_error())
+    assert text in binding.last_error() or "pos" in binding.last_error()
