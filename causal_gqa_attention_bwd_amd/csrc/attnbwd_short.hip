@@ -41,7 +41,9 @@ struct ShortArgs {
   const uint32_t* seg;                     // NULL = all zeros
   float *dQ, *dK, *dV;
   float* Dws;  // [S, H] row term (written by the row-term launch when O is NULL)
+  float* part; // ksplit > 1: [2 ksplit][S, KV, d] partial dK, dV of each head split
   int S, H, KV, d, nqb;
+  int ksplit;  // workgroups sharing a key block's heads (a power of two dividing H / KV)
   float scale;
 };
 
@@ -274,10 +276,13 @@ __device__ __forceinline__ void short_query(const ShortArgs& a, int qb, int h, f
 }
 
 // ---------------------------------------------------------------------------
-// Key role: dK and dV of key block kb, KV head kvh.  A wave's items are
-// numbers wave, wave + 4, ... of the (visible query block, head of the
-// group) pairs, query block major; the next item's Q, dO (and O) rows are
-// loaded while the current item's later products run.
+// Key role: dK and dV of key block kb, KV head kvh, over the heads of head
+// split `split` (all of the group's heads when ksplit = 1).  A wave's items
+// are numbers wave, wave + 4, ... of the (visible query block, head of the
+// split) pairs, query block major; the next item's Q, dO (and O) rows are
+// loaded while the current item's later products run.  With one split the
+// workgroup adds its sums into dK, dV; with several it writes them to its
+// split's slices of `part`, which k_short_sum adds in split order.
 // ---------------------------------------------------------------------------
 template <int HD>
 struct KeyItem {
@@ -286,14 +291,15 @@ struct KeyItem {
 };
 
 template <int DP>
-__device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, float* lds,
-                                          float* sRow, uint32_t* sSeg) {
+__device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, int split,
+                                          float* lds, float* sRow, uint32_t* sSeg) {
   using G = ShortGeom<DP>;
   constexpr int HD = G::HD, LDT = G::LDT, NC = G::NC;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, l32 = lane & 31;
   const int S = a.S, H = a.H, d = a.d, g = H / a.KV;
+  const int gs = g / a.ksplit, head0 = kvh * g + split * gs;  // this split's heads
   const int j0 = kb * 32, j = j0 + l32;
   const bool k_ok = j < S;
   const float sc2 = a.scale * ATTN_LOG2E;
@@ -307,8 +313,10 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, f
   load_half<HD>(rsrc(a.K, kbytes), krow, hf, d, k_ok, kB);
   load_half<HD>(rsrc(a.V, kbytes), krow, hf, d, k_ok, vB);
   BlockOut<DP> outK, outV;
-  outK.load(rsrc(a.dK, kbytes), j0, S, d, a.KV, kvh);
-  outV.load(rsrc(a.dV, kbytes), j0, S, d, a.KV, kvh);
+  if (a.ksplit == 1) {
+    outK.load(rsrc(a.dK, kbytes), j0, S, d, a.KV, kvh);
+    outV.load(rsrc(a.dV, kbytes), j0, S, d, a.KV, kvh);
+  }
 
   stage_seg(a, sSeg);
   // query blocks with a row that sees a key of this block:
@@ -319,7 +327,7 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, f
     if (si <= (uint32_t)i && si <= (uint32_t)(j0 + 31)) qmask |= 1u << (i >> 5);
   }
   qmask = __builtin_amdgcn_readfirstlane(wave_or(qmask));
-  const int nitems = __builtin_popcount(qmask) * g;
+  const int nitems = __builtin_popcount(qmask) * gs;
 
   float* sQ = lds + wave * 2 * 32 * LDT;  // this wave's Q and dO tiles
   float* sO = sQ + 32 * LDT;
@@ -329,12 +337,12 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, f
 #pragma unroll
   for (int c = 0; c < NC; ++c) accK[c] = accV[c] = zero16();
 
-  // item k: query block nth_bit(qmask, k / g), head kvh * g + k % g (k >=
+  // item k: query block nth_bit(qmask, k / gs), head head0 + k % gs (k >=
   // nitems: an empty slot whose loads read zeros)
   auto issue = [&](int k, KeyItem<HD>& it) {
     const bool ok = k < nitems;
     const int kk = ok ? k : 0;
-    const int i = 32 * nth_bit(qmask, kk / g) + l32, h = kvh * g + kk % g;
+    const int i = 32 * nth_bit(qmask, kk / gs) + l32, h = head0 + kk % gs;
     const bool q_ok = ok && i < S;
     const size_t qrow = ((size_t)i * H + h) * d;
     load_half<HD>(rQ, qrow, hf, d, q_ok, it.q);
@@ -349,7 +357,7 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, f
   // the next item's loads go into the same registers
   KeyItem<HD> it;
   auto compute = [&](int k) {
-    const int i0 = 32 * nth_bit(qmask, k / g);
+    const int i0 = 32 * nth_bit(qmask, k / gs);
     float Di = it.dws;
     if (a.O) {
       float s = 0.f;
@@ -408,6 +416,9 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, f
       sRV[e] = accV[c][r];
     }
   __syncthreads();
+  const size_t slice = (size_t)S * a.KV * d;
+  float* pK = a.part + (size_t)(2 * split) * slice;
+  float* pV = pK + slice;
 #pragma unroll
   for (int n = 0; n < BlockOut<DP>::N; ++n) {
     const int e = tid + 256 * n, row = e / DP, col = e % DP;
@@ -415,28 +426,53 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, f
       const float tk = ((sRK[e] + sRK[32 * DP + e]) + sRK[64 * DP + e]) + sRK[96 * DP + e];
       const float tv = ((sRV[e] + sRV[32 * DP + e]) + sRV[64 * DP + e]) + sRV[96 * DP + e];
       const size_t o = ((size_t)(j0 + row) * a.KV + kvh) * d + col;
-      a.dK[o] = outK.old[n] + a.scale * tk;
-      a.dV[o] = outV.old[n] + tv;
+      if (a.ksplit == 1) {
+        a.dK[o] = outK.old[n] + a.scale * tk;
+        a.dV[o] = outV.old[n] + tv;
+      } else {
+        pK[o] = a.scale * tk;
+        pV[o] = tv;
+      }
     }
   }
 }
 
-// One launch of the backward: blocks [0, nqb*KV) take the key role (key
-// block ascending: the first ones see the most queries), the rest the query
-// role (query block descending, likewise).  ROWTERM: the query role only,
-// writing D.
+// One launch of the backward: blocks [0, nqb*KV*ksplit) take the key role
+// (key block ascending: the first ones see the most queries; its KV heads
+// and head splits adjacent), the rest the query role (query block
+// descending, likewise).  ROWTERM: the query role only, writing D.
 template <int DP, bool ROWTERM>
 __global__ __launch_bounds__(256) void k_short(ShortArgs a) {
   __shared__ __attribute__((aligned(16))) float lds[ShortGeom<DP>::LDS_FLOATS];
   __shared__ float sRow[4 * 64];
   __shared__ uint32_t sSeg[SHORT_MAX_S];
   const int b = blockIdx.x;
-  const int nkey = ROWTERM ? 0 : a.nqb * a.KV;
+  const int nkey = ROWTERM ? 0 : a.nqb * a.KV * a.ksplit;
   if (b < nkey) {
-    short_key<DP>(a, b / a.KV, b % a.KV, lds, sRow, sSeg);
+    const int kvh = b % a.KV, r = b / a.KV;
+    short_key<DP>(a, r / a.ksplit, kvh, r % a.ksplit, lds, sRow, sSeg);
   } else {
     const int q = b - nkey;
     short_query<DP, ROWTERM>(a, a.nqb - 1 - q / a.H, q % a.H, lds, sSeg);
+  }
+}
+
+// dK += sum over splits of part[2 split], dV += sum of part[2 split + 1],
+// split by split in order; n = S * KV * d floats per slice (a multiple of 4).
+__global__ __launch_bounds__(256) void k_short_sum(const float* __restrict__ part, int splits,
+                                                   long long n, float* dK, float* dV) {
+  const long long n4 = n / 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    float4 k = reinterpret_cast<float4*>(dK)[i], v = reinterpret_cast<float4*>(dV)[i];
+    for (int s = 0; s < splits; ++s) {
+      const float4 pk = reinterpret_cast<const float4*>(part + (size_t)(2 * s) * n)[i];
+      const float4 pv = reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * n)[i];
+      k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
+      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+    }
+    reinterpret_cast<float4*>(dK)[i] = k;
+    reinterpret_cast<float4*>(dV)[i] = v;
   }
 }
 
@@ -446,7 +482,8 @@ static attn_status_t launch_short(const ShortArgs& a, bool rowterm, hipStream_t 
     hipLaunchKernelGGL((k_short<DP, true>), dim3(a.nqb * a.H), dim3(256), 0, st, a);
     return hip_check(hipGetLastError(), "launching k_short (row term)");
   }
-  hipLaunchKernelGGL((k_short<DP, false>), dim3(a.nqb * (a.KV + a.H)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((k_short<DP, false>), dim3(a.nqb * (a.KV * a.ksplit + a.H)), dim3(256), 0,
+                     st, a);
   return hip_check(hipGetLastError(), "launching k_short");
 }
 
@@ -478,21 +515,37 @@ extern "C" attn_status_t attn_bwd_short(const float* Q, const float* K, const fl
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   ShortArgs a;
   a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO; a.LSE = LSE; a.seg = seg;
-  a.dQ = dQ; a.dK = dK; a.dV = dV; a.Dws = nullptr;
+  a.dQ = dQ; a.dK = dK; a.dV = dV; a.Dws = nullptr; a.part = nullptr;
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim;
   a.nqb = (seq_len + 31) / 32;
   a.scale = scale;
   const int dp = head_dim <= 32 ? 32 : 64;
+  // head splits of the key role: the first key block of a long document
+  // sees up to nqb query blocks times g heads, nqb g / 4 items per wave.
+  // Split its heads (a power of two dividing g) while that chain is longer
+  // than 8 items and than a wave's share of all the items (about
+  // nqb (nqb + 1) H of them over the chip's 1024 SIMDs): beyond that the
+  // launch is bound by the total work, which the split does not reduce
+  const int g = n_heads / n_kv_heads;
+  const double share = (double)a.nqb * (a.nqb + 1) * n_heads / 1024.0;
+  int ksplit = 1;
+  while (ksplit < g && g % (2 * ksplit) == 0 &&
+         (double)a.nqb * g / (4.0 * ksplit) > std::max(8.0, share))
+    ksplit *= 2;
+  a.ksplit = ksplit;
 
   void* ws = nullptr;
-  if (!O) {
+  const size_t d_bytes = O ? 0 : ((size_t)seq_len * n_heads * 4 + 255) / 256 * 256;
+  const size_t part_bytes = ksplit > 1 ? (size_t)2 * ksplit * seq_len * n_kv_heads * head_dim * 4 : 0;
+  if (d_bytes + part_bytes > 0) {
     hipMemPool_t pool;
     rc = device_pool(&pool);
     if (rc != ATTN_OK) return rc;
-    rc = hip_check(hipMallocFromPoolAsync(&ws, (size_t)seq_len * n_heads * 4, pool, st),
+    rc = hip_check(hipMallocFromPoolAsync(&ws, d_bytes + part_bytes, pool, st),
                    "hipMallocFromPoolAsync(workspace)");
     if (rc != ATTN_OK) return rc;
-    a.Dws = static_cast<float*>(ws);
+    if (!O) a.Dws = static_cast<float*>(ws);
+    if (ksplit > 1) a.part = reinterpret_cast<float*>(static_cast<char*>(ws) + d_bytes);
   }
   rc = profile_mark(st, true);
   if (rc == ATTN_OK && !O) {
@@ -500,6 +553,12 @@ extern "C" attn_status_t attn_bwd_short(const float* Q, const float* K, const fl
     if (rc == ATTN_OK) rc = profile_mark(st);
   }
   if (rc == ATTN_OK) rc = dp == 32 ? launch_short<32>(a, false, st) : launch_short<64>(a, false, st);
+  if (rc == ATTN_OK && ksplit > 1) {
+    const long long n = (long long)seq_len * n_kv_heads * head_dim;
+    const int blocks = (int)std::min<long long>((n / 4 + 255) / 256, 2048);
+    hipLaunchKernelGGL(k_short_sum, dim3(blocks), dim3(256), 0, st, a.part, ksplit, n, dK, dV);
+    rc = hip_check(hipGetLastError(), "launching k_short_sum");
+  }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (ws) {
     attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");

@@ -182,9 +182,16 @@ attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const
  * (dK, dV) run side by side, each splitting its visible blocks over its four
  * waves and adding the waves' partial sums in a fixed order (deterministic,
  * no atomics).  Without O, a workspace of seq_len * n_heads * 4 bytes (same
- * pool) holds D between the two launches.  Errors as attn_bwd, plus
- * ATTN_ERR_UNSUPPORTED for seq_len > 1024 or head_dim > 64 (attn_bwd and
- * attn_bwd_o take those).
+ * pool) holds D between a row-term launch and the backward.  When a KV
+ * group's heads are many against the sequence (a key block at the start of
+ * a long document would otherwise take one workgroup's whole time), the
+ * key-side workgroups split the group's heads into `splits` shares (a power
+ * of two dividing n_heads / n_kv_heads, chosen from the shape alone), write
+ * partial dK, dV sums to a workspace of 2 * splits * seq_len * n_kv_heads *
+ * head_dim * 4 bytes, and one more launch adds them in split order (still
+ * deterministic).  Errors as attn_bwd, plus ATTN_ERR_UNSUPPORTED for
+ * seq_len > 1024, head_dim > 64 (attn_bwd and attn_bwd_o take those), or
+ * seq_len * n_heads * head_dim * 4 >= 2^31.
  */
 attn_status_t attn_bwd_short(const float* Q, const float* K, const float* V, const float* O,
                              const float* dO, const float* LSE, const uint32_t* seg,
@@ -253,8 +260,8 @@ attn_status_t attn_fwd_lse(const float* Q, const float* K, const float* V, const
  *   attn_bwd_f16 call records its three: the fp16 copies and the row term,
  *   the key-major pass, the dQ pass; an attn_bwd_decode call its three:
  *   the score-gradient pass, the dK/dV pass, the dq pass; an attn_bwd_short
- *   call its one (the whole backward; with O NULL two: the row term, then
- *   the backward).
+ *   call its one (the whole backward, with the split sums when the heads are
+ *   split; with O NULL two: the row term, then the backward).
  * attn_profile_end: waits for those events, writes into ms[0], ms[1], ms[2]
  *   the summed device time in milliseconds of each of the three passes over
  *   the recorded calls (ms[2] = 0 for calls without the dQ pass), into

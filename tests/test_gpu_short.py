@@ -7,7 +7,11 @@ Covered: the three short workloads whole, with and without O; every padded
 head-dim class (32, 64) with d = 16 .. 64; every mask kind (plain causal,
 documents, arbitrary starts, rows that see no key); lengths 1, 2, ragged
 tails (33, 97, 1000) and the maximum 1024 with several waves' worth of blocks;
-KV groups of 1 .. 8 heads; nonzero initial outputs (+=); repeatability (the
+KV groups of 1 .. 8 heads, with the key blocks' heads split over 1, 2, 4 and 8
+workgroups (the split count follows from the shape: 2 at S=200 with 8 heads
+per group, 4 at S=1024 with 4 (or 8 heads per group over 2 KV heads), 8 at
+S=1024 with 8 heads over one KV head); nonzero initial outputs
+(+=); repeatability (the
 sums have a fixed order, so two calls agree bit for bit); agreement of the O
 and row-term forms; and the size limits (ATTN_ERR_UNSUPPORTED above 1024
 positions or 64 columns).
@@ -35,6 +39,9 @@ SHORT_EDGE = [  # S, H, KV, d, mask
     (1000, 4, 4, 64, "docs"),
     (1024, 8, 2, 32, "causal"),
     (1024, 2, 1, 64, "empty_rows"),
+    (700, 12, 2, 48, "causal"),     # group of 6: two head splits of 3
+    (1024, 16, 2, 64, "docs"),      # group of 8: four head splits
+    (1024, 8, 1, 32, "docs"),       # group of 8: eight head splits
 ]
 
 
