@@ -225,23 +225,33 @@ __device__ __forceinline__ void short_query(const ShortArgs& a, int qb, int h, f
       dp = mfma32(vA[t], oB[t], dp);
     }
     issue(k + 4, kA, vA);  // in flight during the rest of this item
+    // the dQ product's B operands (K from the tile) are read while the
+    // probabilities are formed
+    float kb[ROWTERM ? 1 : 16][NC];
+    if constexpr (!ROWTERM) {
+      __builtin_amdgcn_wave_barrier();  // the wave's K rows are in LDS (in-order LDS)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) kb[r][c] = sK[crow(r, hf) * LDT + l32 + 32 * c];
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int j = j0 + crow(r, hf);
       const bool vis = q_ok && (uint32_t)j >= si && j <= i;
-      const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2)) : 0.f;
+      // computed unconditionally and then selected: a masked entry's value
+      // (possibly inf) is discarded, and the loop stays free of branches
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
+      const float p = vis ? e : 0.f;
       if constexpr (ROWTERM) dsum = fmaf(p, dp[r], dsum);
       else s[r] = p * (dp[r] - Di);  // dS / scale
     }
     if constexpr (!ROWTERM) {
-      __builtin_amdgcn_wave_barrier();  // the wave's K rows are in LDS (in-order LDS)
       // dQ += dS K: A = dS^T registers (lane <-> query), B = K from the tile
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float* kr = sK + crow(r, hf) * LDT + l32;
+      for (int r = 0; r < 16; ++r)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] = mfma32(s[r], kr[32 * c], acc[c]);
-      }
+        for (int c = 0; c < NC; ++c) acc[c] = mfma32(s[r], kb[r][c], acc[c]);
       __builtin_amdgcn_wave_barrier();
     }
   };
@@ -380,23 +390,51 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, i
     }
     issue(k + 4, it);  // in flight during the rest of this item
     __builtin_amdgcn_wave_barrier();  // the item's rows and constants are in LDS
+    // LSE, D and seg of this lane's rows crow(r, hf) = 8 (r / 4) + 4 hf + r % 4:
+    // four consecutive rows per 16-byte read (a row past the end reads the
+    // staged padding, seg = ~0: it sees nothing)
+    float lse[16], dd[16];
+    uint32_t sg[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ii = crow(r, hf), iq = i0 + ii;
-      // a row past the end reads the staged padding (seg = ~0: sees nothing)
-      const bool vis = sSeg[iq] <= (uint32_t)j && j <= iq;
-      const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -sL[ii])) : 0.f;
-      s[r] = p;
-      dp[r] = p * (dp[r] - sD[ii]);  // dS / scale
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int row0 = 8 * a4 + 4 * hf;
+      const float4 l4 = *reinterpret_cast<const float4*>(sL + row0);
+      const float4 d4 = *reinterpret_cast<const float4*>(sD + row0);
+      const uint4 s4 = *reinterpret_cast<const uint4*>(sSeg + i0 + row0);
+      lse[4 * a4] = l4.x; lse[4 * a4 + 1] = l4.y; lse[4 * a4 + 2] = l4.z; lse[4 * a4 + 3] = l4.w;
+      dd[4 * a4] = d4.x; dd[4 * a4 + 1] = d4.y; dd[4 * a4 + 2] = d4.z; dd[4 * a4 + 3] = d4.w;
+      sg[4 * a4] = s4.x; sg[4 * a4 + 1] = s4.y; sg[4 * a4 + 2] = s4.z; sg[4 * a4 + 3] = s4.w;
     }
-    // dV += P^T dO, dK += dS^T Q: A = registers (lane <-> key), B = the tiles
+    // the B operands of the products below, read while the probabilities
+    // are formed
+    float ob[16][NC], qb[16][NC];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ro = crow(r, hf) * LDT + l32;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        accV[c] = mfma32(s[r], sO[ro + 32 * c], accV[c]);
-        accK[c] = mfma32(dp[r], sQ[ro + 32 * c], accK[c]);
+        ob[r][c] = sO[ro + 32 * c];
+        qb[r][c] = sQ[ro + 32 * c];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int iq = i0 + crow(r, hf);
+      const bool vis = sg[r] <= (uint32_t)j && j <= iq;
+      // computed unconditionally and then selected (no branch; a masked
+      // entry's value, possibly inf, is discarded)
+      const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r]));
+      const float p = vis ? e : 0.f;
+      s[r] = p;
+      dp[r] = p * (dp[r] - dd[r]);  // dS / scale
+    }
+    // dV += P^T dO, dK += dS^T Q: A = registers (lane <-> key), B = the tiles
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        accV[c] = mfma32(s[r], ob[r][c], accV[c]);
+        accK[c] = mfma32(dp[r], qb[r][c], accK[c]);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -444,8 +482,8 @@ __device__ __forceinline__ void short_key(const ShortArgs& a, int kb, int kvh, i
 template <int DP, bool ROWTERM>
 __global__ __launch_bounds__(256) void k_short(ShortArgs a) {
   __shared__ __attribute__((aligned(16))) float lds[ShortGeom<DP>::LDS_FLOATS];
-  __shared__ float sRow[4 * 64];
-  __shared__ uint32_t sSeg[SHORT_MAX_S];
+  __shared__ __attribute__((aligned(16))) float sRow[4 * 64];
+  __shared__ __attribute__((aligned(16))) uint32_t sSeg[SHORT_MAX_S];
   const int b = blockIdx.x;
   const int nkey = ROWTERM ? 0 : a.nqb * a.KV * a.ksplit;
   if (b < nkey) {
