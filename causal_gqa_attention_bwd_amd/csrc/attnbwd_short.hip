@@ -18,7 +18,10 @@
 // waves, each of which sums its share in its own accumulators; the four
 // partial sums are then added in wave order through LDS.  Every sum has one
 // writer and a fixed order: deterministic, no atomics.  Without O, a first
-// launch of the query role computes D = sum_j P dP into a workspace.
+// launch of the query role computes D = sum_j P dP into a workspace.  When a
+// KV group's heads are many against the sequence, the key role's heads are
+// split over several workgroups whose partial sums a last launch adds in
+// split order (k_short_sum).
 //
 // Products: v_mfma_f32_32x32x2_f32.  Lane l supplies A[l%32][l/32] and
 // B[l/32][l%32]; register r of the 32x32 result holds row crow(r, l/32),
@@ -55,7 +58,6 @@ struct ShortGeom {
   static constexpr int LDS_FLOATS = 4 * 2 * 32 * LDT;  // two tiles per wave
 };
 
-// Columns hf*HD .. hf*HD + HD - 1 of one row (zero beyond d or when !ok).
 // ---------------------------------------------------------------------------
 // Loads.  Every global read goes through a buffer resource: an offset beyond
 // the buffer (SHORT_OOB) reads zeros, so rows past the end, columns past d
