@@ -267,7 +267,7 @@ def main():
     binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, O, lse, scale)
     ws_bytes, stored = binding.bwd_plan(w.S, w.H, w.KV, w.d)
     dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
-    f16_ws = (4 * w.H + 3 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + w.S * w.H * 4
+    f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + w.S * w.H * 4
     if args.f16:
         log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
     else:

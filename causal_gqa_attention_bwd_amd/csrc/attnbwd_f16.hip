@@ -10,17 +10,15 @@
 //
 // Per call:
 //   k_prep    per 32-row query block seg min / max (shared with attn_bwd).
-//   k_cvt16   fp16 copies of Q, dO, K, V as head-major row tiles [head][Sp][DP],
-//             and d-major copies of Q, dO, K [head][DP][Sp] for the products
-//             that contract over rows.  Sp = S rounded up to 128, DP = head_dim
-//             rounded up to a tile width; padding is zero.
+//   k_cvt16   fp16 copies of Q, dO, K, V as head-major row tiles [head][Sp][DP]
+//             (Sp = S rounded up to 128, DP = head_dim rounded up to a tile
+//             width; padding is zero).
 //   D         k_rowdot (D = dO . O) when the forward output is given, else
 //             k_q16<D only>: S^T and dP^T of every visible pair, D = sum P dP.
-//   k_kv16    key-major, one workgroup per (64-key tile, KV head), owns its
-//             dK / dV rows and sums the group's heads; a wave pair per 32-key
-//             block: role 0 forms S = Q K^T, P, and dV += P^T dO; role 1 forms
-//             dP = dO V^T, dS from P (handed over through LDS), and
-//             dK += dS^T Q.  4 products per visible pair.
+//   k_kv16    key-major, one workgroup per (128-key tile, KV head, head
+//             split, column part), owns its dK / dV rows and sums its heads:
+//             S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q.  4
+//             products per visible pair.
 //   k_q16     query-major, one workgroup per (128-query tile, head): S^T, dP^T,
 //             dS, dQ += dS K.  3 products per visible pair.
 // Executed products per visible pair: 7 with the forward output, 9 without
@@ -32,9 +30,9 @@
 // product (register r: row crow(r, l/32), column l%32).  Registers 8s..8s+7 of
 // an accumulator tile, rounded to fp16, are therefore the A operand of a
 // product that contracts over the tile's rows, taken in the row order
-// crow(8s + j, hf).  The d-major copies store every 16-row group in that order
-// (rows 4..7 and 8..11 swapped, tpos), so the matching B operand is one
-// 16-byte read per lane.
+// crow(8s + j, hf).  The matching B operand (those rows, one column per lane)
+// comes from the staged row tile through two transposing LDS loads
+// (tr_operand below), so no transposed copy of any tensor is made.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -61,22 +59,47 @@ __device__ __forceinline__ h8 pack8(const f32x16& c, int s) {
   return __builtin_convertvector(v, h8);
 }
 
-// Position of row q of a 32-row block inside the d-major copies (and the row
-// at position q): bits 2 and 3 swapped, so that positions 8hf + j of a 16-row
-// group hold rows crow(j, hf).
-__device__ __forceinline__ int tpos(int q) { return (q & ~12) | ((q & 4) << 1) | ((q >> 1) & 4); }
+// The B operand of a 32x32x16 product -- lane l supplies B[8 (l/32) + j]
+// [l%32], j = 0..7 -- read straight from a row-major Tile16 (its rows are
+// the contraction index, 8 columns per 16-byte chunk) by two transposing LDS
+// loads (ds_read_b64_tr_b16).  Within each group of 16 lanes such a load
+// hands lane i, as element j, the (i mod 4)-th 16-bit value of the 8 bytes
+// that lane 4j + i/4 of the group addressed (checked on the device).  So
+// lane L = 4a + b of group G addresses row r + a, columns n0 + 16 (G % 2) +
+// 4b .. + 3, and receives column n0 + 16 (G % 2) + L = n0 + l%32 of rows
+// r .. r + 3.  The caller gives the first tile row of each load (row_c0 for
+// j = 0..3, row_c1 for j = 4..7), for the rows of its lane's half-wave.
+typedef short s4v __attribute__((__vector_size__(8)));
+typedef short s8v __attribute__((ext_vector_type(8)));
+template <class T>
+__device__ __forceinline__ h8 tr_operand(const char* tile, int row_c0, int row_c1, int n0, int lane) {
+  const int L = lane & 15, G = lane >> 4;
+  const int col = n0 + 16 * (G & 1) + 4 * (L & 3);
+  const uint32_t sub = (uint32_t)(col & 7) * 2u;  // 0 or 8 bytes into the 16-byte chunk
+  const char* p0 = tile + T::at(row_c0 + (L >> 2), col >> 3) + sub;
+  const char* p1 = tile + T::at(row_c1 + (L >> 2), col >> 3) + sub;
+  const s4v x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)p0);
+  const s4v y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4v*)p1);
+  const s8v v = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return __builtin_bit_cast(h8, v);
+}
 
 // ---------------------------------------------------------------------------
 // fp16 tiles in LDS: ROWS x CH chunks of 16 bytes, unpadded; chunk c of row r
-// sits at chunk r*CH + (c ^ swz(r)).  The swizzle makes the 16-byte reads of
-// 8 (and of 16) consecutive rows at one chunk hit distinct banks for every CH
-// used here (4, 8, 12, 16, 24, 32), and keeps c ^ swz(r) below CH.
+// sits at chunk r*CH + (c ^ swz(r)).  Two reads meet these tiles: 16-byte
+// reads of 8 (and 16) consecutive rows at one chunk (the row operands), and
+// the transposing 8-byte reads of 4 consecutive rows at 4 adjacent chunks
+// (tr_operand; 2 chunks per 16 lanes).  The swizzle, a linear map of the row's
+// low four bits (b0..b3), was found by exhaustive search to make both hit
+// distinct banks, counting 64 banks (16 chunk slots) and 32 (8 chunk slots),
+// for every CH used here (4, 8, 12, 16, 24, 32), and keeps c ^ swz(r) < CH.
 // ---------------------------------------------------------------------------
 template <int CH>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (CH % 8 != 0) return ((r >> 1) ^ (r >> 2)) & 3;
-  else if constexpr (CH % 16 != 0) return (r ^ (r >> 3)) & 7;
-  else return (r ^ (r >> 4)) & 15;
+  const int b0 = r & 1, b1 = (r >> 1) & 1, b2 = (r >> 2) & 1, b3 = (r >> 3) & 1;
+  if constexpr (CH % 8 != 0) return (b1 << 1) ^ b2 ^ (b3 << 1);
+  else if constexpr (CH % 16 != 0) return (b0 << 1) ^ (b1 << 2) ^ b2 ^ (b3 << 1);
+  else return (b0 << 2) ^ (b1 * 10) ^ b2 ^ (b3 << 1);
 }
 
 template <int ROWS, int CH>
@@ -126,7 +149,6 @@ __device__ __forceinline__ void wait_vm() {
 
 struct F16Args {
   const _Float16 *Qh, *dOh, *Kh, *Vh;  // [heads][Sp][DP] row tiles
-  const _Float16 *QT, *dOT, *KT;       // [heads][DP][Sp], each 32-row block in tpos order
   const float* LSE;                    // [S, H]
   const uint32_t* seg;                 // [S], NULL = all zeros
   float *dQ, *dK, *dV;
@@ -141,18 +163,17 @@ struct F16Args {
 
 struct CvtArgs {
   const float *Q, *dO, *K, *V;
-  _Float16 *Qh, *dOh, *Kh, *Vh, *QT, *dOT, *KT;
+  _Float16 *Qh, *dOh, *Kh, *Vh;
   int S, Sp, H, KV, d;
 };
 
 // ---------------------------------------------------------------------------
 // k_cvt16: one workgroup per (32-row block, head) of one tensor; blocks
 // [0, nb*H) convert Q, then dO, then K (nb*KV), then V.  Rows past S and
-// columns past head_dim become zeros.  V needs no d-major copy.
+// columns past head_dim become zeros.
 // ---------------------------------------------------------------------------
 template <int DP>
 __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
-  __shared__ _Float16 sT[DP][34];  // d-major staging of the block (positions tpos)
   const int nb = a.Sp / 32;
   const long long nq = (long long)nb * a.H, nk = (long long)nb * a.KV;
   long long b = blockIdx.x;
@@ -166,7 +187,6 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
   const int r0 = (int)(b / heads) * 32;
   const float* src = which == 0 ? a.Q : which == 1 ? a.dO : which == 2 ? a.K : a.V;
   _Float16* dst = which == 0 ? a.Qh : which == 1 ? a.dOh : which == 2 ? a.Kh : a.Vh;
-  _Float16* dstT = which == 0 ? a.QT : which == 1 ? a.dOT : which == 2 ? a.KT : nullptr;
   const size_t stride = (size_t)heads * a.d;
   for (int i = threadIdx.x; i < 32 * (DP / 2); i += 256) {
     const int r = i / (DP / 2), c = 2 * (i % (DP / 2));
@@ -174,20 +194,7 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
     f32x2 v = {0.f, 0.f};
     if (s < a.S && c < a.d)
       v = *reinterpret_cast<const f32x2*>(src + (size_t)s * stride + (size_t)head * a.d + c);
-    const h2 hv = __builtin_convertvector(v, h2);
-    *reinterpret_cast<h2*>(dst + ((size_t)head * a.Sp + s) * DP + c) = hv;
-    if (dstT) {
-      sT[c][tpos(r)] = hv[0];
-      sT[c + 1][tpos(r)] = hv[1];
-    }
-  }
-  if (dstT) {  // the same for the whole workgroup
-    __syncthreads();
-    for (int i = threadIdx.x; i < DP * 16; i += 256) {
-      const int c = i / 16, p = 2 * (i % 16);
-      const h2 hv = {sT[c][p], sT[c][p + 1]};
-      *reinterpret_cast<h2*>(dstT + ((size_t)head * DP + c) * a.Sp + r0 + p) = hv;
-    }
+    *reinterpret_cast<h2*>(dst + ((size_t)head * a.Sp + s) * DP + c) = __builtin_convertvector(v, h2);
   }
 }
 
@@ -200,17 +207,17 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
 // of query l%32, so each lane's LSE, D and seg are one value.
 //   DONLY: D[q] = sum_j P dP (the row term, for the key-major pass).
 //   else:  dQ += dS K with dS = scale P (dP - D), A operand straight from the
-//          dS registers, B from the K^T tile; the accumulators stay in AGPRs.
+//          dS registers, B from the K row tile by transposing loads; the
+//          accumulators stay in AGPRs.
 // ---------------------------------------------------------------------------
 template <int DP, bool DONLY>
 struct QGeom {
   using RT = Tile16<32, DP / 8>;
-  using TT = Tile16<DP, 4>;
-  static constexpr int STAGE = 2 * RT::BYTES + (DONLY ? 0 : TT::BYTES);
+  static constexpr int STAGE = 2 * RT::BYTES;
   // two workgroups per CU up to 128 columns, one above
   static constexpr int BUDGET = DP <= 128 ? 72 * 1024 : 150 * 1024;
   static constexpr int NBUF = 4 * STAGE <= BUDGET ? 4 : 3 * STAGE <= BUDGET ? 3 : 2;
-  static constexpr int LPS = 2 * RT::CPW + (DONLY ? 0 : TT::CPW);  // loads per wave per block
+  static constexpr int LPS = 2 * RT::CPW;  // loads per wave per block
   static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
 
@@ -218,7 +225,6 @@ template <int DP, bool DONLY>
 __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
   using G = QGeom<DP, DONLY>;
   using RT = typename G::RT;
-  using TT = typename G::TT;
   constexpr int NT = DP / 16;  // k-steps of the d-contractions
   constexpr int NO = DP / 32;  // 32-column output tiles
   constexpr int NBUF = G::NBUF, STAGE = G::STAGE;
@@ -235,8 +241,6 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
   const uint32_t smem0 = lds_addr(smem);
   Loader16<32, DP / 8> ldr;
   ldr.init(DP * 2, wave, lane);
-  Loader16<DP, 4> ldt;
-  if constexpr (!DONLY) ldt.init((uint32_t)a.Sp * 2u, wave, lane);
 
   auto tile = [&](const int qt) __attribute__((always_inline)) {
     const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
@@ -278,10 +282,6 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
       const size_t roff = ((size_t)kvh * a.Sp + (size_t)kb * 32) * DP;
       ldr.load(buf_rsrc(a.Kh + roff, 32 * DP * 2), st, wave);
       ldr.load(buf_rsrc(a.Vh + roff, 32 * DP * 2), st + RT::BYTES, wave);
-      if constexpr (!DONLY)
-        ldt.load(buf_rsrc(a.KT + (size_t)kvh * DP * a.Sp + (size_t)kb * 32,
-                          (uint32_t)(((size_t)(DP - 1) * a.Sp + 32) * 2)),
-                 st + 2 * RT::BYTES, wave);
     };
 
     f32x16 acc[NO];
@@ -313,14 +313,19 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
         else s[r] = p * (dp[r] - Dq) * a.scale;
       }
       if constexpr (!DONLY) {
+        // B operands from the K row tile (transposing loads): the k order of
+        // a0 is keys crow(j, hf), j = 0..7 (rows 4 hf .. 4 hf + 3, then 8 +
+        // 4 hf ..), of a1 the same plus 16
         const h8 a0 = pack8(s, 0), a1 = pack8(s, 1);
-        const char* kt = st + 2 * RT::BYTES;
 #pragma unroll
         for (int o = 0; o < NO; ++o) {
-          const int row = 32 * o + l32;
-          acc[o] = mfma16(a0, *reinterpret_cast<const h8*>(kt + TT::at(row, hf)), acc[o]);
-          acc[o] = mfma16(a1, *reinterpret_cast<const h8*>(kt + TT::at(row, 2 + hf)), acc[o]);
-          asm volatile("" : "+a"(acc[o]));
+          const h8 k0 = tr_operand<RT>(st, 4 * hf, 8 + 4 * hf, 32 * o, lane);
+          const h8 k1 = tr_operand<RT>(st, 16 + 4 * hf, 24 + 4 * hf, 32 * o, lane);
+          acc[o] = mfma16(a0, k0, acc[o]);
+          acc[o] = mfma16(a1, k1, acc[o]);
+          // the next tile's operand loads stay behind this point: hoisting
+          // them all would not fit two waves' registers per SIMD
+          asm volatile("" : "+a"(acc[o])::"memory");
         }
       }
     };
@@ -382,11 +387,11 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
 // column part).  Wave w owns key block w (keys j0 + 32w + l%32) and holds its
 // K and V rows in registers as the B operands of S = Q K^T and dP = dO V^T.
 // Per visible 32-row query block and head of the split's share of the group,
-// the Q and dO row tiles, the part's columns of their d-major tiles, and the
-// rows' LSE, D and seg stream through an LDS ring of NBUF stages (NBUF - 1
-// steps in flight), shared by the four waves.  Each wave forms P and
-// dS = scale P (dP - D) in registers and accumulates dV += P^T dO and
-// dK += dS^T Q over its part's output columns.  Above 128 columns the output
+// the Q and dO row tiles and the rows' LSE, D and seg stream through an LDS
+// ring of NBUF stages (NBUF - 1 steps in flight), shared by the four waves.
+// Each wave forms P and dS = scale P (dP - D) in registers and accumulates
+// dV += P^T dO and dK += dS^T Q over its part's output columns, with the B
+// operands read from the same row tiles by transposing loads.  Above 128 columns the output
 // columns come in two parts, one workgroup each (both form S and dP), so that
 // a wave's accumulators fit the register file.  The visible query blocks of
 // the tile (blk_min <= last key, at or after the diagonal) come from 64-block
@@ -401,13 +406,11 @@ struct KvGeom {
   static constexpr int DW = DP / NC;           // output columns per part
   static constexpr int NOW = DW / 32;          // 32-column output tiles per part
   using RT = Tile16<32, DP / 8>;
-  using TT = Tile16<DW, 4>;
-  static constexpr int OFF_DO = RT::BYTES, OFF_QT = 2 * RT::BYTES;
-  static constexpr int OFF_DOT = 2 * RT::BYTES + TT::BYTES;
-  static constexpr int OFF_ROW = 2 * RT::BYTES + 2 * TT::BYTES;  // LSE, D, seg, spare (256 B each)
+  static constexpr int OFF_DO = RT::BYTES;
+  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE, D, seg, spare (256 B each)
   static constexpr int STAGE = OFF_ROW + 4 * 256;
   static constexpr int NBUF = 4 * STAGE <= 150 * 1024 ? 4 : 3 * STAGE <= 150 * 1024 ? 3 : 2;
-  static constexpr int LPS = 2 * RT::CPW + 2 * TT::CPW + 1;  // loads per wave per step
+  static constexpr int LPS = 2 * RT::CPW + 1;  // loads per wave per step
   static_assert(DW % 32 == 0, "whole output tiles per part");
   static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
@@ -416,7 +419,6 @@ template <int DP>
 __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
   using G = KvGeom<DP>;
   using RT = typename G::RT;
-  using TT = typename G::TT;
   constexpr int NT = DP / 16, NOW = G::NOW, NBUF = G::NBUF, STAGE = G::STAGE;
   __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
 
@@ -436,8 +438,6 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
   const uint32_t smem0 = lds_addr(smem);
   Loader16<32, DP / 8> ldr;
   ldr.init(DP * 2, wave, lane);
-  Loader16<G::DW, 4> ldt;
-  ldt.init((uint32_t)a.Sp * 2u, wave, lane);
 
   auto tile = [&](const int kt) __attribute__((always_inline)) {
     const int j0 = kt * 128;
@@ -499,10 +499,6 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       const size_t roff = ((size_t)head * a.Sp + (size_t)qb * 32) * DP;
       ldr.load(buf_rsrc(a.Qh + roff, 32 * DP * 2), st, wave);
       ldr.load(buf_rsrc(a.dOh + roff, 32 * DP * 2), st + G::OFF_DO, wave);
-      const size_t toff = ((size_t)head * DP + (size_t)cpart * G::DW) * a.Sp + (size_t)qb * 32;
-      const uint32_t tbytes = (uint32_t)(((size_t)(G::DW - 1) * a.Sp + 32) * 2);
-      ldt.load(buf_rsrc(a.QT + toff, tbytes), st + G::OFF_QT, wave);
-      ldt.load(buf_rsrc(a.dOT + toff, tbytes), st + G::OFF_DOT, wave);
       // LSE, D and seg of the block's rows (lanes 0..31; the rest, and wave 3's
       // spare load, deposit zeros)
       const int rows = min(32, S - qb * 32);
@@ -553,14 +549,20 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         dp[r] = p * (dp[r] - dv[r]) * a.scale;
       }
       const h8 p0 = pack8(s, 0), p1 = pack8(s, 1), d0 = pack8(dp, 0), d1 = pack8(dp, 1);
+      // B operands from the Q and dO row tiles (transposing loads): the k
+      // order of p0 / d0 is queries crow(j, hf), j = 0..7, i.e. rows 4 hf ..
+      // 4 hf + 3 then 8 + 4 hf .. ; of p1 / d1 the same plus 16
 #pragma unroll
       for (int o = 0; o < NOW; ++o) {
-        const int row = 32 * o + l32;
-        const uint32_t c0 = TT::at(row, hf), c1 = TT::at(row, 2 + hf);
-        accV[o] = mfma16(p0, *reinterpret_cast<const h8*>(st + G::OFF_DOT + c0), accV[o]);
-        accV[o] = mfma16(p1, *reinterpret_cast<const h8*>(st + G::OFF_DOT + c1), accV[o]);
-        accK[o] = mfma16(d0, *reinterpret_cast<const h8*>(st + G::OFF_QT + c0), accK[o]);
-        accK[o] = mfma16(d1, *reinterpret_cast<const h8*>(st + G::OFF_QT + c1), accK[o]);
+        const int n0 = cpart * G::DW + 32 * o;
+        const h8 ov0 = tr_operand<RT>(st + G::OFF_DO, 4 * hf, 8 + 4 * hf, n0, lane);
+        const h8 ov1 = tr_operand<RT>(st + G::OFF_DO, 16 + 4 * hf, 24 + 4 * hf, n0, lane);
+        const h8 qv0 = tr_operand<RT>(st, 4 * hf, 8 + 4 * hf, n0, lane);
+        const h8 qv1 = tr_operand<RT>(st, 16 + 4 * hf, 24 + 4 * hf, n0, lane);
+        accV[o] = mfma16(p0, ov0, accV[o]);
+        accV[o] = mfma16(p1, ov1, accV[o]);
+        accK[o] = mfma16(d0, qv0, accK[o]);
+        accK[o] = mfma16(d1, qv1, accK[o]);
         asm volatile("" : "+a"(accK[o]), "+a"(accV[o]));
       }
     };
@@ -726,9 +728,6 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   if (seq_len == 0) return ATTN_OK;
   const int dp = padded_dim(head_dim);
   const long long Sp = ((long long)seq_len + 127) / 128 * 128;
-  // byte offsets inside one d-major tile must fit the 32-bit buffer offsets
-  if ((long long)dp * Sp * 2 >= (1ll << 31))
-    return fail(ATTN_ERR_UNSUPPORTED, "seq_len = %d is too long for head_dim = %d", seq_len, head_dim);
 
   const long long nblk = ((long long)seq_len + 31) / 32;
   const size_t qbytes = (size_t)n_heads * Sp * dp * 2, kbytes = (size_t)n_kv_heads * Sp * dp * 2;
@@ -737,10 +736,10 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   const size_t off_min = off; off += align256((size_t)nblk * 4);
   const size_t off_max = off; off += align256((size_t)nblk * 4);
   const size_t off_slot = off; off += align256((size_t)(nblk + 1) * 8);
-  size_t off_x[7];  // Qh, dOh, QT, dOT, Kh, Vh, KT
-  for (int i = 0; i < 7; ++i) {
+  size_t off_x[4];  // Qh, dOh, Kh, Vh
+  for (int i = 0; i < 4; ++i) {
     off_x[i] = off;
-    off += align256(i < 4 ? qbytes : kbytes);
+    off += align256(i < 2 ? qbytes : kbytes);
   }
   // k_kv16 splits a group's heads over workgroups until the grid has ~1024 of
   // them (or the group cannot be split further); several splits add their
@@ -765,8 +764,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   auto half_at = [&](int i) { return reinterpret_cast<_Float16*>(w + off_x[i]); };
 
   F16Args f;
-  f.Qh = half_at(0); f.dOh = half_at(1); f.QT = half_at(2); f.dOT = half_at(3);
-  f.Kh = half_at(4); f.Vh = half_at(5); f.KT = half_at(6);
+  f.Qh = half_at(0); f.dOh = half_at(1); f.Kh = half_at(2); f.Vh = half_at(3);
   f.LSE = LSE; f.seg = seg; f.dQ = dQ; f.dK = dK; f.dV = dV;
   f.D = reinterpret_cast<float*>(w + off_D);
   f.blk_min = reinterpret_cast<const uint32_t*>(w + off_min);
@@ -776,8 +774,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   f.part = splits > 1 ? reinterpret_cast<float*>(w + off_part) : nullptr;
   CvtArgs c;
   c.Q = Q; c.dO = dO; c.K = K; c.V = V;
-  c.Qh = half_at(0); c.dOh = half_at(1); c.QT = half_at(2); c.dOT = half_at(3);
-  c.Kh = half_at(4); c.Vh = half_at(5); c.KT = half_at(6);
+  c.Qh = half_at(0); c.dOh = half_at(1); c.Kh = half_at(2); c.Vh = half_at(3);
   c.S = seq_len; c.Sp = (int)Sp; c.H = n_heads; c.KV = n_kv_heads; c.d = head_dim;
 
   rc = launch_prep(seg, seq_len, reinterpret_cast<uint32_t*>(w + off_min),

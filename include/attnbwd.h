@@ -152,16 +152,16 @@ attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, cons
  *
  * O is the forward output, as for attn_bwd_o, or NULL: the row term is then
  * computed by an extra pass over the scores.  Arguments, layouts, +=
- * semantics and errors as attn_bwd, plus ATTN_ERR_UNSUPPORTED when
- * Sp * DP * 2 >= 2^31, with Sp = seq_len rounded up to 128 and DP = head_dim
- * rounded up to 32, 64, 96, 128, 192 or 256.  Workspace (same private pool):
- * fp16 copies of Q, dO and K in two layouts each and of V,
- * (4 * n_heads + 3 * n_kv_heads) * Sp * DP * 2 bytes; the row term and block
+ * semantics and errors as attn_bwd.  Workspace (same private pool): fp16
+ * row-tile copies of Q, dO, K and V, (2 * n_heads + 2 * n_kv_heads) * Sp *
+ * DP * 2 bytes, with Sp = seq_len rounded up to 128 and DP = head_dim rounded
+ * up to 32, 64, 96, 128, 192 or 256 (the products that contract over rows
+ * read these tiles through transposing LDS loads); the row term and block
  * metadata; and, when the key-major pass splits each KV group's heads over
  * `splits` workgroups (a power of two dividing n_heads / n_kv_heads, chosen
  * to give about 1024 workgroups), 2 * splits * seq_len * n_kv_heads *
  * head_dim * 4 bytes of partial dK, dV sums, added in split order (the result
- * does not depend on the schedule).  0.29 GiB at seq_len 4096, 32 heads,
+ * does not depend on the schedule).  0.20 GiB at seq_len 4096, 32 heads,
  * 8 KV heads, head_dim 128 (4 splits).
  */
 attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
