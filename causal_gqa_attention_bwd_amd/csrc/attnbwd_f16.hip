@@ -741,15 +741,26 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
     off_x[i] = off;
     off += align256(i < 2 ? qbytes : kbytes);
   }
-  // k_kv16 splits a group's heads over workgroups until the grid has ~1024 of
-  // them (or the group cannot be split further); several splits add their
-  // partial dK, dV through a workspace slice each
+  // k_kv16 splits a group's heads over workgroups (partial dK, dV through a
+  // workspace slice each, added by k_sumparts).  Paired tiles (plain causal)
+  // carry equal work, so the splits stop at one round of resident workgroups
+  // (one per CU, two up to 64 columns): more rounds only add partial sums.
+  // Under a document mask the key tiles' work differs widely, and the splits
+  // go on to ~1024 workgroups, which balance it (measured at S=4096 and S=16384)
   const bool pair = seg == nullptr && pairing_enabled();
   const int g = n_heads / n_kv_heads;
   const int nkt = (seq_len + 127) / 128;
   const long long kv_blocks = (long long)(pair ? (nkt + 1) / 2 : nkt) * n_kv_heads;
+  long long target = 1024;
+  if (pair) {
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      ncu = 256;
+    target = (long long)ncu * (dp <= 64 ? 2 : 1);
+  }
   int splits = 1;
-  while (kv_blocks * splits < 1024 && g % (2 * splits) == 0) splits *= 2;
+  while (kv_blocks * splits < target && g % (2 * splits) == 0) splits *= 2;
   const size_t off_part = off;
   if (splits > 1) off += align256((size_t)2 * splits * seq_len * n_kv_heads * head_dim * 4);
 

@@ -159,10 +159,11 @@ attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, cons
  * read these tiles through transposing LDS loads); the row term and block
  * metadata; and, when the key-major pass splits each KV group's heads over
  * `splits` workgroups (a power of two dividing n_heads / n_kv_heads, chosen
- * to give about 1024 workgroups), 2 * splits * seq_len * n_kv_heads *
+ * from the shape: one round of resident workgroups for plain causal calls,
+ * about 1024 workgroups under a document mask), 2 * splits * seq_len * n_kv_heads *
  * head_dim * 4 bytes of partial dK, dV sums, added in split order (the result
- * does not depend on the schedule).  0.20 GiB at seq_len 4096, 32 heads,
- * 8 KV heads, head_dim 128 (4 splits).
+ * does not depend on the schedule).  0.14 GiB at seq_len 4096, 32 heads,
+ * 8 KV heads, head_dim 128, plain causal (2 splits).
  */
 attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
                            const float* dO, const float* LSE, const uint32_t* seg,
