@@ -158,6 +158,7 @@ struct F16Args {
   float scale;
   int pair;                            // 1: block p serves tiles p and n-1-p (plain causal)
   int splits;                          // k_kv16: workgroups sharing one key tile's heads
+  int kv_work;                         // k_kv16: (key tile, KV head, split) triples
   float* part;                         // [2 * splits][S, KV, d] partial dK, dV (splits > 1)
 };
 
@@ -427,12 +428,22 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
   const int hf = lane >> 5, l32 = lane & 31;
   const int S = a.S, H = a.H, KV = a.KV;
   const int g = H / KV, gs = g / a.splits;  // heads of the group per split
-  int b = (int)blockIdx.x;
+  // grid position -> (KV head, column part, split, first key tile).  With two
+  // column parts, those of one (tile, KV head, split) run 8 blocks apart:
+  // blocks are dispatched round-robin over the 8 XCDs, so both land on the
+  // same XCD at about the same time, and the second finds the Q and dO
+  // tiles the first brought into that XCD's L2.  (The grid is then padded
+  // to a multiple of 16 blocks; the padding exits here.)
+  int b = (int)blockIdx.x, cpart = 0;
+  if constexpr (G::NC == 2) {
+    cpart = (b >> 3) & 1;
+    b = ((b >> 4) << 3) | (b & 7);
+    if (b >= a.kv_work) return;
+  }
   const int kvh = b % KV;
   b /= KV;
-  const int cpart = b % G::NC;
-  b /= G::NC;
   const int split = b % a.splits;
+  const int first_tile = b / a.splits;
   const int nblk = (S + 31) / 32;
   const float sc2 = a.scale * ATTN_LOG2E;
   const uint32_t smem0 = lds_addr(smem);
@@ -645,7 +656,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
     }
   };
   // low key tiles (most queries) first; paired: then the mirror tile
-  const int first = (int)(blockIdx.x / (KV * G::NC * a.splits));
+  const int first = first_tile;
   const int second = mirror_tile(first, (S + 127) / 128, a.pair);
   tile(first);
   if (second >= 0) tile(second);
@@ -694,8 +705,8 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
-  hipLaunchKernelGGL(k_kv16<DP>, dim3(blocks((f.S + 127) / 128) * f.KV * KvGeom<DP>::NC * f.splits),
-                     dim3(256), 0, st, f);
+  const int kv_grid = KvGeom<DP>::NC == 2 ? (f.kv_work + 7) / 8 * 16 : f.kv_work;
+  hipLaunchKernelGGL(k_kv16<DP>, dim3(kv_grid), dim3(256), 0, st, f);
   rc = hip_check(hipGetLastError(), "launching k_kv16");
   if (rc == ATTN_OK && f.splits > 1) {
     const long long n = (long long)f.S * f.KV * f.d;
@@ -782,6 +793,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   f.S = seq_len; f.Sp = (int)Sp; f.H = n_heads; f.KV = n_kv_heads; f.d = head_dim; f.scale = scale;
   f.pair = pair;
   f.splits = splits;
+  f.kv_work = (int)(kv_blocks * splits);
   f.part = splits > 1 ? reinterpret_cast<float*>(w + off_part) : nullptr;
   CvtArgs c;
   c.Q = Q; c.dO = dO; c.K = K; c.V = V;
