@@ -378,6 +378,11 @@ def main():
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
                    "head_dim": w.d, "mask": "causal" if seg is None else "documents",
                    "valid_pairs": npairs, "credited_flops_per_step": flops,
+                   # the same time counted on all causal pairs (labelled; differs from value
+                   # only under a document mask)
+                   "tflops_on_causal_pairs": round(
+                       10.0 * w.d * w.H * (w.S * (w.S + 1) // 2) / (ms_step * 1e-3) / 1e12, 3),
+                   "device_compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
                    "entry": ("attn_bwd_short" if args.short else
                              "attn_bwd_f16" if args.f16 else "attn_bwd_rope" if args.rope else
                              "attn_bwd_o" if args.o_entry else "attn_bwd"),
