@@ -44,6 +44,8 @@
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
@@ -189,13 +191,14 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
   const float* src = which == 0 ? a.Q : which == 1 ? a.dO : which == 2 ? a.K : a.V;
   _Float16* dst = which == 0 ? a.Qh : which == 1 ? a.dOh : which == 2 ? a.Kh : a.Vh;
   const size_t stride = (size_t)heads * a.d;
-  for (int i = threadIdx.x; i < 32 * (DP / 2); i += 256) {
-    const int r = i / (DP / 2), c = 2 * (i % (DP / 2));
+  // 4 columns per thread: 16-byte reads, 8-byte writes (head_dim is a multiple of 16)
+  for (int i = threadIdx.x; i < 32 * (DP / 4); i += 256) {
+    const int r = i / (DP / 4), c = 4 * (i % (DP / 4));
     const int s = r0 + r;
-    f32x2 v = {0.f, 0.f};
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (s < a.S && c < a.d)
-      v = *reinterpret_cast<const f32x2*>(src + (size_t)s * stride + (size_t)head * a.d + c);
-    *reinterpret_cast<h2*>(dst + ((size_t)head * a.Sp + s) * DP + c) = __builtin_convertvector(v, h2);
+      v = *reinterpret_cast<const f32x4*>(src + (size_t)s * stride + (size_t)head * a.d + c);
+    *reinterpret_cast<h4*>(dst + ((size_t)head * a.Sp + s) * DP + c) = __builtin_convertvector(v, h4);
   }
 }
 
