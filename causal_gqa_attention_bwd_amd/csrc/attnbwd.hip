@@ -980,8 +980,11 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   const int S = a.S, H = a.H, KV = a.KV, d = a.d;
   const int g = H / KV;
   const int kvh = blockIdx.x % KV;
+  const int nkt = (S + BC - 1) / BC;
   auto tile = [&](const int kt) __attribute__((always_inline)) {
   const int j0 = kt * BC;
+  // paired: the upper half of the key tiles sweeps the query tiles upwards
+  const bool up = a.pair && 2 * kt > nkt - 1;
   const int kblk = kt * KB + kb;  // this wave's key block
   const int head0 = kvh * g;
   const size_t qstride = (size_t)H * d, kstride = (size_t)KV * d;
@@ -995,16 +998,18 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   // query tiles that can see these keys: [qt_lo, qt_hi]
   const int qt_lo = j0 / BR, qt_hi = (S - 1) / BR;
 
-  // segment of tiles top, top-1, ..., top-63 (lane i <-> tile top - i):
-  // the mask of tiles with a visible pair, and this lane's slot base of the
-  // wave's (query block, key block) pair (-1: no visible key in the pair)
-  int seg_top = qt_hi, sbv = -1;
+  // segment of 64 tiles in sweep order, from base (lane i <-> tile base - i
+  // downwards, base + i upwards): the mask of tiles with a visible pair, and
+  // this lane's slot base of the wave's (query block, key block) pair (-1: no
+  // visible key in the pair)
+  int seg = up ? qt_lo : qt_hi, sbv = -1;
   uint64_t mask = 0;
-  auto build = [&](int top) {
-    const int t = top - lane;
+  auto tile_of = [&](int base, int i) { return up ? base + i : base - i; };
+  auto build = [&](int base) {
+    const int t = tile_of(base, lane);
     bool vis = false;
     int sb = -1;
-    if (t >= qt_lo) {
+    if (t >= qt_lo && t <= qt_hi) {
       uint32_t mn = 0xffffffffu, mine = 0xffffffffu;
 #pragma unroll
       for (int b = 0; b < QS; ++b) {
@@ -1028,9 +1033,9 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
     hh = 0;
     uint64_t rest = li < 0 ? mask : (li >= 63 ? 0ull : mask & (~0ull << (li + 1)));
     while (rest == 0) {
-      seg_top -= 64;
-      if (seg_top < qt_lo) return false;
-      build(seg_top);
+      seg = tile_of(seg, 64);
+      if (seg < qt_lo || seg > qt_hi) return false;
+      build(seg);
       rest = mask;
     }
     li = __builtin_ctzll(rest);
@@ -1066,11 +1071,11 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
     }
   };
 
-  build(seg_top);
+  build(seg);
   int li = -1, hh = g - 1, buf = 0, cslot = -1;
   bool has = advance(li, hh);
   if (has) {
-    const int t = seg_top - li;
+    const int t = tile_of(seg, li);
     const i32x4 rq = ld.rsrc(a.Q + (size_t)(head0 + hh) * d, t * BR, S, qstride, d, true);
     const i32x4 rg = ld.rsrc(a.dO + (size_t)(head0 + hh) * d, t * BR, S, qstride, d, true);
     ld.load_all(rq, lds_qg, wave);
@@ -1095,7 +1100,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
     // the next item: its stored tiles into registers, its Q/dO/D rows into
     // the other buffers (issued between the dV products below)
     const bool more = advance(li, hh);
-    const int nt = more ? seg_top - li : 0;
+    const int nt = more ? tile_of(seg, li) : 0;
     const int nslot = more ? item_slot(li, hh) : -1;
     fetch_tiles(nslot);
     const int nh = head0 + (more ? hh : 0);
@@ -1231,8 +1236,16 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   }
   }  // qs == 0
   };
-  // low key tiles (most queries) first; paired: then the mirror tile
-  const int first = (int)(blockIdx.x / KV), second = mirror_tile(first, (S + BC - 1) / BC, a.pair);
+  // Low key tiles (most queries) first, sweeping the query tiles downwards:
+  // the blocks of one KV head start together, so they all read the same
+  // query tile at the same time.  Paired, the mirror tile follows and is
+  // swept upwards: of n key tiles, mirror n-1-k starts after the n-k query
+  // tiles of tile k, at its own lowest query tile, so all blocks are then at
+  // query tile t-1 at time t and their Q and dO reads share L2 again
+  // (downwards they would spread over all tiles).  Unpaired (documents), a
+  // block's tile lies inside one document and the blocks of a document
+  // start together, so downwards is kept.
+  const int first = (int)(blockIdx.x / KV), second = mirror_tile(first, nkt, a.pair);
   tile(first);
   if (second >= 0) {
     __syncthreads();  // the first tile is done with the LDS

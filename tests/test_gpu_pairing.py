@@ -1,12 +1,16 @@
 """GPU tests of the paired schedule of plain causal calls (seg = NULL).
 
 With a plain causal mask every workgroup serves a tile and its mirror
-(n - 1 - t), so the grids halve; each tile's arithmetic is unchanged.  The
-results must therefore equal, bit for bit, those of the same problem given an
+(n - 1 - t), so the grids halve; each tile's arithmetic is unchanged, except
+that with stored tiles the dK/dV pass sweeps a mirror tile's query tiles
+upwards (so that the workgroups read the same Q and dO rows at the same
+time), which reorders the fp32 sums of those dK and dV rows.  The results
+must therefore equal, bit for bit, those of the same problem given an
 all-zero seg (served one tile per workgroup, and held to the oracle by the
 other parity tests), in every mode: stored tiles and recomputed scores, the
 row term computed or read off the forward output, with and without the RoPE
-backward.  The shapes give odd and even tile counts of both tile heights,
+backward -- dK and dV with stored tiles to rounding only (1e-4 of their
+largest entry, a twentieth of the parity bound).  The shapes give odd and even tile counts of both tile heights,
 ragged last tiles, and sequences shorter than one tile.  A few are also held
 to the oracle directly, with nonzero initial outputs.
 """
@@ -18,6 +22,7 @@ from causal_gqa_attention_bwd_amd.workloads import random_problem
 from tests.gpu_helpers import TOL, gpu_bwd, rel_err
 
 pytestmark = pytest.mark.gpu
+ROUNDING = 1e-4  # two fp32 sums of the same terms in opposite orders
 
 SHAPES = [  # S, H, KV, d
     (1, 2, 1, 64),
@@ -56,8 +61,12 @@ def test_paired_equals_unpaired(shape, mode, entry, monkeypatch):
     say(f"[gpu] pairing S{shape[0]} H{shape[1]} KV{shape[2]} d{shape[3]} {mode} {entry}")
     paired = gpu_bwd(p, lse, use_seg=False, **kw)
     unpaired = gpu_bwd(p, lse, **kw)
-    for name, a, b in zip(("dQ", "dK", "dV"), paired, unpaired):
-        assert np.array_equal(a, b), f"{name}: paired and unpaired schedules differ"
+    for name, a, b, i0 in zip(("dQ", "dK", "dV"), paired, unpaired, init):
+        if mode == "stored" and name != "dQ":
+            e = float(np.max(np.abs(a - b))) / max(float(np.max(np.abs(b - i0))), 1e-30)
+            assert e <= ROUNDING, f"{name}: paired and unpaired schedules differ by {e:.2e}"
+        else:
+            assert np.array_equal(a, b), f"{name}: paired and unpaired schedules differ"
 
 
 @pytest.mark.parametrize("shape", [SHAPES[1], SHAPES[4], SHAPES[6], SHAPES[8]],
