@@ -73,6 +73,8 @@ struct BwdArgs {
   int rope;              // 1: rotate dQ, dK back by RoPE after the += (rope_bwd)
   int rope_pos;          // position of row 0 (the page's pos_offset)
   double rope_base;      // frequency base
+  int hsplit;            // k_dkdv_p: blocks sharing one key tile's heads (1, or 2^k | g)
+  float* part;           // [2 * hsplit][S, KV, d] partial dK, dV (hsplit > 1), else NULL
 };
 
 struct FwdArgs {
@@ -346,6 +348,29 @@ __global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint3
     __syncthreads();
   }
   if (t == 0) slot_off[nblk] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// k_sumparts: dK += sum over splits of part[2 split], dV += sum of
+// part[2 split + 1], split by split in order; n = S * KV * d floats per slice
+// (a multiple of 4: d is a multiple of 16).  Adds the partial sums of the
+// key-major passes that split a group's heads over workgroups.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sumparts(const float* __restrict__ part, int splits,
+                                                  long long n, float* dK, float* dV) {
+  const long long n4 = n / 4;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * blockDim.x) {
+    float4 k = reinterpret_cast<float4*>(dK)[i], v = reinterpret_cast<float4*>(dV)[i];
+    for (int s = 0; s < splits; ++s) {
+      const float4 pk = reinterpret_cast<const float4*>(part + (size_t)(2 * s) * n)[i];
+      const float4 pv = reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * n)[i];
+      k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
+      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+    }
+    reinterpret_cast<float4*>(dK)[i] = k;
+    reinterpret_cast<float4*>(dV)[i] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -947,17 +972,22 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 // the two accumulations dV += P^T dO and dK += (dS/scale)^T Q.  With a given
 // row term (DK) the second tile already holds dS/scale.  Above 128 columns
 // the two waves of a key block split the output columns instead of the query
-// rows.
+// rows.  With hsplit > 1, hsplit workgroups share a key tile, each taking
+// g / hsplit heads of the group and writing its partial dK, dV to its own
+// slices of `part` (k_sumparts then adds them, split by split): under a
+// document mask one key tile's work can exceed the per-CU share of the whole
+// launch, and the split halves the longest workgroups.
+//
+// The sweep order (query tiles, then the heads of the split) lives in
+// registers: the query tiles are scanned in segments of 64 (lane i <-> tile
+// base -/+ i); a ballot gives the tiles any query of which sees these keys,
+// and each lane keeps its tile's slot base for this wave's block pair.  The
+// walk over a segment is scalar bit arithmetic, so no memory read sits
+// between an item and the next one's prefetch.
 //
 // Output columns are permuted: lane l's accumulator block nb holds column
 // dcol0 + NB*(l%32) + nb, so that the NB operands a lane needs per step are
 // adjacent in LDS (one wide read) and its NB results adjacent in memory.
-//
-// The sweep order is kept in registers: the query tiles are scanned in
-// segments of 64 (lane i <-> tile top - i); a ballot gives the tiles any query
-// of which sees these keys, and each lane keeps its tile's slot base for this
-// wave's block pair.  The walk over a segment is scalar bit arithmetic, so no
-// memory read sits between an item and the next one's prefetch.
 // ---------------------------------------------------------------------------
 template <int DP, bool DK>
 __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
@@ -978,15 +1008,17 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   const int qs = DSPLIT ? 0 : (wave & 1);
   const int dcol0 = DSPLIT ? (wave & 1) * DW : 0;
   const int S = a.S, H = a.H, KV = a.KV, d = a.d;
-  const int g = H / KV;
+  const int g = H / KV, gs = g / a.hsplit;  // heads of the group per split
+  // block -> (tile, head split, KV head), KV head fastest
   const int kvh = blockIdx.x % KV;
+  const int split = (int)(blockIdx.x / KV) % a.hsplit;
   const int nkt = (S + BC - 1) / BC;
   auto tile = [&](const int kt) __attribute__((always_inline)) {
   const int j0 = kt * BC;
   // paired: the upper half of the key tiles sweeps the query tiles upwards
   const bool up = a.pair && 2 * kt > nkt - 1;
   const int kblk = kt * KB + kb;  // this wave's key block
-  const int head0 = kvh * g;
+  const int head0 = kvh * g + split * gs;
   const size_t qstride = (size_t)H * d, kstride = (size_t)KV * d;
 
   f32x16 accK[NB], accV[NB];
@@ -1029,7 +1061,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   };
   // step (li, hh) to the next item of the sweep; false at its end
   auto advance = [&](int& li, int& hh) -> bool {
-    if (++hh < g) return true;
+    if (++hh < gs) return true;
     hh = 0;
     uint64_t rest = li < 0 ? mask : (li >= 63 ? 0ull : mask & (~0ull << (li + 1)));
     while (rest == 0) {
@@ -1072,7 +1104,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   };
 
   build(seg);
-  int li = -1, hh = g - 1, buf = 0, cslot = -1;
+  int li = -1, hh = gs - 1, buf = 0, cslot = -1;
   bool has = advance(li, hh);
   if (has) {
     const int t = tile_of(seg, li);
@@ -1192,7 +1224,26 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
       }
     }
   }
-  if (qs == 0) {  // the other query block's waves only contributed partial sums
+  if (qs == 0 && a.hsplit > 1) {
+  // this split's partial sums scale * accK, accV into its slices of part
+  // (k_sumparts adds them to dK, dV); no RoPE with splits
+  const size_t slice = (size_t)S * kstride;
+  float* __restrict__ pK = a.part + (size_t)(2 * split) * slice + (size_t)kvh * d;
+  float* __restrict__ pV = a.part + (size_t)(2 * split + 1) * slice + (size_t)kvh * d;
+  const int col0 = dcol0 + NB * l32;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = j0 + kb * 32 + crow(r, hf);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if (row < S && col0 + nb < d) {
+        const size_t off = (size_t)row * kstride + col0 + nb;
+        pK[off] = a.scale * accK[nb][r];
+        pV[off] = accV[nb][r];
+      }
+    }
+  }
+  } else if (qs == 0) {  // the other query block's waves only contributed partial sums
   // dK += scale * accK, dV += accV: all old values are read first, then all written
   float* __restrict__ dKh = a.dK + (size_t)kvh * d;
   float* __restrict__ dVh = a.dV + (size_t)kvh * d;
@@ -1245,7 +1296,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   // (downwards they would spread over all tiles).  Unpaired (documents), a
   // block's tile lies inside one document and the blocks of a document
   // start together, so downwards is kept.
-  const int first = (int)(blockIdx.x / KV), second = mirror_tile(first, nkt, a.pair);
+  const int first = (int)(blockIdx.x / KV) / a.hsplit, second = mirror_tile(first, nkt, a.pair);
   tile(first);
   if (second >= 0) {
     __syncthreads();  // the first tile is done with the LDS
@@ -1703,10 +1754,12 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
   if (rc != ATTN_OK) return rc;
   const int nkt = blocks((a.S + 63) / 64);
   if (a.scratch)
-    hipLaunchKernelGGL((k_dkdv_p<DP, DK>), dim3(nkt * a.KV), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((k_dkdv_p<DP, DK>), dim3(nkt * a.hsplit * a.KV), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching the dK/dV kernel");
+  if (rc == ATTN_OK && a.scratch && a.hsplit > 1)
+    rc = launch_sumparts(a.part, a.hsplit, (long long)a.S * a.KV * a.d, a.dK, a.dV, st);
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK || !a.scratch) return rc;
   const int BRs = DP > 128 ? 64 : 128;
@@ -1780,15 +1833,24 @@ static long long scratch_budget() {
 
 // How attn_bwd runs a problem: with the stored P / P*dP tiles when their
 // bound fits the budget (tile indices then also stay below 2^31), else with
-// the scores recomputed by the key-major kernel; and the layout of the
-// per-call workspace: D [S, H], per-block seg min/max and slot offsets, then
-// the scratch.
+// the scores recomputed by the key-major kernel; how many workgroups share a
+// key tile's heads in k_dkdv_p; and the layout of the per-call workspace:
+// D [S, H], per-block seg min/max and slot offsets, the scratch, then the
+// partial dK, dV of the head splits.
 struct Plan {
   bool stored = false;
-  size_t off_blk = 0, off_slot = 0, off_scr = 0, bytes = 0;
+  int hsplit = 1;
+  size_t off_blk = 0, off_slot = 0, off_scr = 0, off_part = 0, bytes = 0;
 };
 
-static Plan make_plan(int S, int H) {
+// may_split: the call is unpaired (a seg given, or pairing off) and has no
+// RoPE step.  Paired tiles carry equal work; unpaired, under a document mask,
+// the first key tile of a long document can hold more work than a CU's share
+// of the whole pass, so k_dkdv_p splits each group's heads over workgroups
+// until the launch has ~1024 of them (S=16384, 2 KV heads, documents: the
+// longest workgroup came down from 1.3 to 1.12 times the mean load of a CU).
+// The RoPE step rotates the summed dK, so it takes no splits.
+static Plan make_plan(int S, int H, int KV, int d, bool may_split) {
   Plan p;
   const long long nblk = ((long long)S + 31) / 32;
   const long long need = scratch_bound(nblk, H);
@@ -1798,7 +1860,14 @@ static Plan make_plan(int S, int H) {
   p.off_blk = (nD * sizeof(float) + 255) & ~(size_t)255;
   p.off_slot = (p.off_blk + 2 * nblk * sizeof(uint32_t) + 255) & ~(size_t)255;
   p.off_scr = (p.off_slot + (nblk + 1) * sizeof(long long) + 255) & ~(size_t)255;
-  p.bytes = p.off_scr + (p.stored ? (size_t)need : 0);
+  p.off_part = (p.off_scr + (p.stored ? (size_t)need : 0) + 255) & ~(size_t)255;
+  if (p.stored && may_split) {
+    const long long blocks = ((long long)S + 63) / 64 * KV;
+    const int g = H / KV;
+    while (blocks * p.hsplit < 1024 && g % (2 * p.hsplit) == 0) p.hsplit *= 2;
+  }
+  p.bytes = p.hsplit > 1 ? p.off_part + (size_t)2 * p.hsplit * S * KV * d * sizeof(float)
+                         : p.off_scr + (p.stored ? (size_t)need : 0);
   return p;
 }
 
@@ -1807,7 +1876,8 @@ extern "C" attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads,
   g_err[0] = 0;
   attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, 1.f);
   if (rc != ATTN_OK) return rc;
-  const Plan p = make_plan(seq_len, n_heads);
+  // the most a call of this size takes: an unpaired one, with head splits
+  const Plan p = make_plan(seq_len, n_heads, n_kv_heads, head_dim, true);
   if (workspace_bytes) *workspace_bytes = seq_len ? p.bytes : 0;
   if (stored_tiles) *stored_tiles = p.stored ? 1 : 0;
   return ATTN_OK;
@@ -1827,6 +1897,13 @@ attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* blk_min, uint32_
                           long long* slot_off, hipStream_t st) {
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, st, seg, S, blk_min, blk_max, slot_off);
   return hip_check(hipGetLastError(), "launching k_prep");
+}
+
+attn_status_t launch_sumparts(const float* part, int splits, long long n, float* dK, float* dV,
+                              hipStream_t st) {
+  const int blocks = (int)std::min<long long>((n / 4 + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_sumparts, dim3(blocks), dim3(256), 0, st, part, splits, n, dK, dV);
+  return hip_check(hipGetLastError(), "launching k_sumparts");
 }
 
 attn_status_t launch_rowdot(const float* O, const float* dO, float* D, long long rows, int d,
@@ -1863,7 +1940,10 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const int dp = padded_dim(head_dim);
   const long long nblk = ((long long)seq_len + 31) / 32;
-  const Plan pl = make_plan(seq_len, n_heads);
+  // plain causal: every tile's work falls linearly with its index, so a tile
+  // and its mirror sum to the same work (ATTNBWD_PAIR=0 turns this off)
+  const bool pair = seg == nullptr && pairing_enabled();
+  const Plan pl = make_plan(seq_len, n_heads, n_kv_heads, head_dim, !pair && !rope);
   hipMemPool_t pool;
   rc = device_pool(&pool);
   if (rc != ATTN_OK) return rc;
@@ -1881,9 +1961,9 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   a.slot_off = reinterpret_cast<long long*>(wsb + pl.off_slot);
   a.scratch = pl.stored ? reinterpret_cast<float*>(wsb + pl.off_scr) : nullptr;
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim; a.scale = scale;
-  // plain causal: every tile's work falls linearly with its index, so a tile
-  // and its mirror sum to the same work (ATTNBWD_PAIR=0 turns this off)
-  a.pair = seg == nullptr && pairing_enabled();
+  a.pair = pair;
+  a.hsplit = pl.hsplit;
+  a.part = pl.hsplit > 1 ? reinterpret_cast<float*>(wsb + pl.off_part) : nullptr;
   a.rope = rope;
   a.rope_pos = pos_offset;
   a.rope_base = (double)rope_base;

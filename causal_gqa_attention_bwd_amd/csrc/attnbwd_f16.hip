@@ -665,26 +665,6 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
   if (second >= 0) tile(second);
 }
 
-// k_sumparts: dK += sum over splits of part[2 split], dV += sum of
-// part[2 split + 1], split by split in order; n = S * KV * d floats per slice
-// (a multiple of 4: d is a multiple of 16).
-__global__ __launch_bounds__(256) void k_sumparts(const float* __restrict__ part, int splits,
-                                                  long long n, float* dK, float* dV) {
-  const long long n4 = n / 4;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (long long)gridDim.x * blockDim.x) {
-    float4 k = reinterpret_cast<float4*>(dK)[i], v = reinterpret_cast<float4*>(dV)[i];
-    for (int s = 0; s < splits; ++s) {
-      const float4 pk = reinterpret_cast<const float4*>(part + (size_t)(2 * s) * n)[i];
-      const float4 pv = reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * n)[i];
-      k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
-      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
-    }
-    reinterpret_cast<float4*>(dK)[i] = k;
-    reinterpret_cast<float4*>(dV)[i] = v;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -712,10 +692,7 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   hipLaunchKernelGGL(k_kv16<DP>, dim3(kv_grid), dim3(256), 0, st, f);
   rc = hip_check(hipGetLastError(), "launching k_kv16");
   if (rc == ATTN_OK && f.splits > 1) {
-    const long long n = (long long)f.S * f.KV * f.d;
-    const int nb4 = (int)std::min<long long>((n / 4 + 255) / 256, 4096);
-    hipLaunchKernelGGL(k_sumparts, dim3(nb4), dim3(256), 0, st, f.part, f.splits, n, f.dK, f.dV);
-    rc = hip_check(hipGetLastError(), "launching k_sumparts");
+    rc = launch_sumparts(f.part, f.splits, (long long)f.S * f.KV * f.d, f.dK, f.dV, st);
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;

@@ -154,3 +154,7 @@ ATTN_INTERNAL attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* bl
 // k_rowdot: D[r] = dO[r, :] . O[r, :] for rows [0, rows) of two [rows, d] tensors.
 ATTN_INTERNAL attn_status_t launch_rowdot(const float* O, const float* dO, float* D, long long rows,
                                           int d, hipStream_t st);
+// k_sumparts: dK += sum of part[2 s], dV += sum of part[2 s + 1] over the
+// splits s in order; n = S * KV * d floats per slice.
+ATTN_INTERNAL attn_status_t launch_sumparts(const float* part, int splits, long long n, float* dK,
+                                            float* dV, hipStream_t st);

@@ -49,12 +49,19 @@ def up(n):
 def test_plan_sizes_the_workspace(monkeypatch):
     # host-only query: D [S,H], block metadata, and the P / P*dP tile scratch
     # (two 32x32 fp32 tiles per (query block, key block, head) of the causal
-    # triangle), each part 256-byte aligned
+    # triangle), each part 256-byte aligned, then -- the most a call takes is
+    # an unpaired one -- the partial dK, dV of the key-major head splits: 64
+    # key tiles x 8 KV heads = 512 workgroups, so the 4 heads of a group go
+    # to 2 workgroups, each with its own [S, KV, d] slice of dK and of dV
     monkeypatch.delenv("ATTNBWD_SCRATCH_MB", raising=False)
     S, H = 4096, 32
     nblk = S // 32
     meta = up(up(up(S * H * 4) + 2 * nblk * 4) + (nblk + 1) * 8)
-    assert binding.bwd_plan(S, H, 8, 128) == (meta + causal_pairs(nblk) * H * 8192, True)
+    part = 2 * 2 * S * 8 * 128 * 4
+    assert binding.bwd_plan(S, H, 8, 128) == (meta + causal_pairs(nblk) * H * 8192 + part, True)
+    # a group of one head cannot split
+    assert binding.bwd_plan(S, 8, 8, 128) == (
+        up(up(up(S * 8 * 4) + 2 * nblk * 4) + (nblk + 1) * 8) + causal_pairs(nblk) * 8 * 8192, True)
     monkeypatch.setenv("ATTNBWD_SCRATCH_MB", "0")
     assert binding.bwd_plan(S, H, 8, 128) == (meta, False)
 

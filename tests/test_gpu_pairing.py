@@ -10,7 +10,9 @@ all-zero seg (served one tile per workgroup, and held to the oracle by the
 other parity tests), in every mode: stored tiles and recomputed scores, the
 row term computed or read off the forward output, with and without the RoPE
 backward -- dK and dV with stored tiles to rounding only (1e-4 of their
-largest entry, a twentieth of the parity bound).  The shapes give odd and even tile counts of both tile heights,
+largest entry, a twentieth of the parity bound).  Unpaired calls of few key
+tiles also split each group's heads over workgroups whose partial dK, dV are
+summed afterwards, which reorders those sums once more.  The shapes give odd and even tile counts of both tile heights,
 ragged last tiles, and sequences shorter than one tile.  A few are also held
 to the oracle directly, with nonzero initial outputs.
 """
@@ -61,9 +63,13 @@ def test_paired_equals_unpaired(shape, mode, entry, monkeypatch):
     say(f"[gpu] pairing S{shape[0]} H{shape[1]} KV{shape[2]} d{shape[3]} {mode} {entry}")
     paired = gpu_bwd(p, lse, use_seg=False, **kw)
     unpaired = gpu_bwd(p, lse, **kw)
+    # a gradient that is zero in exact arithmetic (dK with one key: dS = 0)
+    # holds rounding noise only: its bound is then relative to the largest one
+    overall = max(float(np.max(np.abs(b - i0))) for b, i0 in zip(unpaired, init))
     for name, a, b, i0 in zip(("dQ", "dK", "dV"), paired, unpaired, init):
         if mode == "stored" and name != "dQ":
-            e = float(np.max(np.abs(a - b))) / max(float(np.max(np.abs(b - i0))), 1e-30)
+            ref = max(float(np.max(np.abs(b - i0))), 1e-2 * overall, 1e-30)
+            e = float(np.max(np.abs(a - b))) / ref
             assert e <= ROUNDING, f"{name}: paired and unpaired schedules differ by {e:.2e}"
         else:
             assert np.array_equal(a, b), f"{name}: paired and unpaired schedules differ"
