@@ -271,7 +271,7 @@ def main():
     if args.f16:
         log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
     else:
-        log(f"bench: workspace {ws_bytes / 2**30:.2f} GiB, "
+        log(f"bench: workspace at most {ws_bytes / 2**30:.2f} GiB (attn_bwd_plan), "
             f"{'stored' if stored else 'recomputed'} probability tiles")
     dQ = torch.zeros_like(t["Q"])
     dK = torch.zeros_like(t["K"])
@@ -389,9 +389,13 @@ def main():
                    "operands": ("fp16, fp32 accumulation" if args.f16 else "fp32"),
                    "forward_output_given": bool(args.o_entry),
                    "stored_tiles": None if args.f16 or args.short else stored,
-                   "workspace_bytes": (0 if args.short and args.o_entry else
-                                       w.S * w.H * 4 if args.short else
-                                       f16_ws if args.f16 else ws_bytes),
+                   # general path: attn_bwd_plan's figure, the most a call of this size
+                   # takes (with a seg: head-split partial sums); fp16: the operand
+                   # copies and D, before any partial sums; short: the row term D
+                   ("row_term_bytes" if args.short else "fp16_copies_bytes" if args.f16 else
+                    "workspace_bytes_max"):
+                       (0 if args.short and args.o_entry else
+                        w.S * w.H * 4 if args.short else f16_ws if args.f16 else ws_bytes),
                    "kernel_ms": kernel_ms},
         "roofline": roofline,
         "cpu_baseline": cpu,
