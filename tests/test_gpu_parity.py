@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
+from causal_gqa_attention_bwd_amd import binding
 from causal_gqa_attention_bwd_amd.workloads import make_inputs, random_problem, seg_from_lengths
 from tests.gpu_helpers import TOL, gpu_bwd, gpu_fwd, rel_err
 
@@ -184,3 +185,32 @@ def test_forward_empty_rows():
     assert np.all(np.isneginf(L[empty])) and np.all(O[empty] == 0)
     assert np.max(np.abs(L[~empty] - L_ref[~empty])) <= 2e-5 * max(1.0, np.abs(L_ref[~empty]).max())
     assert rel_err(O, O_ref) <= 1e-4
+
+
+# (S, H, KV, d, splits): calls with a seg whose key-major pass has few
+# workgroups (64-key tiles x KV heads) split each group's heads over `splits`
+# workgroups; their partial dK, dV go through the workspace.  The plan's
+# workspace size shows the split count; parity with nonzero initial outputs
+# (the += contract through the partial sums) and through both entries.
+HEAD_SPLITS = [
+    (100, 4, 2, 64, 2),
+    (130, 8, 2, 96, 4),
+    (200, 16, 2, 128, 8),
+    (450, 8, 1, 256, 8),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_SPLITS, ids=lambda c: "S%dH%dKV%dd%d_x%d" % c)
+@pytest.mark.parametrize("with_o", [False, True])
+def test_head_splits_parity(case, with_o):
+    S, H, KV, d, splits = case
+    nbytes, stored = binding.bwd_plan(S, H, KV, d)
+    nblk = (S + 31) // 32
+    up = lambda n: (n + 255) // 256 * 256
+    meta = up(up(up(S * H * 4) + 2 * nblk * 4) + (nblk + 1) * 8)
+    tiles = nblk * (nblk + 1) // 2 * H * 8192
+    assert stored and nbytes == meta + tiles + 2 * splits * S * KV * d * 4
+    rng = np.random.default_rng(4400 + S + H)
+    p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, "docs"))
+    init = [rng.standard_normal(p[k].shape).astype(np.float32) for k in ("Q", "K", "V")]
+    check_full(p, "head splits x%d" % splits, init=init, with_o=with_o)
