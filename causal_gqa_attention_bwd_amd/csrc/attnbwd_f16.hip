@@ -156,6 +156,7 @@ struct F16Args {
   float *dQ, *dK, *dV;
   float* D;                            // [S, H] row term
   const uint32_t* blk_min;             // [ceil(S/32)] min seg per 32-row query block
+  const uint32_t* blk_max;             // [ceil(S/32)] max seg per 32-row query block
   int S, Sp, H, KV, d;
   float scale;
   int pair;                            // 1: block p serves tiles p and n-1-p (plain causal)
@@ -210,9 +211,12 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
 // in flight), shared by the four waves.  The score tiles hold key crow(r, hf)
 // of query l%32, so each lane's LSE, D and seg are one value.
 //   DONLY: D[q] = sum_j P dP (the row term, for the key-major pass).
-//   else:  dQ += dS K with dS = scale P (dP - D), A operand straight from the
-//          dS registers, B from the K row tile by transposing loads; the
-//          accumulators stay in AGPRs.
+//   else:  dQ += scale (dS/scale) K with dS/scale = P (dP - D), A operand
+//          straight from the dS registers, B from the K row tile by
+//          transposing loads; the accumulators stay in AGPRs.
+// A block whose every pair is visible (keys at or before every query of the
+// wave, at or after every row's document start, every row inside S) skips
+// the per-element mask; the wave's largest document start comes from k_prep.
 // ---------------------------------------------------------------------------
 template <int DP, bool DONLY>
 struct QGeom {
@@ -268,6 +272,10 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
     const int nblk = (S + 31) / 32;
     const int qb = (i0 >> 5) + wave;
     const uint32_t lo = qb < nblk ? a.blk_min[qb] : 0xffffffffu;
+    // the largest document start of this wave's rows, and whether all 32 exist
+    const uint32_t wmx = (a.seg && qb < nblk) ? a.blk_max[qb] : 0u;
+    const int q_first = i0 + 32 * wave;
+    const bool rows_in = q_first + 31 < S;
     if (lane == 0) sMin[wave] = lo;
     // the register loads above land here, where the compiler sees it (not
     // inside the block loop, on a counter that also counts the ring's loads)
@@ -307,14 +315,28 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
         s = mfma16(ka, qreg[t], s);
         dp = mfma16(va, oreg[t], dp);
       }
+      // every pair visible: the block's keys at or before every query of the
+      // wave, at or after every row's document start, and all rows inside S
+      const bool full = rows_in & (kb * 32 + 31 <= q_first) & (wmx <= (uint32_t)(kb * 32));
+      // P; the row term D += P dP, or dS/scale = P (dP - D) (the scale goes
+      // onto dQ at the end)
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kb * 32 + crow(r, hf);
-        const bool vis = (key <= q) & ((uint32_t)key >= sq);
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
-        const float p = vis ? e : 0.f;
-        if constexpr (DONLY) Dacc = fmaf(p, dp[r], Dacc);
-        else s[r] = p * (dp[r] - Dq) * a.scale;
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
+          if constexpr (DONLY) Dacc = fmaf(p, dp[r], Dacc);
+          else s[r] = p * (dp[r] - Dq);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kb * 32 + crow(r, hf);
+          const bool vis = (key <= q) & ((uint32_t)key >= sq);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse2));
+          const float p = vis ? e : 0.f;
+          if constexpr (DONLY) Dacc = fmaf(p, dp[r], Dacc);
+          else s[r] = p * (dp[r] - Dq);
+        }
       }
       if constexpr (!DONLY) {
         // B operands from the K row tile (transposing loads): the k order of
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i0 + 32 * wave + crow(r, hf);
-          if (row < S && col < a.d) dQh[(size_t)row * qstride + col] += acc[o][r];
+          if (row < S && col < a.d) dQh[(size_t)row * qstride + col] += a.scale * acc[o][r];
         }
       }
     }
@@ -393,9 +415,12 @@ __global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
 // Per visible 32-row query block and head of the split's share of the group,
 // the Q and dO row tiles and the rows' LSE, D and seg stream through an LDS
 // ring of NBUF stages (NBUF - 1 steps in flight), shared by the four waves.
-// Each wave forms P and dS = scale P (dP - D) in registers and accumulates
-// dV += P^T dO and dK += dS^T Q over its part's output columns, with the B
-// operands read from the same row tiles by transposing loads.  Above 128 columns the output
+// Each wave forms P and dS/scale = P (dP - D) in registers and accumulates
+// dV += P^T dO and dK/scale += (dS/scale)^T Q over its part's output columns
+// (the scale goes onto dK at the end), with the B operands read from the same
+// row tiles by transposing loads.  A step whose every pair is visible skips
+// the per-element mask: the block's largest document start (from k_prep) is
+// staged with its rows.  Above 128 columns the output
 // columns come in two parts, one workgroup each (both form S and dP), so that
 // a wave's accumulators fit the register file.  The visible query blocks of
 // the tile (blk_min <= last key, at or after the diagonal) come from 64-block
@@ -411,7 +436,7 @@ struct KvGeom {
   static constexpr int NOW = DW / 32;          // 32-column output tiles per part
   using RT = Tile16<32, DP / 8>;
   static constexpr int OFF_DO = RT::BYTES;
-  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE, D, seg, spare (256 B each)
+  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE, D, seg, max seg (256 B each)
   static constexpr int STAGE = OFF_ROW + 4 * 256;
   static constexpr int NBUF = 4 * STAGE <= 150 * 1024 ? 4 : 3 * STAGE <= 150 * 1024 ? 3 : 2;
   static constexpr int LPS = 2 * RT::CPW + 1;  // loads per wave per step
@@ -513,8 +538,8 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       const size_t roff = ((size_t)head * a.Sp + (size_t)qb * 32) * DP;
       ldr.load(buf_rsrc(a.Qh + roff, 32 * DP * 2), st, wave);
       ldr.load(buf_rsrc(a.dOh + roff, 32 * DP * 2), st + G::OFF_DO, wave);
-      // LSE, D and seg of the block's rows (lanes 0..31; the rest, and wave 3's
-      // spare load, deposit zeros)
+      // LSE, D and seg of the block's rows (lanes 0..31; the rest deposit
+      // zeros), and the block's largest seg (wave 3, lane 0; 0 without a seg)
       const int rows = min(32, S - qb * 32);
       const bool rok = hf == 0 && l32 < rows;
       const uint32_t roff4 = rok ? (uint32_t)(l32 * H + head) * 4u : ATTN_BUF_OOB;
@@ -525,13 +550,21 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         dma4(buf_rsrc(a.seg ? (const void*)(a.seg + (size_t)qb * 32) : (const void*)a.LSE,
                       a.seg ? (uint32_t)rows * 4u : 0u),
              rok ? (uint32_t)l32 * 4u : ATTN_BUF_OOB, st + G::OFF_ROW + 512);
-      else dma4(buf_rsrc(a.LSE, 0u), ATTN_BUF_OOB, st + G::OFF_ROW + 768);
+      else dma4(buf_rsrc(a.seg ? (const void*)(a.blk_max + qb) : (const void*)a.LSE,
+                         a.seg ? 4u : 0u),
+                lane == 0 ? 0u : ATTN_BUF_OOB, st + G::OFF_ROW + 768);
     };
 
     auto compute = [&](int qb, int buf) {
-      const int q0 = qb * 32;
-      if (j0 + 32 * wave > q0 + 31) return;  // every key of the block after every query
+      const int q0 = qb * 32, k0 = j0 + 32 * wave;
+      if (k0 > q0 + 31) return;  // every key of the block after every query
       const char* st = smem + buf * STAGE;
+      // every pair visible: keys at or before every query, every row inside
+      // S, and no document start of the rows after the first key (the
+      // block's largest seg is staged with its rows)
+      const uint32_t mx = __builtin_amdgcn_readfirstlane(
+          *reinterpret_cast<const uint32_t*>(st + G::OFF_ROW + 768));
+      const bool full = (k0 + 31 <= q0) & (q0 + 31 < S) & (mx <= (uint32_t)k0);
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -539,28 +572,42 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         dp = mfma16(*reinterpret_cast<const h8*>(st + G::OFF_DO + RT::at(l32, 2 * t + hf)), vreg[t],
                     dp);
       }
-      // LSE, D and seg of this lane's rows crow(r, hf): rows 8(r/4) + 4hf + r%4,
+      // LSE and D of this lane's rows crow(r, hf): rows 8(r/4) + 4hf + r%4,
       // four 16-byte reads each
       float lse[16], dv[16];
-      uint32_t sg[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int row0 = 8 * a4 + 4 * hf;
         const float4 l4 = *reinterpret_cast<const float4*>(st + G::OFF_ROW + 4 * row0);
         const float4 d4 = *reinterpret_cast<const float4*>(st + G::OFF_ROW + 256 + 4 * row0);
-        const uint4 s4 = *reinterpret_cast<const uint4*>(st + G::OFF_ROW + 512 + 4 * row0);
         lse[4 * a4] = l4.x; lse[4 * a4 + 1] = l4.y; lse[4 * a4 + 2] = l4.z; lse[4 * a4 + 3] = l4.w;
         dv[4 * a4] = d4.x; dv[4 * a4 + 1] = d4.y; dv[4 * a4 + 2] = d4.z; dv[4 * a4 + 3] = d4.w;
-        sg[4 * a4] = s4.x; sg[4 * a4 + 1] = s4.y; sg[4 * a4 + 2] = s4.z; sg[4 * a4 + 3] = s4.w;
       }
+      // P, and dS/scale = P (dP - D) (the scale goes onto dK at the end)
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qq = q0 + crow(r, hf);
-        const bool vis = (qq < S) & (key <= qq) & ((uint32_t)key >= sg[r]);
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r] * ATTN_LOG2E));
-        const float p = vis ? e : 0.f;
-        s[r] = p;
-        dp[r] = p * (dp[r] - dv[r]) * a.scale;
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r] * ATTN_LOG2E));
+          s[r] = p;
+          dp[r] = p * (dp[r] - dv[r]);
+        }
+      } else {
+        uint32_t sg[16];  // seg of the rows
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const uint4 s4 =
+              *reinterpret_cast<const uint4*>(st + G::OFF_ROW + 512 + 4 * (8 * a4 + 4 * hf));
+          sg[4 * a4] = s4.x; sg[4 * a4 + 1] = s4.y; sg[4 * a4 + 2] = s4.z; sg[4 * a4 + 3] = s4.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = q0 + crow(r, hf);
+          const bool vis = (qq < S) & (key <= qq) & ((uint32_t)key >= sg[r]);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r] * ATTN_LOG2E));
+          const float p = vis ? e : 0.f;
+          s[r] = p;
+          dp[r] = p * (dp[r] - dv[r]);
+        }
       }
       const h8 p0 = pack8(s, 0), p1 = pack8(s, 1), d0 = pack8(dp, 0), d1 = pack8(dp, 1);
       // B operands from the Q and dO row tiles (transposing loads): the k
@@ -648,10 +695,10 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         if (row < S && col < a.d) {
           const size_t off = (size_t)row * kstride + col;
           if (a.splits == 1) {
-            outK[off] += accK[o][r];
+            outK[off] += a.scale * accK[o][r];
             outV[off] += accV[o][r];
           } else {
-            outK[off] = accK[o][r];
+            outK[off] = a.scale * accK[o][r];
             outV[off] = accV[o][r];
           }
         }
@@ -770,6 +817,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   f.LSE = LSE; f.seg = seg; f.dQ = dQ; f.dK = dK; f.dV = dV;
   f.D = reinterpret_cast<float*>(w + off_D);
   f.blk_min = reinterpret_cast<const uint32_t*>(w + off_min);
+  f.blk_max = reinterpret_cast<const uint32_t*>(w + off_max);
   f.S = seq_len; f.Sp = (int)Sp; f.H = n_heads; f.KV = n_kv_heads; f.d = head_dim; f.scale = scale;
   f.pair = pair;
   f.splits = splits;
