@@ -267,7 +267,7 @@ def main():
     binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, O, lse, scale)
     ws_bytes, stored = binding.bwd_plan(w.S, w.H, w.KV, w.d)
     dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
-    f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + w.S * w.H * 4
+    f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + 2 * w.S * w.H * 4
     if args.f16:
         log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
     else:
@@ -391,7 +391,7 @@ def main():
                    "stored_tiles": None if args.f16 or args.short else stored,
                    # general path: attn_bwd_plan's figure, the most a call of this size
                    # takes (with a seg: head-split partial sums); fp16: the operand
-                   # copies and D, before any partial sums; short: the row term D
+                   # copies, D and LSE*log2e, before any partial sums; short: the row term D
                    ("row_term_bytes" if args.short else "fp16_copies_bytes" if args.f16 else
                     "workspace_bytes_max"):
                        (0 if args.short and args.o_entry else

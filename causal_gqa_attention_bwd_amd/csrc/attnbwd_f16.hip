@@ -157,6 +157,7 @@ struct F16Args {
   float* D;                            // [S, H] row term
   const uint32_t* blk_min;             // [ceil(S/32)] min seg per 32-row query block
   const uint32_t* blk_max;             // [ceil(S/32)] max seg per 32-row query block
+  const float* LSE2;                   // [S, H] LSE * log2(e) (k_cvt16)
   int S, Sp, H, KV, d;
   float scale;
   int pair;                            // 1: block p serves tiles p and n-1-p (plain causal)
@@ -168,13 +169,16 @@ struct F16Args {
 struct CvtArgs {
   const float *Q, *dO, *K, *V;
   _Float16 *Qh, *dOh, *Kh, *Vh;
+  const float* LSE;                    // [S, H]
+  float* LSE2;                         // [S, H] LSE * log2(e), for k_kv16
   int S, Sp, H, KV, d;
 };
 
 // ---------------------------------------------------------------------------
 // k_cvt16: one workgroup per (32-row block, head) of one tensor; blocks
 // [0, nb*H) convert Q, then dO, then K (nb*KV), then V.  Rows past S and
-// columns past head_dim become zeros.
+// columns past head_dim become zeros.  The Q blocks also write their rows'
+// LSE * log2(e), the exponent offset k_kv16 stages per step.
 // ---------------------------------------------------------------------------
 template <int DP>
 __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
@@ -200,6 +204,10 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
     if (s < a.S && c < a.d)
       v = *reinterpret_cast<const f32x4*>(src + (size_t)s * stride + (size_t)head * a.d + c);
     *reinterpret_cast<h4*>(dst + ((size_t)head * a.Sp + s) * DP + c) = __builtin_convertvector(v, h4);
+  }
+  if (which == 0 && threadIdx.x < 32 && r0 + (int)threadIdx.x < a.S) {
+    const size_t i = (size_t)(r0 + threadIdx.x) * a.H + head;
+    a.LSE2[i] = a.LSE[i] * ATTN_LOG2E;
   }
 }
 
@@ -436,7 +444,7 @@ struct KvGeom {
   static constexpr int NOW = DW / 32;          // 32-column output tiles per part
   using RT = Tile16<32, DP / 8>;
   static constexpr int OFF_DO = RT::BYTES;
-  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE, D, seg, max seg (256 B each)
+  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE*log2e, D, seg, max seg (256 B each)
   static constexpr int STAGE = OFF_ROW + 4 * 256;
   static constexpr int NBUF = 4 * STAGE <= 150 * 1024 ? 4 : 3 * STAGE <= 150 * 1024 ? 3 : 2;
   static constexpr int LPS = 2 * RT::CPW + 1;  // loads per wave per step
@@ -544,7 +552,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       const bool rok = hf == 0 && l32 < rows;
       const uint32_t roff4 = rok ? (uint32_t)(l32 * H + head) * 4u : ATTN_BUF_OOB;
       const uint32_t rbytes = (uint32_t)(rows * H * 4);
-      if (wave == 0) dma4(buf_rsrc(a.LSE + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW);
+      if (wave == 0) dma4(buf_rsrc(a.LSE2 + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW);
       else if (wave == 1) dma4(buf_rsrc(a.D + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW + 256);
       else if (wave == 2)
         dma4(buf_rsrc(a.seg ? (const void*)(a.seg + (size_t)qb * 32) : (const void*)a.LSE,
@@ -572,8 +580,8 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         dp = mfma16(*reinterpret_cast<const h8*>(st + G::OFF_DO + RT::at(l32, 2 * t + hf)), vreg[t],
                     dp);
       }
-      // LSE and D of this lane's rows crow(r, hf): rows 8(r/4) + 4hf + r%4,
-      // four 16-byte reads each
+      // LSE * log2(e) and D of this lane's rows crow(r, hf): rows 8(r/4) +
+      // 4hf + r%4, four 16-byte reads each
       float lse[16], dv[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -587,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       if (full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r] * ATTN_LOG2E));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r]));
           s[r] = p;
           dp[r] = p * (dp[r] - dv[r]);
         }
@@ -603,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         for (int r = 0; r < 16; ++r) {
           const int qq = q0 + crow(r, hf);
           const bool vis = (qq < S) & (key <= qq) & ((uint32_t)key >= sg[r]);
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r] * ATTN_LOG2E));
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r]));
           const float p = vis ? e : 0.f;
           s[r] = p;
           dp[r] = p * (dp[r] - dv[r]);
@@ -771,6 +779,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   const size_t qbytes = (size_t)n_heads * Sp * dp * 2, kbytes = (size_t)n_kv_heads * Sp * dp * 2;
   size_t off = 0;
   const size_t off_D = off; off += align256((size_t)seq_len * n_heads * 4);
+  const size_t off_L2 = off; off += align256((size_t)seq_len * n_heads * 4);
   const size_t off_min = off; off += align256((size_t)nblk * 4);
   const size_t off_max = off; off += align256((size_t)nblk * 4);
   const size_t off_slot = off; off += align256((size_t)(nblk + 1) * 8);
@@ -818,6 +827,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   f.D = reinterpret_cast<float*>(w + off_D);
   f.blk_min = reinterpret_cast<const uint32_t*>(w + off_min);
   f.blk_max = reinterpret_cast<const uint32_t*>(w + off_max);
+  f.LSE2 = reinterpret_cast<const float*>(w + off_L2);
   f.S = seq_len; f.Sp = (int)Sp; f.H = n_heads; f.KV = n_kv_heads; f.d = head_dim; f.scale = scale;
   f.pair = pair;
   f.splits = splits;
@@ -825,6 +835,8 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   f.part = splits > 1 ? reinterpret_cast<float*>(w + off_part) : nullptr;
   CvtArgs c;
   c.Q = Q; c.dO = dO; c.K = K; c.V = V;
+  c.LSE = LSE;
+  c.LSE2 = reinterpret_cast<float*>(w + off_L2);
   c.Qh = half_at(0); c.dOh = half_at(1); c.Kh = half_at(2); c.Vh = half_at(3);
   c.S = seq_len; c.Sp = (int)Sp; c.H = n_heads; c.KV = n_kv_heads; c.d = head_dim;
 

@@ -162,8 +162,9 @@ attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, cons
  * row-tile copies of Q, dO, K and V, (2 * n_heads + 2 * n_kv_heads) * Sp *
  * DP * 2 bytes, with Sp = seq_len rounded up to 128 and DP = head_dim rounded
  * up to 32, 64, 96, 128, 192 or 256 (the products that contract over rows
- * read these tiles through transposing LDS loads); the row term and block
- * metadata; and, when the key-major pass splits each KV group's heads over
+ * read these tiles through transposing LDS loads); the row term and the
+ * rows' LSE * log2(e) (seq_len * n_heads * 4 bytes each) and block metadata;
+ * and, when the key-major pass splits each KV group's heads over
  * `splits` workgroups (a power of two dividing n_heads / n_kv_heads, chosen
  * from the shape: one round of resident workgroups for plain causal calls,
  * about 1024 workgroups under a document mask), 2 * splits * seq_len * n_kv_heads *
