@@ -1,0 +1,43 @@
+"""GPU parity on seeded random shapes, through every general entry: attn_bwd
+and attn_bwd_f16 with nonzero initial outputs (the += contract), attn_bwd_o
+and attn_bwd_f16 with the forward output.  Shapes draw the group size (1, 2,
+4, 8), the KV head count, every padded head-dim class, lengths up to 900 and
+every mask kind (plain causal, packed documents, arbitrary starts, rows that
+see no key), so they reach the paired and unpaired schedules, the head
+splits and the fp16 full-block steps in combinations the fixed lists do not.
+Bars as in the fixed tests: 2e-3 of the largest gradient for fp32 operands,
+1e-2 for fp16 operands on such small shapes (the fp16 tests explain it)."""
+import numpy as np
+import pytest
+
+from causal_gqa_attention_bwd_amd.workloads import random_problem
+from tests.gpu_helpers import TOL
+from tests.test_gpu_f16 import TOL_F16_EDGE
+from tests.test_gpu_parity import check_full, make_seg
+
+pytestmark = pytest.mark.gpu
+
+
+def draw(i):
+    rng = np.random.default_rng(7700 + i)
+    g = int(rng.choice([1, 2, 4, 8]))
+    KV = int(rng.choice([1, 2, 3, 4]))
+    H = g * KV
+    d = int(rng.choice([16, 32, 48, 64, 96, 128, 160, 192, 256]))
+    S = int(rng.integers(1, 900))
+    while S * H * d > 900 * 16 * 64:  # the oracle finishes each in well under a second
+        S = max(1, S // 2)
+    kind = str(rng.choice(["causal", "docs", "arbitrary", "empty_rows"]))
+    p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
+    init = [rng.standard_normal(p[k].shape).astype(np.float32) for k in ("Q", "K", "V")]
+    return p, init, f"random {i}: S={S} H={H} KV={KV} d={d} {kind}"
+
+
+@pytest.mark.parametrize("mode", ["plain", "o", "f16", "f16o"])
+@pytest.mark.parametrize("i", range(24))
+def test_random_shape_parity(i, mode):
+    p, init, tag = draw(i)
+    f16 = mode.startswith("f16")
+    with_o = mode in ("o", "f16o")
+    check_full(p, f"{tag} {mode}", init=None if with_o else init, with_o=with_o, f16=f16,
+               tol=TOL_F16_EDGE if f16 else TOL)
