@@ -230,15 +230,18 @@ template <int DP, bool DONLY>
 struct QGeom {
   using RT = Tile16<32, DP / 8>;
   static constexpr int STAGE = 2 * RT::BYTES;
-  // two workgroups per CU up to 128 columns, one above
-  static constexpr int BUDGET = DP <= 128 ? 72 * 1024 : 150 * 1024;
+  // two workgroups per CU up to 128 columns; above, one in dQ mode, and two
+  // for the row term (fewer registers) with a shallower ring (S=16384, d=256:
+  // 0.77 -> 0.60 ms; three per CU up to 128 columns gained nothing)
+  static constexpr int BUDGET = DP <= 128 ? 72 * 1024 : DONLY ? 72 * 1024 : 150 * 1024;
+  static constexpr int WAVES_PER_SIMD = DP <= 128 || DONLY ? 2 : 1;
   static constexpr int NBUF = 4 * STAGE <= BUDGET ? 4 : 3 * STAGE <= BUDGET ? 3 : 2;
   static constexpr int LPS = 2 * RT::CPW;  // loads per wave per block
   static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
 
 template <int DP, bool DONLY>
-__global__ __launch_bounds__(256, DP <= 128 ? 2 : 1) void k_q16(F16Args a) {
+__global__ __launch_bounds__(256, (QGeom<DP, DONLY>::WAVES_PER_SIMD)) void k_q16(F16Args a) {
   using G = QGeom<DP, DONLY>;
   using RT = typename G::RT;
   constexpr int NT = DP / 16;  // k-steps of the d-contractions
