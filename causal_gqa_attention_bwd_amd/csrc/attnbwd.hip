@@ -74,7 +74,7 @@ struct BwdArgs {
   int rope_pos;          // position of row 0 (the page's pos_offset)
   double rope_base;      // frequency base
   int hsplit;            // k_dkdv_p: blocks sharing one key tile's heads (1, or 2^k | g)
-  float* part;           // [2 * hsplit][S, KV, d] partial dK, dV (hsplit > 1), else NULL
+  float* part;           // [2 * (hsplit - 1)][S, KV, d] partial dK, dV of splits 1.., or NULL
 };
 
 struct FwdArgs {
@@ -973,10 +973,12 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
 // row term (DK) the second tile already holds dS/scale.  Above 128 columns
 // the two waves of a key block split the output columns instead of the query
 // rows.  With hsplit > 1, hsplit workgroups share a key tile, each taking
-// g / hsplit heads of the group and writing its partial dK, dV to its own
-// slices of `part` (k_sumparts then adds them, split by split): under a
-// document mask one key tile's work can exceed the per-CU share of the whole
-// launch, and the split halves the longest workgroups.
+// g / hsplit heads of the group: the first adds its sums into dK, dV like an
+// unsplit one, the others write theirs to their own slices of `part`
+// (k_sumparts then adds them, split by split): under a document mask one key
+// tile's work can exceed the per-CU share of the whole launch, and the split
+// halves the longest workgroups.  With RoPE each part is rotated back on its
+// own (the rotation is linear).
 //
 // The sweep order (query tiles, then the heads of the split) lives in
 // registers: the query tiles are scanned in segments of 64 (lane i <-> tile
@@ -1224,26 +1226,40 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
       }
     }
   }
-  if (qs == 0 && a.hsplit > 1) {
-  // this split's partial sums scale * accK, accV into its slices of part
-  // (k_sumparts adds them to dK, dV); no RoPE with splits
+  if (qs == 0 && split > 0) {
+  // splits after the first: the partial sums scale * accK (rotated back by
+  // RoPE, which is linear) and accV into this split's slices of part;
+  // k_sumparts adds them to what the first split wrote
   const size_t slice = (size_t)S * kstride;
-  float* __restrict__ pK = a.part + (size_t)(2 * split) * slice + (size_t)kvh * d;
-  float* __restrict__ pV = a.part + (size_t)(2 * split + 1) * slice + (size_t)kvh * d;
+  float* __restrict__ pK = a.part + (size_t)(2 * split - 2) * slice + (size_t)kvh * d;
+  float* __restrict__ pV = a.part + (size_t)(2 * split - 1) * slice + (size_t)kvh * d;
   const int col0 = dcol0 + NB * l32;
+  double fq[NB];  // RoPE frequency of each of this lane's columns
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) fq[nb] = a.rope ? rope_freq(col0 + nb, d, a.rope_base) : 0.0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = j0 + kb * 32 + crow(r, hf);
+    float vk[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) vk[nb] = a.scale * accK[nb][r];
+    if (a.rope) {
+      float pv[NB];
+      rope_partners_perm<NB>(vk, l32, pv);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        vk[nb] = rope_back(vk[nb], pv[nb], col0 + nb, (long long)row + a.rope_pos, fq[nb]);
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (row < S && col0 + nb < d) {
         const size_t off = (size_t)row * kstride + col0 + nb;
-        pK[off] = a.scale * accK[nb][r];
+        pK[off] = vk[nb];
         pV[off] = accV[nb][r];
       }
     }
   }
-  } else if (qs == 0) {  // the other query block's waves only contributed partial sums
+  } else if (qs == 0) {  // one split, or the first of several  // the other query block's waves only contributed partial sums
   // dK += scale * accK, dV += accV: all old values are read first, then all written
   float* __restrict__ dKh = a.dK + (size_t)kvh * d;
   float* __restrict__ dVh = a.dV + (size_t)kvh * d;
@@ -1759,7 +1775,7 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching the dK/dV kernel");
   if (rc == ATTN_OK && a.scratch && a.hsplit > 1)
-    rc = launch_sumparts(a.part, a.hsplit, (long long)a.S * a.KV * a.d, a.dK, a.dV, st);
+    rc = launch_sumparts(a.part, a.hsplit - 1, (long long)a.S * a.KV * a.d, a.dK, a.dV, st);
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK || !a.scratch) return rc;
   const int BRs = DP > 128 ? 64 : 128;
@@ -1836,20 +1852,19 @@ static long long scratch_budget() {
 // the scores recomputed by the key-major kernel; how many workgroups share a
 // key tile's heads in k_dkdv_p; and the layout of the per-call workspace:
 // D [S, H], per-block seg min/max and slot offsets, the scratch, then the
-// partial dK, dV of the head splits.
+// partial dK, dV of the head splits after the first.
 struct Plan {
   bool stored = false;
   int hsplit = 1;
   size_t off_blk = 0, off_slot = 0, off_scr = 0, off_part = 0, bytes = 0;
 };
 
-// may_split: the call is unpaired (a seg given, or pairing off) and has no
-// RoPE step.  Paired tiles carry equal work; unpaired, under a document mask,
-// the first key tile of a long document can hold more work than a CU's share
-// of the whole pass, so k_dkdv_p splits each group's heads over workgroups
-// until the launch has ~1024 of them (S=16384, 2 KV heads, documents: the
-// longest workgroup came down from 1.3 to 1.12 times the mean load of a CU).
-// The RoPE step rotates the summed dK, so it takes no splits.
+// may_split: the call is unpaired (a seg given, or pairing off).  Paired
+// tiles carry equal work; unpaired, under a document mask, the first key tile
+// of a long document can hold more work than a CU's share of the whole pass,
+// so k_dkdv_p splits each group's heads over workgroups until the launch has
+// ~1024 of them (S=16384, 2 KV heads, documents: the longest workgroup came
+// down from 1.3 to 1.12 times the mean load of a CU).
 static Plan make_plan(int S, int H, int KV, int d, bool may_split) {
   Plan p;
   const long long nblk = ((long long)S + 31) / 32;
@@ -1866,7 +1881,7 @@ static Plan make_plan(int S, int H, int KV, int d, bool may_split) {
     const int g = H / KV;
     while (blocks * p.hsplit < 1024 && g % (2 * p.hsplit) == 0) p.hsplit *= 2;
   }
-  p.bytes = p.hsplit > 1 ? p.off_part + (size_t)2 * p.hsplit * S * KV * d * sizeof(float)
+  p.bytes = p.hsplit > 1 ? p.off_part + (size_t)2 * (p.hsplit - 1) * S * KV * d * sizeof(float)
                          : p.off_scr + (p.stored ? (size_t)need : 0);
   return p;
 }
@@ -1943,7 +1958,7 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   // plain causal: every tile's work falls linearly with its index, so a tile
   // and its mirror sum to the same work (ATTNBWD_PAIR=0 turns this off)
   const bool pair = seg == nullptr && pairing_enabled();
-  const Plan pl = make_plan(seq_len, n_heads, n_kv_heads, head_dim, !pair && !rope);
+  const Plan pl = make_plan(seq_len, n_heads, n_kv_heads, head_dim, !pair);
   hipMemPool_t pool;
   rc = device_pool(&pool);
   if (rc != ATTN_OK) return rc;

@@ -89,13 +89,13 @@ typedef enum {
  * The budget is 32 GiB, or ATTNBWD_SCRATCH_MB MiB (a decimal number) when
  * that environment variable is set, read at every call; above it (or at 0)
  * there is no scratch and the key-major pass recomputes the scores.  With
- * the scratch, a call given a seg (and no RoPE step) whose key-major pass
- * would have fewer than 1024 workgroups (64-key tiles x KV heads) splits
- * each group's heads over 2^k workgroups (k as large as that bound and the
- * group size allow), and the workspace then also holds their partial dK
- * and dV: 2 * 2^k * seq_len * n_kv_heads * head_dim * 4 bytes (64 MiB at
- * seq_len 16384, 2 KV heads, head_dim 256, 2 splits).  attn_bwd_plan
- * reports the choice and the largest size for a problem.
+ * the scratch, a call given a seg whose key-major pass would have fewer
+ * than 1024 workgroups (64-key tiles x KV heads) splits each group's heads
+ * over 2^k workgroups (k as large as that bound and the group size allow);
+ * the first adds into dK, dV, and the workspace then also holds the others'
+ * partial dK and dV: 2 * (2^k - 1) * seq_len * n_kv_heads * head_dim * 4
+ * bytes (32 MiB at seq_len 16384, 2 KV heads, head_dim 256, 2 splits).
+ * attn_bwd_plan reports the choice and the largest size for a problem.
  *
  * seq_len == 0 returns ATTN_OK and enqueues nothing.
  */
@@ -238,8 +238,8 @@ attn_status_t attn_bwd_decode(const float* q, const float* K, const float* V, co
 /*
  * attn_bwd_plan -- host-side query (no GPU work): the most workspace bytes
  * one attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes (that
- * of a call with a seg, with head splits where they apply; plain causal and
- * RoPE calls take no splits), and whether its key-major pass reads stored
+ * of a call with a seg, with head splits where they apply; plain causal
+ * calls take no splits), and whether its key-major pass reads stored
  * probability tiles (1) or recomputes them (0).  Either output pointer may
  * be NULL.  Same argument checks as attn_bwd.
  */

@@ -189,9 +189,11 @@ def test_forward_empty_rows():
 
 # (S, H, KV, d, splits): calls with a seg whose key-major pass has few
 # workgroups (64-key tiles x KV heads) split each group's heads over `splits`
-# workgroups; their partial dK, dV go through the workspace.  The plan's
-# workspace size shows the split count; parity with nonzero initial outputs
-# (the += contract through the partial sums) and through both entries.
+# workgroups; the first adds into dK, dV, the others' partial sums go
+# through the workspace.  The plan's workspace size shows the split count;
+# parity with nonzero initial outputs (the += contract through the partial
+# sums) through attn_bwd and attn_bwd_rope (each partial rotated back on its
+# own), and through attn_bwd_o.
 HEAD_SPLITS = [
     (100, 4, 2, 64, 2),
     (130, 8, 2, 96, 4),
@@ -201,16 +203,17 @@ HEAD_SPLITS = [
 
 
 @pytest.mark.parametrize("case", HEAD_SPLITS, ids=lambda c: "S%dH%dKV%dd%d_x%d" % c)
-@pytest.mark.parametrize("with_o", [False, True])
-def test_head_splits_parity(case, with_o):
+@pytest.mark.parametrize("mode", ["plain", "o", "rope"])
+def test_head_splits_parity(case, mode):
     S, H, KV, d, splits = case
     nbytes, stored = binding.bwd_plan(S, H, KV, d)
     nblk = (S + 31) // 32
     up = lambda n: (n + 255) // 256 * 256
     meta = up(up(up(S * H * 4) + 2 * nblk * 4) + (nblk + 1) * 8)
     tiles = nblk * (nblk + 1) // 2 * H * 8192
-    assert stored and nbytes == meta + tiles + 2 * splits * S * KV * d * 4
+    assert stored and nbytes == meta + tiles + 2 * (splits - 1) * S * KV * d * 4
     rng = np.random.default_rng(4400 + S + H)
     p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, "docs"))
     init = [rng.standard_normal(p[k].shape).astype(np.float32) for k in ("Q", "K", "V")]
-    check_full(p, "head splits x%d" % splits, init=init, with_o=with_o)
+    check_full(p, "head splits x%d %s" % (splits, mode), init=init, with_o=mode == "o",
+               rope=(10000.0, 7) if mode == "rope" else None)
