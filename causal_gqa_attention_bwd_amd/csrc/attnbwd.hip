@@ -746,6 +746,15 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
       if (visible_tile(t)) return t;
     return -1;
   };
+  auto next_tile = [&](int t) {  // smallest visible tile index >= t, or -1
+    for (; t < nqt; ++t)
+      if (visible_tile(t)) return t;
+    return -1;
+  };
+  // paired: the upper half of the key tiles sweeps the query tiles upwards
+  // (the mirrors start at staggered times; upwards they read the same query
+  // tile together, as the first tiles do downwards)
+  const bool up = a.pair && 2 * kt > (S + BC - 1) / BC - 1;
   TileLoader<BR, DP> ld;
   ld.init(qstride, d, wave, lane);
   const uint32_t lds_qg = lds_addr(&sQG[0][0]);
@@ -773,10 +782,10 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   auto next_item = [&](int t, int hx, int& nt, int& nh) {  // item after (t, hx), nt = -1 at the end
     nt = t;
     nh = hx + 1;
-    if (nh == g) { nh = 0; nt = prev_tile(t - 1); }
+    if (nh == g) { nh = 0; nt = up ? next_tile(t + 1) : prev_tile(t - 1); }
   };
 
-  int qt = prev_tile(nqt - 1), hh = 0, buf = 0;
+  int qt = up ? next_tile(qt0) : prev_tile(nqt - 1), hh = 0, buf = 0;
   int nqt_ = -1, nhh = 0;
   uint32_t bmax = 0;
   if (qt >= 0) {

@@ -2,15 +2,15 @@
 
 With a plain causal mask every workgroup serves a tile and its mirror
 (n - 1 - t), so the grids halve; each tile's arithmetic is unchanged, except
-that with stored tiles the dK/dV pass sweeps a mirror tile's query tiles
-upwards (so that the workgroups read the same Q and dO rows at the same
-time), which reorders the fp32 sums of those dK and dV rows.  The results
-must therefore equal, bit for bit, those of the same problem given an
-all-zero seg (served one tile per workgroup, and held to the oracle by the
-other parity tests), in every mode: stored tiles and recomputed scores, the
-row term computed or read off the forward output, with and without the RoPE
-backward -- dK and dV with stored tiles to rounding only (1e-4 of their
-largest entry, a twentieth of the parity bound).  Unpaired calls of few key
+that the dK/dV pass sweeps a mirror tile's query tiles upwards (so that the
+workgroups read the same Q and dO rows at the same time), which reorders the
+fp32 sums of those dK and dV rows.  The results must therefore equal, bit
+for bit, those of the same problem given an all-zero seg (served one tile
+per workgroup, and held to the oracle by the other parity tests), in every
+mode: stored tiles and recomputed scores, the row term computed or read off
+the forward output, with and without the RoPE backward -- dK and dV to
+rounding only (1e-4 of their largest entry, a twentieth of the parity
+bound).  Unpaired calls of few key
 tiles also split each group's heads over workgroups whose partial dK, dV are
 summed afterwards, which reorders those sums once more.  The shapes give odd and even tile counts of both tile heights,
 ragged last tiles, and sequences shorter than one tile.  A few are also held
@@ -67,7 +67,7 @@ def test_paired_equals_unpaired(shape, mode, entry, monkeypatch):
     # holds rounding noise only: its bound is then relative to the largest one
     overall = max(float(np.max(np.abs(b - i0))) for b, i0 in zip(unpaired, init))
     for name, a, b, i0 in zip(("dQ", "dK", "dV"), paired, unpaired, init):
-        if mode == "stored" and name != "dQ":
+        if name != "dQ":
             ref = max(float(np.max(np.abs(b - i0))), 1e-2 * overall, 1e-30)
             e = float(np.max(np.abs(a - b))) / ref
             assert e <= ROUNDING, f"{name}: paired and unpaired schedules differ by {e:.2e}"
