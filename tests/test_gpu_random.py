@@ -7,7 +7,7 @@ see no key), so they reach the paired and unpaired schedules, the head
 splits and the fp16 full-block steps in combinations the fixed lists do not.
 Also random shapes through attn_bwd_short (its range: S <= 1024, head_dim <=
 64), attn_bwd_rope (random position offsets) and attn_bwd_decode.  Bars as in
-the fixed tests: 2e-3 of the largest gradient for fp32 operands, 1e-2 for
+the fixed tests: 2e-3 of the largest gradient for fp32 operands, 2e-2 for
 fp16 operands on such small shapes (the fp16 tests explain it)."""
 import numpy as np
 import pytest
