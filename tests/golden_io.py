@@ -1,7 +1,7 @@
 """Reader of the hand-worked fixtures under tests/golden/.
 
 A fixture is text: '#' comments, then lines 'name token token ...'.  A token is a
-number or an expression over numbers and ln (the natural log); it is evaluated
+number or an expression over numbers, ln (the natural log) and inf; it is evaluated
 with nothing else in scope.  Shapes come from the S, H, KV, d lines.
 """
 import math
@@ -17,7 +17,7 @@ _SHAPES = {"Q": "SHd", "dO": "SHd", "O": "SHd", "dQ": "SHd",
 
 
 def _value(tok):
-    return float(eval(tok, {"__builtins__": {}}, {"ln": math.log}))
+    return float(eval(tok, {"__builtins__": {}}, {"ln": math.log, "inf": math.inf}))
 
 
 def golden_files():
