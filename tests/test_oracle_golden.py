@@ -50,3 +50,35 @@ def test_fixture_reader_pads_without_changing_the_problem(oracle_mod):
                                          g["scale"])
     for name, got in (("dQ", dQ), ("dK", dK), ("dV", dV)):
         np.testing.assert_allclose(got, g[name], rtol=0, atol=1e-13, err_msg=name)
+
+
+def golden_fails(oracle):
+    """Names of the hand-worked fixtures whose values the given oracle misses."""
+    failed = []
+    for path in FILES:
+        g = load_golden(path)
+        with np.errstate(all="ignore"):
+            O, LSE = oracle.attn_fwd_f64(g["Q"], g["K"], g["V"], g["seg"], g["scale"])
+            got = [LSE, O] + list(oracle.attn_bwd_f64(g["Q"], g["K"], g["V"], g["dO"], g["LSE"],
+                                                      g["seg"], g["scale"]))
+        want = [g[n] for n in ("LSE", "O", "dQ", "dK", "dV")]
+        if not all(np.allclose(a, b, rtol=0, atol=1e-13) for a, b in zip(got, want)):
+            failed.append(path)
+    return failed
+
+
+@pytest.mark.parametrize("name", ["none", "drop_D_term", "flip_dS_sign", "drop_scale_in_dS",
+                                  "drop_diagonal_in_dKdV", "ignore_doc_mask_in_dKdV",
+                                  "wrong_group_map", "dK_uses_dO", "dV_uses_dS", "P_ignores_LSE",
+                                  "fwd_drops_max", "dQ_uses_V"])
+def test_hand_worked_examples_alone_catch_planted_mistakes(oracle_mod, tmp_path, name):
+    """The same planted mistakes as the other pins face (a copy of the oracle's
+    C source, edited, built apart): the fixtures by themselves catch each."""
+    from tests.test_oracle_mutants import build_mutant
+    so = build_mutant(tmp_path, name)
+    with oracle_mod._use_library(so):
+        failed = golden_fails(oracle_mod)
+    if name == "none":
+        assert failed == [], failed
+    else:
+        assert failed, f"the hand-worked examples miss mutant {name}"
