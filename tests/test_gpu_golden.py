@@ -68,25 +68,40 @@ def test_forward_matches_hand_worked(path):
     check(O, g["O"], TOL32, "O")
 
 
-def test_decode_matches_row_1_of_hand_worked():
-    path = next(f for f in FILES if f.endswith("hand_worked_s3_h2_kv1_d1.txt"))
+# Row 1's part of each hand derivation (keys 0 and 1): dK and dV per key, column 0, [T, KV].
+ROW1 = {
+    "hand_worked_s3_h2_kv1_d1.txt": ([[-0.75 * np.log(3)], [0.75 * np.log(3)]],
+                                     [[0.75], [1.25]]),
+    "hand_worked_s4_h4_kv2_d1.txt": ([[-2 / 3 * np.log(2)] * 2, [2 / 3 * np.log(2)] * 2],
+                                     [[4 / 3, 5 / 6], [5 / 3, 7 / 6]]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(ROW1))
+def test_decode_matches_row_1_of_hand_worked(name):
+    path = next(f for f in FILES if f.endswith(name))
     print(f"golden {path.rsplit('/', 1)[-1]} row 1 through attn_bwd_decode", flush=True)
     g = pad_head_dim(load_golden(path), 16)
-    assert g["seg"][1] == 0 and g["KV"] == 1      # row 1 sees keys 0 and 1 of KV head 0
+    assert g["seg"][1] == 0                        # row 1 sees keys 0 and 1
     T = 2
     q = g["Q"][1]                                  # [H, d]
     K, V = g["K"][:T], g["V"][:T]                  # [T, KV, d]
-    P = np.exp(g["scale"] * (q @ K[:, 0, :].T) - g["LSE"][1][:, None])   # [H, T]
+    grp = np.arange(g["H"]) // (g["H"] // g["KV"])  # KV head of each query head
+    Kh, Vh = K[:, grp, :], V[:, grp, :]            # [T, H, d]
+    P = np.exp(g["scale"] * np.einsum("hd,thd->ht", q, Kh) - g["LSE"][1][:, None])   # [H, T]
     # row 1's part of the hand derivation: dS = scale*P*(dP - D) with D = sum_j P*dP
-    dP = g["dO"][1] @ V[:, 0, :].T
+    dP = np.einsum("hd,thd->ht", g["dO"][1], Vh)
     dS = g["scale"] * P * (dP - np.sum(P * dP, axis=1, keepdims=True))
-    want_dq = dS @ K[:, 0, :]
-    want_dK = (dS.T @ q)[:, None, :]
-    want_dV = (P.T @ g["dO"][1])[:, None, :]
+    want_dq = np.einsum("ht,thd->hd", dS, Kh)
+    want_dK = np.zeros_like(K)
+    want_dV = np.zeros_like(V)
+    for h in range(g["H"]):
+        want_dK[:, grp[h], :] += dS[h][:, None] * q[h]
+        want_dV[:, grp[h], :] += P[h][:, None] * g["dO"][1][h]
     # the same numbers the fixture's derivation writes out for row 1
     assert np.allclose(want_dq[:, 0], g["dQ"][1][:, 0])
-    assert np.allclose(want_dK[:, 0, 0], [-0.75 * np.log(3), 0.75 * np.log(3)])
-    assert np.allclose(want_dV[:, 0, 0], [0.75, 1.25])
+    assert np.allclose(want_dK[:, :, 0], ROW1[name][0])
+    assert np.allclose(want_dV[:, :, 0], ROW1[name][1])
     t = [to_dev(x.astype(np.float32)) for x in (q, K, V, P, g["dO"][1])]
     dq, dK, dV = torch.zeros_like(t[0]), torch.zeros_like(t[1]), torch.zeros_like(t[2])
     binding.attn_bwd_decode(*t, dq, dK, dV, float(g["scale"]))
