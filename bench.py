@@ -78,9 +78,11 @@ def read_traffic(kname, workload):
         return None
 
 
-def cpu_baseline(x, groups):
+def cpu_baseline(x, groups, with_o=False, rope=None):
     """The oracle's backward on a bounded sample (the first `groups` KV groups:
-    all S rows, `groups` KV heads and their query heads), timed on host cores."""
+    all S rows, `groups` KV heads and their query heads), timed on host cores.
+    Returns (the baseline record, the sample's inputs with the oracle's LSE
+    (and O when with_o), the oracle's gradients of the sample)."""
     import numpy as np
     import oracle
     w = x["workload"]
@@ -91,10 +93,12 @@ def cpu_baseline(x, groups):
     dO = np.ascontiguousarray(x["dO"][:, :nh])
     K = np.ascontiguousarray(x["K"][:, :groups])
     V = np.ascontiguousarray(x["V"][:, :groups])
+    # the machine's CPU share for one GPU is 16 threads (its OMP_NUM_THREADS)
     threads = min(16, len(os.sched_getaffinity(0)))
-    _, lse = oracle.attn_fwd(Q, K, V, x["seg"], x["scale"], nthreads=threads, want_o=False)
+    O, lse = oracle.attn_fwd(Q, K, V, x["seg"], x["scale"], nthreads=threads, want_o=with_o)
     t0 = time.perf_counter()
-    oracle.attn_bwd(Q, K, V, dO, lse, x["seg"], x["scale"], nthreads=threads)
+    ref = oracle.attn_bwd(Q, K, V, dO, lse, x["seg"], x["scale"], nthreads=threads, O=O,
+                          rope=rope)
     dt = time.perf_counter() - t0
     flops = 10.0 * w.d * nh * valid_pairs(x["seg"])
     cpu_model = ""
@@ -105,11 +109,164 @@ def cpu_baseline(x, groups):
                 break
     except OSError:
         pass
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"oracle attn_bwd (fp64 C, {threads} threads) on KV heads 0..{groups - 1} "
-                      f"({nh} of {w.H} query heads, all {w.S} rows) of the same workload; "
-                      f"{dt:.2f} s wall; {cpu_model}",
-            "seconds": dt}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"oracle attn_bwd (fp64 C, {threads} threads) on KV heads 0..{groups - 1} "
+                     f"({nh} of {w.H} query heads, all {w.S} rows) of the same workload; "
+                     f"{dt:.2f} s wall; {cpu_model}",
+           "seconds": dt}
+    sample = dict(Q=Q, K=K, V=V, dO=dO, seg=x["seg"], scale=x["scale"], LSE=lse, O=O)
+    return rec, sample, ref
+
+
+def parity_errors(sample, ref, entry, with_o, rope=None):
+    """The timed entry once more on the oracle's sample, on zeroed outputs and
+    the oracle's LSE (and O): max|gpu - oracle| / max|oracle| per gradient."""
+    import numpy as np
+    import torch
+    from causal_gqa_attention_bwd_amd import binding
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(np.ascontiguousarray(sample[k])).to(dev)
+         for k in ("Q", "K", "V", "dO", "LSE")}
+    O = torch.from_numpy(sample["O"]).to(dev) if with_o else None
+    seg = (None if not np.any(sample["seg"]) else
+           torch.from_numpy(sample["seg"].astype(np.int32)).to(dev))
+    out = [torch.zeros_like(t["Q"]), torch.zeros_like(t["K"]), torch.zeros_like(t["V"])]
+    sc = float(sample["scale"])
+    args = (t["Q"], t["K"], t["V"])
+    if entry == "attn_bwd":
+        binding.attn_bwd(*args, t["dO"], t["LSE"], seg, *out, sc)
+    elif entry == "attn_bwd_o":
+        binding.attn_bwd_o(*args, O, t["dO"], t["LSE"], seg, *out, sc)
+    elif entry == "attn_bwd_rope":
+        binding.attn_bwd_rope(*args, O, t["dO"], t["LSE"], seg, *out, sc, rope[0], rope[1])
+    else:
+        getattr(binding, entry)(*args, O, t["dO"], t["LSE"], seg, *out, sc)
+    torch.cuda.synchronize()
+    errs = {}
+    for name, g, r in zip(("dQ", "dK", "dV"), out, ref):
+        g = g.cpu().numpy().astype(np.float64)
+        errs[name] = float(np.max(np.abs(g - r))) / max(float(np.max(np.abs(r))), 1e-30)
+    return errs
+
+
+def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
+    """Time `steps` calls of one backward entry on workload `wid` (inputs in
+    HBM, LSE and O from attn_fwd_lse beforehand, untimed) between HIP events;
+    the library's measurement hooks give each pass's device time.  Returns the
+    figures of the step and of its dominant kernel."""
+    import numpy as np
+    import torch
+
+    from causal_gqa_attention_bwd_amd import binding
+    from causal_gqa_attention_bwd_amd.workloads import make_inputs
+
+    dev = torch.device("cuda:0")
+    x = make_inputs(wid)
+    w = x["workload"]
+    log(f"bench: workload {w.name}: S={w.S} H={w.H} KV={w.KV} d={w.d}, {entry}")
+    t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev) for k in ("Q", "K", "V", "dO")}
+    seg_np = x["seg"]
+    seg = None if not np.any(seg_np) else torch.from_numpy(seg_np.astype(np.int32)).to(dev)
+    scale = float(x["scale"])
+    lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
+    O = torch.empty_like(t["Q"]) if with_o else None
+    binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, O, lse, scale)
+    ws_bytes, heads = binding.bwd_plan_heads(w.S, w.H, w.KV, w.d)
+    stored = heads > 0
+    dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
+    f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + 2 * w.S * w.H * 4
+    if entry == "attn_bwd_f16":
+        log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
+    elif entry != "attn_bwd_short":
+        log(f"bench: workspace at most {ws_bytes / 2**30:.2f} GiB (attn_bwd_plan), "
+            + (f"stored probability tiles for {heads} heads at a time" if stored
+               else "recomputed probability tiles"))
+    dQ = torch.zeros_like(t["Q"])
+    dK = torch.zeros_like(t["K"])
+    dV = torch.zeros_like(t["V"])
+    torch.cuda.synchronize()
+    a = (t["Q"], t["K"], t["V"])
+
+    def step():
+        if entry == "attn_bwd":
+            binding.attn_bwd(*a, t["dO"], lse, seg, dQ, dK, dV, scale)
+        elif entry == "attn_bwd_o":
+            binding.attn_bwd_o(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale)
+        elif entry == "attn_bwd_rope":
+            binding.attn_bwd_rope(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale, 10000.0, 0)
+        else:
+            getattr(binding, entry)(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    calibration_copy(calib_copy_mb, dev)
+
+    binding.profile_begin()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_q, ms_k, ms_s, ncalls = binding.profile_end()
+    ms_step = e0.elapsed_time(e1) / steps
+    assert ncalls == steps, (ncalls, steps)
+    if not (torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()):
+        raise RuntimeError("non-finite gradients")
+
+    npairs = valid_pairs(seg_np)
+    flops = 10.0 * w.d * w.H * npairs
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    # the passes, with the algorithmic flops per visible (pair, head) of each
+    # (2*d per contraction): with stored tiles k_dq forms S = Q.K^T and
+    # dP = dO.V^T, k_dkdv_p P^T.dO and dS^T.Q, k_dqs dS.K; recomputing, k_dq
+    # forms Q.K^T, dO.V^T and dS.K (with the row term), k_dkdv all four
+    # (the O entry's row-term kernel, k_rowdot, runs before the first pass and
+    # is in ms_per_step only)
+    # attn_bwd_f16: the fp16 copies plus the row term (S and dP once more when
+    # no forward output is given), k_kv16 (S, dP, P^T.dO, dS^T.Q) and k_q16
+    # (S, dP, dS.K)
+    # attn_bwd_short: one launch whose key-role workgroups form S, dP, P^T.dO,
+    # dS^T.Q and whose query-role workgroups form S, dP, dS.K (14 d per pair
+    # and head together), after a row-term launch (S, dP) when no O is given
+    if entry == "attn_bwd_short":
+        passes = ([("k_short", ms_q, 14.0)] if with_o else
+                  [("k_short_rowterm", ms_q, 4.0), ("k_short", ms_k, 14.0)])
+    elif entry == "attn_bwd_f16":
+        passes = [("k_cvt16", ms_q, 0.0 if with_o else 4.0), ("k_kv16", ms_k, 8.0),
+                  ("k_q16", ms_s, 6.0)]
+    elif stored:
+        passes = [("k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0), ("k_dqs", ms_s, 2.0)]
+    else:
+        passes = [("k_dq", ms_q, 6.0), ("k_dkdv", ms_k, 8.0)]
+    kernel_ms = {n: round(tt / ncalls, 4) for n, tt, _ in passes}
+
+    # dominant kernel: algorithmic flops per launch / its measured average duration
+    kname, kms_sum, per_pair = max(passes, key=lambda p: p[1])
+    kms = kms_sum / ncalls
+    kflops = per_pair * w.d * w.H * npairs
+    kach = kflops / (kms * 1e-3) / 1e12
+    peak = PEAK_FP16_MFMA if entry == "attn_bwd_f16" else PEAK_FP32_MFMA
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
+                "peak": peak, "unit": "TFLOP/s", "frac": round(kach / peak, 4),
+                "traffic": read_traffic(kname, w.name), "avg_launch_ms": round(kms, 4)}
+    # general path: attn_bwd_plan's figure, the most a call of this size takes
+    # (with a seg: head-split partial sums); fp16: the operand copies, D and
+    # LSE*log2e, before any partial sums; short: the row term D
+    ws_key = ("row_term_bytes" if entry == "attn_bwd_short" else
+              "fp16_copies_bytes" if entry == "attn_bwd_f16" else "workspace_bytes_max")
+    ws_val = (0 if entry == "attn_bwd_short" and with_o else
+              w.S * w.H * 4 if entry == "attn_bwd_short" else
+              f16_ws if entry == "attn_bwd_f16" else ws_bytes)
+    del t, dQ, dK, dV, lse, O
+    torch.cuda.empty_cache()
+    return dict(workload=w, inputs=x, ms_step=ms_step, tflops=tflops, flops=flops, npairs=npairs,
+                kernel_ms=kernel_ms, roofline=roofline, peak=peak,
+                stored=None if entry in ("attn_bwd_f16", "attn_bwd_short") else stored,
+                ws_key=ws_key, ws_bytes=ws_val)
 
 
 def calibration_copy(mb, dev):
@@ -238,6 +395,9 @@ def main():
     ap.add_argument("--f16", action="store_true",
                     help="time attn_bwd_f16 (fp16 matrix-core operands, fp32 accumulation; with "
                          "--o-entry the forward output is passed)")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="skip the extra timings (S=16384 documents in fp32, S=4096 with fp16 "
+                         "operands) that the default run adds to config.extra")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no "
@@ -251,115 +411,45 @@ def main():
     import numpy as np
     import torch
 
-    from causal_gqa_attention_bwd_amd import binding
-    from causal_gqa_attention_bwd_amd.workloads import make_inputs
+    entry = ("attn_bwd_short" if args.short else "attn_bwd_f16" if args.f16 else
+             "attn_bwd_rope" if args.rope else "attn_bwd_o" if args.o_entry else "attn_bwd")
+    r = time_entry(args.workload, entry, args.o_entry, args.steps, args.warmup, args.calib_copy_mb)
+    w, x = r["workload"], r["inputs"]
+    log(f"bench: {r['ms_step']:.3f} ms/step, "
+        + ", ".join(f"{n} {t:.3f} ms" for n, t in r["kernel_ms"].items())
+        + f", {r['tflops']:.2f} TFLOP/s credited")
 
-    dev = torch.device("cuda:0")
-    x = make_inputs(args.workload)
-    w = x["workload"]
-    log(f"bench: workload {w.name}: S={w.S} H={w.H} KV={w.KV} d={w.d}")
-    t = {k: torch.from_numpy(np.ascontiguousarray(x[k])).to(dev) for k in ("Q", "K", "V", "dO")}
-    seg_np = x["seg"]
-    seg = None if not np.any(seg_np) else torch.from_numpy(seg_np.astype(np.int32)).to(dev)
-    scale = float(x["scale"])
-    lse = torch.empty((w.S, w.H), dtype=torch.float32, device=dev)
-    O = torch.empty_like(t["Q"]) if args.o_entry else None
-    binding.attn_fwd_lse(t["Q"], t["K"], t["V"], seg, O, lse, scale)
-    ws_bytes, stored = binding.bwd_plan(w.S, w.H, w.KV, w.d)
-    dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
-    f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + 2 * w.S * w.H * 4
-    if args.f16:
-        log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
-    else:
-        log(f"bench: workspace at most {ws_bytes / 2**30:.2f} GiB (attn_bwd_plan), "
-            f"{'stored' if stored else 'recomputed'} probability tiles")
-    dQ = torch.zeros_like(t["Q"])
-    dK = torch.zeros_like(t["K"])
-    dV = torch.zeros_like(t["V"])
-    torch.cuda.synchronize()
-
-    def step():
-        if args.short:
-            binding.attn_bwd_short(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
-        elif args.f16:
-            binding.attn_bwd_f16(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
-        elif args.rope:
-            binding.attn_bwd_rope(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale,
-                                  10000.0, 0)
-        elif args.o_entry:
-            binding.attn_bwd_o(t["Q"], t["K"], t["V"], O, t["dO"], lse, seg, dQ, dK, dV, scale)
-        else:
-            binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], lse, seg, dQ, dK, dV, scale)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    calibration_copy(args.calib_copy_mb, dev)
-
-    binding.profile_begin()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms_q, ms_k, ms_s, ncalls = binding.profile_end()
-    ms_step = e0.elapsed_time(e1) / args.steps
-    assert ncalls == args.steps, (ncalls, args.steps)
-    if not (torch.isfinite(dQ).all() and torch.isfinite(dK).all() and torch.isfinite(dV).all()):
-        raise RuntimeError("non-finite gradients")
-
-    npairs = valid_pairs(seg_np)
-    flops = 10.0 * w.d * w.H * npairs
-    tflops = flops / (ms_step * 1e-3) / 1e12
-    # the passes, with the algorithmic flops per visible (pair, head) of each
-    # (2*d per contraction): with stored tiles k_dq forms S = Q.K^T and
-    # dP = dO.V^T, k_dkdv_p P^T.dO and dS^T.Q, k_dqs dS.K; recomputing, k_dq
-    # forms Q.K^T, dO.V^T and dS.K (with the row term), k_dkdv all four
-    # (the O entry's row-term kernel, k_rowdot, runs before the first pass and
-    # is in ms_per_step only)
-    # attn_bwd_f16: the fp16 copies plus the row term (S and dP once more when
-    # no forward output is given), k_kv16 (S, dP, P^T.dO, dS^T.Q) and k_q16
-    # (S, dP, dS.K)
-    # attn_bwd_short: one launch whose key-role workgroups form S, dP, P^T.dO,
-    # dS^T.Q and whose query-role workgroups form S, dP, dS.K (14 d per pair
-    # and head together), after a row-term launch (S, dP) when no O is given
-    if args.short:
-        passes = ([("k_short", ms_q, 14.0)] if args.o_entry else
-                  [("k_short_rowterm", ms_q, 4.0), ("k_short", ms_k, 14.0)])
-    elif args.f16:
-        passes = [("k_cvt16", ms_q, 0.0 if args.o_entry else 4.0), ("k_kv16", ms_k, 8.0),
-                  ("k_q16", ms_s, 6.0)]
-    elif stored:
-        passes = [("k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0), ("k_dqs", ms_s, 2.0)]
-    else:
-        passes = [("k_dq", ms_q, 6.0), ("k_dkdv", ms_k, 8.0)]
-    kernel_ms = {n: round(t / ncalls, 4) for n, t, _ in passes}
-    log(f"bench: {ms_step:.3f} ms/step, " + ", ".join(f"{n} {t:.3f} ms" for n, t in kernel_ms.items())
-        + f", {tflops:.2f} TFLOP/s credited")
-
-    # dominant kernel: algorithmic flops per launch / its measured average duration
-    kname, kms_sum, per_pair = max(passes, key=lambda p: p[1])
-    kms = kms_sum / ncalls
-    kflops = per_pair * w.d * w.H * npairs
-    traffic = read_traffic(kname, w.name)
-    kach = kflops / (kms * 1e-3) / 1e12
-    peak = PEAK_FP16_MFMA if args.f16 else PEAK_FP32_MFMA
-    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
-                "peak": peak, "unit": "TFLOP/s", "frac": round(kach / peak, 4),
-                "traffic": traffic, "avg_launch_ms": round(kms, 4)}
-
-    cpu = None
+    cpu = errs = None
     if args.cpu_groups > 0:
         log("bench: timing the oracle on the host ...")
-        cpu = cpu_baseline(x, args.cpu_groups)
+        rope = (10000.0, 0) if args.rope else None
+        cpu, sample, ref = cpu_baseline(x, args.cpu_groups, with_o=args.o_entry, rope=rope)
         log(f"bench: oracle {cpu['value'] * 1e3:.2f} GFLOP/s on {cpu['cores']} threads "
             f"({cpu['seconds']:.1f} s)")
         cpu = {k: (round(v, 6) if isinstance(v, float) else v) for k, v in cpu.items()
                if k != "seconds"}
+        errs = parity_errors(sample, ref, entry, args.o_entry, rope)
+        log("bench: parity against the oracle on the same sample: "
+            + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
 
+    extra = None
+    if args.extra and entry == "attn_bwd" and args.workload == 4:
+        extra = {}
+        for key, wid, ent in (("s16384_h16_kv2_d256_docs_geom2048_f32", 5, "attn_bwd"),
+                              ("s4096_h32_kv8_d128_causal_f16", 4, "attn_bwd_f16")):
+            log(f"bench: extra: {ent} on workload {wid}")
+            e = time_entry(wid, ent, False, max(5, args.steps // 2), args.warmup, 0)
+            extra[key] = {"entry": ent, "ms_per_step": round(e["ms_step"], 4),
+                          "tflops_credited": round(e["tflops"], 3),
+                          "pct_of_peak_dtype": round(100.0 * e["tflops"] / e["peak"], 2),
+                          "kernel_ms": e["kernel_ms"],
+                          "dominant_kernel": e["roofline"]["kernel"],
+                          "dominant_kernel_frac": e["roofline"]["frac"]}
+            log(f"bench: extra: {e['ms_step']:.3f} ms/step, {e['tflops']:.2f} TFLOP/s, "
+                f"{e['roofline']['kernel']} frac {e['roofline']['frac']:.3f}")
+            del e
+
+    tflops, ms_step = r["tflops"], r["ms_step"]
     out = {
         "metric": "attention-backward TFLOP/s (causal FLOPs) and % of MI355X matrix peak",
         "value": round(tflops, 3),
@@ -375,29 +465,28 @@ def main():
         "data": "synthetic",
         "pct_of_peak_fp32_matrix": round(100.0 * tflops / PEAK_FP32_MFMA, 2),
         "pct_of_peak_fp16_matrix": round(100.0 * tflops / PEAK_FP16_MFMA, 3),
+        "err_dq": None if errs is None else errs["dQ"],
+        "err_dk": None if errs is None else errs["dK"],
+        "err_dv": None if errs is None else errs["dV"],
         "config": {"workload": w.name, "seq_len": w.S, "n_heads": w.H, "n_kv_heads": w.KV,
-                   "head_dim": w.d, "mask": "causal" if seg is None else "documents",
-                   "valid_pairs": npairs, "credited_flops_per_step": flops,
+                   "head_dim": w.d, "mask": "causal" if not np.any(x["seg"]) else "documents",
+                   "valid_pairs": r["npairs"], "credited_flops_per_step": r["flops"],
                    # the same time counted on all causal pairs (labelled; differs from value
                    # only under a document mask)
                    "tflops_on_causal_pairs": round(
                        10.0 * w.d * w.H * (w.S * (w.S + 1) // 2) / (ms_step * 1e-3) / 1e12, 3),
                    "device_compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
-                   "entry": ("attn_bwd_short" if args.short else
-                             "attn_bwd_f16" if args.f16 else "attn_bwd_rope" if args.rope else
-                             "attn_bwd_o" if args.o_entry else "attn_bwd"),
+                   "entry": entry,
                    "operands": ("fp16, fp32 accumulation" if args.f16 else "fp32"),
                    "forward_output_given": bool(args.o_entry),
-                   "stored_tiles": None if args.f16 or args.short else stored,
-                   # general path: attn_bwd_plan's figure, the most a call of this size
-                   # takes (with a seg: head-split partial sums); fp16: the operand
-                   # copies, D and LSE*log2e, before any partial sums; short: the row term D
-                   ("row_term_bytes" if args.short else "fp16_copies_bytes" if args.f16 else
-                    "workspace_bytes_max"):
-                       (0 if args.short and args.o_entry else
-                        w.S * w.H * 4 if args.short else f16_ws if args.f16 else ws_bytes),
-                   "kernel_ms": kernel_ms},
-        "roofline": roofline,
+                   "stored_tiles": r["stored"],
+                   # errors: max|gpu - oracle| / max|oracle| per gradient over the oracle's
+                   # sample (cpu_baseline.sample), on zeroed outputs and the oracle's LSE
+                   "parity_sample": None if cpu is None else cpu["sample"].split(";")[0],
+                   r["ws_key"]: r["ws_bytes"],
+                   "kernel_ms": r["kernel_ms"],
+                   "extra": extra},
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

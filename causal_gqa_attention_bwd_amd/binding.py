@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_o", "attn_bwd_plan",
             "attn_bwd_rope", "attn_bwd_short", "attn_fwd_lse", "attn_last_error",
-            "attn_profile_begin", "attn_profile_end")
+            "attn_profile_begin", "attn_profile_end", "attn_set_scratch_limit")
 
 _lib = None
 
@@ -51,6 +51,8 @@ def load():
     lib.attn_bwd_plan.argtypes = [I, I, I, I, ctypes.POINTER(ctypes.c_size_t),
                                   ctypes.POINTER(ctypes.c_int)]
     lib.attn_bwd_plan.restype = I
+    lib.attn_set_scratch_limit.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_size_t)]
+    lib.attn_set_scratch_limit.restype = I
     lib.attn_fwd_lse.argtypes = [P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_fwd_lse.restype = I
     lib.attn_profile_begin.argtypes = []
@@ -84,16 +86,34 @@ def _stream(stream):
 
 
 def _check_tensors(named, dev):
+    """Every tensor must be a contiguous GPU tensor of an accepted dtype on the
+    current HIP device: the C ABI takes device pointers, and a host pointer
+    handed to a kernel would fault the GPU.  Raises ValueError before any
+    launch otherwise."""
     import torch
     for name, t, dtypes in named:
         if t is None:
             continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} is on {t.device}: the library takes GPU tensors only")
         if t.device != dev:
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
         if t.dtype not in dtypes:
             raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+
+
+def _device_of(first):
+    """The device every tensor of a call must be on: the current HIP device
+    (kernels are launched there), checked against the first tensor's."""
+    import torch
+    if first.device.type != "cuda":
+        raise ValueError(f"tensors are on {first.device}: the library takes GPU tensors only")
+    cur = torch.device("cuda", torch.cuda.current_device())
+    if first.device != cur:
+        raise ValueError(f"tensors are on {first.device} but the current device is {cur}")
+    return cur
 
 
 def _dims(Q, K):
@@ -111,7 +131,7 @@ def _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV):
     f32 = (torch.float32,)
     _check_tensors([("Q", Q, f32), ("K", K, f32), ("V", V, f32), ("O", O, f32), ("dO", dO, f32),
                     ("LSE", LSE, f32), ("seg", seg, (torch.int32, torch.uint32)),
-                    ("dQ", dQ, f32), ("dK", dK, f32), ("dV", dV, f32)], Q.device)
+                    ("dQ", dQ, f32), ("dK", dK, f32), ("dV", dV, f32)], _device_of(Q))
     for name, t, shape in (("V", V, K.shape), ("O", O, Q.shape), ("dO", dO, Q.shape),
                            ("LSE", LSE, (S, H)), ("dQ", dQ, Q.shape), ("dK", dK, K.shape),
                            ("dV", dV, K.shape)):
@@ -190,7 +210,7 @@ def attn_bwd_decode(q, K, V, P, dO, dq, dK, dV, scale, stream=None):
         raise ValueError(f"q {tuple(q.shape)} and K {tuple(K.shape)} disagree")
     f32 = (torch.float32,)
     _check_tensors([("q", q, f32), ("K", K, f32), ("V", V, f32), ("P", P, f32), ("dO", dO, f32),
-                    ("dq", dq, f32), ("dK", dK, f32), ("dV", dV, f32)], q.device)
+                    ("dq", dq, f32), ("dK", dK, f32), ("dV", dV, f32)], _device_of(q))
     for name, t, shape in (("V", V, K.shape), ("P", P, (H, T)), ("dO", dO, q.shape),
                            ("dq", dq, q.shape), ("dK", dK, K.shape), ("dV", dV, K.shape)):
         if tuple(t.shape) != tuple(shape):
@@ -207,7 +227,7 @@ def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):
     f32 = (torch.float32,)
     _check_tensors([("Q", Q, f32), ("K", K, f32), ("V", V, f32),
                     ("seg", seg, (torch.int32, torch.uint32)), ("O", O, f32), ("LSE", LSE, f32)],
-                   Q.device)
+                   _device_of(Q))
     if tuple(LSE.shape) != (S, H) or (O is not None and tuple(O.shape) != tuple(Q.shape)):
         raise ValueError("O must be [S,H,d] and LSE [S,H]")
     st = load().attn_fwd_lse(_ptr(Q), _ptr(K), _ptr(V), _ptr(seg), _ptr(O), _ptr(LSE),
@@ -215,13 +235,45 @@ def attn_fwd_lse(Q, K, V, seg, O, LSE, scale, stream=None):
     _raise_on(st, "attn_fwd_lse")
 
 
+def bwd_plan_heads(seq_len, n_heads, n_kv_heads, head_dim):
+    """(workspace bytes, heads per stored-tile chunk) of one attn_bwd call; 0
+    heads: the key-major pass recomputes the scores (nothing stored)."""
+    nbytes = ctypes.c_size_t(0)
+    heads = ctypes.c_int(0)
+    _raise_on(load().attn_bwd_plan(seq_len, n_heads, n_kv_heads, head_dim, ctypes.byref(nbytes),
+                                   ctypes.byref(heads)), "attn_bwd_plan")
+    return int(nbytes.value), int(heads.value)
+
+
 def bwd_plan(seq_len, n_heads, n_kv_heads, head_dim):
     """(workspace bytes, stored probability tiles?) of one attn_bwd call."""
-    nbytes = ctypes.c_size_t(0)
-    stored = ctypes.c_int(0)
-    _raise_on(load().attn_bwd_plan(seq_len, n_heads, n_kv_heads, head_dim, ctypes.byref(nbytes),
-                                   ctypes.byref(stored)), "attn_bwd_plan")
-    return int(nbytes.value), bool(stored.value)
+    nbytes, heads = bwd_plan_heads(seq_len, n_heads, n_kv_heads, head_dim)
+    return nbytes, heads > 0
+
+
+def set_scratch_limit(nbytes):
+    """Set the most bytes of stored probability tiles one call may take
+    (process-wide; the C ABI's attn_set_scratch_limit).  Returns the previous
+    limit."""
+    prev = ctypes.c_size_t(0)
+    _raise_on(load().attn_set_scratch_limit(int(nbytes), ctypes.byref(prev)),
+              "attn_set_scratch_limit")
+    return int(prev.value)
+
+
+class scratch_limit:
+    """Context manager: run a block with another scratch limit, then restore it."""
+
+    def __init__(self, nbytes):
+        self.nbytes = int(nbytes)
+
+    def __enter__(self):
+        self.prev = set_scratch_limit(self.nbytes)
+        return self
+
+    def __exit__(self, *exc):
+        set_scratch_limit(self.prev)
+        return False
 
 
 def profile_begin():

@@ -1,9 +1,13 @@
-"""Build the HIP library in-tree: libattnbwd.so next to this file (gfx950 only)."""
+"""Build the HIP library in-tree: libattnbwd.so next to this file (gfx950 only).
+
+Each source compiles to its own object in parallel (_build/ next to this
+file), then one link makes the shared library."""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -11,30 +15,55 @@ SRCS = [os.path.join(HERE, "csrc", f)
         for f in ("attnbwd.hip", "attnbwd_f16.hip", "attnbwd_decode.hip", "attnbwd_short.hip")]
 LIB = os.path.join(HERE, "libattnbwd.so")
 INCLUDE = os.path.join(ROOT, "include")
+OBJDIR = os.path.join(HERE, "_build")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+# the host compilation pass does not know the GPU feature; that line is expected
+_NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+    err = "\n".join(l for l in res.stderr.splitlines() if _NOISE not in l)
+    return res.returncode, err
 
 
 def build(verbose: bool = False, extra: list | None = None) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-o", tmp, *SRCS]
-    if verbose:
-        print(" ".join(cmd), file=sys.stderr)
-    res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
-    # the host compilation pass does not know the GPU feature; that line is expected
-    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if err.strip():
-        print(err, file=sys.stderr)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
-    os.replace(tmp, LIB)
+    os.makedirs(OBJDIR, exist_ok=True)
+    pid = os.getpid()
+    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".%d.o" % pid) for s in SRCS]
+    cmds = [[hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-c", "-o", o, s]
+            for s, o in zip(SRCS, objs)]
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), cmds))
+    failed = False
+    for rc, err in results:
+        if err.strip():
+            print(err, file=sys.stderr)
+        failed |= rc != 0
+    tmp = LIB + ".tmp%d" % pid
+    try:
+        if failed:
+            raise RuntimeError("hipcc failed")
+        rc, err = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                       verbose)
+        if err.strip():
+            print(err, file=sys.stderr)
+        if rc != 0:
+            raise RuntimeError(f"linking {LIB} failed ({rc})")
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -52,6 +52,8 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <atomic>
+#include <climits>
 #include <map>
 #include <mutex>
 #include <vector>
@@ -67,7 +69,10 @@ struct BwdArgs {
   uint32_t* blk_max;     // [ceil(S/32)] max seg per 32-row query block (k_prep)
   long long* slot_off;   // [ceil(S/32) + 1] first tile slot of each query block (k_prep)
   float* scratch;        // P and P*dP tiles of every visible pair, or NULL
-  int S, H, KV, d;
+  int S, H, KV, d;       // H, KV: the heads this launch covers (a chunk of KV groups, or
+                         // a share of one group's heads; pointers start at its first)
+  int Hs, KVs;           // row strides in heads: Q, dO, dQ, LSE, D rows hold Hs heads,
+                         // K, V, dK, dV (and the partial dK, dV slices) rows KVs
   float scale;
   int pair;              // 1: block p serves tiles p and n-1-p (equal causal work)
   int rope;              // 1: rotate dQ, dK back by RoPE after the += (rope_bwd)
@@ -352,24 +357,35 @@ __global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint3
 
 // ---------------------------------------------------------------------------
 // k_sumparts: dK += sum over splits of part[2 split], dV += sum of
-// part[2 split + 1], split by split in order; n = S * KV * d floats per slice
-// (a multiple of 4: d is a multiple of 16).  Adds the partial sums of the
-// key-major passes that split a group's heads over workgroups.
+// part[2 split + 1], split by split in order, over `rows` rows of `width`
+// floats (a multiple of 4: d is a multiple of 16) that sit `stride` floats
+// apart in dK, dV and each slice (a slice is rows * stride floats).  Adds the
+// partial sums of the key-major passes that split a group's heads over
+// workgroups; with a chunk of KV heads, dK, dV and part start at its first.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_sumparts(const float* __restrict__ part, int splits,
-                                                  long long n, float* dK, float* dV) {
-  const long long n4 = n / 4;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n4;
-       i += (long long)gridDim.x * blockDim.x) {
-    float4 k = reinterpret_cast<float4*>(dK)[i], v = reinterpret_cast<float4*>(dV)[i];
-    for (int s = 0; s < splits; ++s) {
-      const float4 pk = reinterpret_cast<const float4*>(part + (size_t)(2 * s) * n)[i];
-      const float4 pv = reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * n)[i];
-      k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
-      v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+                                                  long long rows, int width, long long stride,
+                                                  float* dK, float* dV) {
+  const size_t slice = (size_t)rows * stride;
+  // tpr threads (a power of two, at most 256) per row, 256 / tpr rows per block
+  const int w4 = width / 4;
+  int tpr = 1;
+  while (tpr < w4 && tpr < 256) tpr <<= 1;
+  const int rpb = 256 / tpr;
+  for (long long r = (long long)blockIdx.x * rpb + threadIdx.x / tpr; r < rows;
+       r += (long long)gridDim.x * rpb) {
+    for (int c4 = threadIdx.x % tpr; c4 < w4; c4 += tpr) {
+      const size_t off = (size_t)r * stride + 4 * c4;
+      float4 k = *reinterpret_cast<float4*>(dK + off), v = *reinterpret_cast<float4*>(dV + off);
+      for (int s = 0; s < splits; ++s) {
+        const float4 pk = *reinterpret_cast<const float4*>(part + (size_t)(2 * s) * slice + off);
+        const float4 pv = *reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * slice + off);
+        k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
+        v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+      }
+      *reinterpret_cast<float4*>(dK + off) = k;
+      *reinterpret_cast<float4*>(dV + off) = v;
     }
-    reinterpret_cast<float4*>(dK)[i] = k;
-    reinterpret_cast<float4*>(dV)[i] = v;
   }
 }
 
@@ -446,7 +462,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   const int i0 = qt * BR;
   const int q = i0 + qb * 32 + l32;
   const bool q_ok = q < S;
-  const size_t qstride = (size_t)H * d, kstride = (size_t)a.KV * d;
+  const size_t qstride = (size_t)a.Hs * d, kstride = (size_t)a.KVs * d;
   const float sc2 = a.scale * ATTN_LOG2E;
   const float* Kh = a.K + (size_t)kvh * d;
   const float* Vh = a.V + (size_t)kvh * d;
@@ -462,8 +478,8 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
     pin_agpr<PG::TH>(gr);
   }
   pin_agpr<PG::TH>(qr);
-  const float lse2 = q_ok ? a.LSE[(size_t)q * H + h] * ATTN_LOG2E : 0.f;
-  const float Dk = (DK && q_ok) ? a.Dws[(size_t)q * H + h] : 0.f;  // given row term
+  const float lse2 = q_ok ? a.LSE[(size_t)q * a.Hs + h] * ATTN_LOG2E : 0.f;
+  const float Dk = (DK && q_ok) ? a.Dws[(size_t)q * a.Hs + h] : 0.f;  // given row term
   const uint32_t sq = (q_ok && a.seg) ? a.seg[q] : 0u;
 
   // smallest document start of the tile bounds the key sweep; the largest one
@@ -625,7 +641,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   if constexpr (!DK) {
     const float Dq = Dp + __shfl_xor(Dp, 32);
     if (ACC && hf == 0) sD[wave * 32 + l32] = Dq;
-    if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * H + h] = Dq;
+    if (q_ok && hf == 0 && role == 0) a.Dws[(size_t)q * a.Hs + h] = Dq;
   }
   if constexpr (ACC) {
     __syncthreads();
@@ -706,7 +722,7 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   const int j0 = kt * BC;
   const int key = j0 + kb * 32 + l32;
   const bool key_ok = key < S;
-  const size_t qstride = (size_t)H * d, kstride = (size_t)KV * d;
+  const size_t qstride = (size_t)a.Hs * d, kstride = (size_t)a.KVs * d;
   const float sc2 = a.scale * ATTN_LOG2E;
 
   // B operands of the score blocks: this lane's key row, half-wave hf's columns
@@ -761,7 +777,7 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
   // per-row values of a tile, one wave-wide 4-byte load per wave: wave 0 LSE,
   // wave 1 D (rows H floats apart), wave 2 seg, wave 3 nothing (empty range
   // into a spare slot); lanes past the tile read nothing
-  const uint32_t row_off = lane < BR ? (uint32_t)(lane * (wave == 2 ? 4 : 4 * H)) : ATTN_BUF_OOB;
+  const uint32_t row_off = lane < BR ? (uint32_t)(lane * (wave == 2 ? 4 : 4 * a.Hs)) : ATTN_BUF_OOB;
   auto row_rsrc = [&](int t, int hh, bool live) {
     const int i0 = t * BR, h = kvh * g + hh;
     const int rows = live ? min(S - i0, BR) : 0;
@@ -769,8 +785,8 @@ __global__ __launch_bounds__(256) void k_dkdv(BwdArgs a) {
     uint32_t nbytes = 0;
     if (rows > 0) {
       if (wave == 0 || wave == 1) {
-        base = (wave == 0 ? a.LSE : a.Dws) + (size_t)i0 * H + h;
-        nbytes = (uint32_t)(((rows - 1) * (size_t)H + 1) * 4);
+        base = (wave == 0 ? a.LSE : a.Dws) + (size_t)i0 * a.Hs + h;
+        nbytes = (uint32_t)(((rows - 1) * (size_t)a.Hs + 1) * 4);
       } else if (wave == 2 && a.seg) {
         base = a.seg + i0;
         nbytes = (uint32_t)(rows * 4);
@@ -1030,7 +1046,7 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
   const bool up = a.pair && 2 * kt > nkt - 1;
   const int kblk = kt * KB + kb;  // this wave's key block
   const int head0 = kvh * g + split * gs;
-  const size_t qstride = (size_t)H * d, kstride = (size_t)KV * d;
+  const size_t qstride = (size_t)a.Hs * d, kstride = (size_t)a.KVs * d;
 
   f32x16 accK[NB], accV[NB];
 #pragma unroll
@@ -1091,12 +1107,12 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
 
   TileLoader<BR, DP> ld;
   ld.init(qstride, d, wave, lane);
-  const uint32_t row_off = lane < BR ? (uint32_t)(lane * 4 * H) : ATTN_BUF_OOB;
+  const uint32_t row_off = lane < BR ? (uint32_t)(lane * 4 * a.Hs) : ATTN_BUF_OOB;
   auto row_rsrc = [&](int t, int hh, bool live) {  // D of the tile's rows (wave 0 only)
     const int i0 = t * BR;
     const int rows = (live && wave == 0) ? min(S - i0, BR) : 0;
-    return buf_rsrc(rows > 0 ? a.Dws + (size_t)i0 * H + head0 + hh : a.Dws,
-                    rows > 0 ? (uint32_t)(((rows - 1) * (size_t)H + 1) * 4) : 0u);
+    return buf_rsrc(rows > 0 ? a.Dws + (size_t)i0 * a.Hs + head0 + hh : a.Dws,
+                    rows > 0 ? (uint32_t)(((rows - 1) * (size_t)a.Hs + 1) * 4) : 0u);
   };
   const uint32_t lds_qg = lds_addr(&sQG[0][0]), lds_row = lds_addr(&sRow[0][wave][0]);
   constexpr uint32_t QG_BYTES = 2 * TILE * 4, ROW_BYTES = 4 * 64 * 4;
@@ -1377,7 +1393,7 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
   const int last_blk = (min(i0 + BR, S) - 1) / 32;
   const bool any = kb_first <= last_blk;
   const int kt_lo = any ? kb_first / KB : 1, kt_hi = any ? last_blk / KB : 0;
-  const size_t kstride = (size_t)a.KV * d;
+  const size_t kstride = (size_t)a.KVs * d;
   const float* Kh = a.K + (size_t)kvh * d;
   // lane's offset in a stored tile: dS[query l32][key crow(r, hf)] sits at
   // st_base + 8*(r/4) + r%4
@@ -1453,7 +1469,7 @@ __global__ __launch_bounds__(256, 2) void k_dqs(BwdArgs a) {
 
   // dQ += scale * acc: all old values are read first, then all written
   float* __restrict__ dQh = a.dQ + (size_t)h * d;
-  const size_t qstride = (size_t)H * d;
+  const size_t qstride = (size_t)a.Hs * d;
   const int col0 = dcol0 + NB * l32;
   float old[16][NB];
 #pragma unroll
@@ -1671,7 +1687,7 @@ extern "C" const char* attn_last_error(void) { return g_err; }
 
 // Per-thread event log of the measurement hooks (see attn_profile_begin):
 // per recorded attn_bwd call, one event before its first pass and one after
-// each of its passes (2 or 3).
+// each of its passes (2 or 3, or 3 per head chunk).
 struct ProfileLog {
   bool on = false;
   std::vector<std::vector<hipEvent_t>> calls;
@@ -1697,12 +1713,13 @@ extern "C" attn_status_t attn_profile_end(double* ms, int* n_calls) {
   attn_status_t rc = ATTN_OK;
   for (size_t i = 0; i < g_prof.calls.size() && rc == ATTN_OK; ++i) {
     const auto& ev = g_prof.calls[i];
-    for (size_t k = 0; k + 1 < ev.size() && k < 3 && rc == ATTN_OK; ++k) {
+    // a call run in head chunks records its three passes once per chunk
+    for (size_t k = 0; k + 1 < ev.size() && rc == ATTN_OK; ++k) {
       float t = 0.f;
       hipError_t e = hipEventSynchronize(ev[k + 1]);
       if (e == hipSuccess) e = hipEventElapsedTime(&t, ev[k], ev[k + 1]);
       if (e != hipSuccess) rc = fail(ATTN_ERR_HIP, "reading profile events: %s", hipGetErrorString(e));
-      sum[k] += t;
+      sum[k % 3] += t;
     }
   }
   if (ms) { ms[0] = sum[0]; ms[1] = sum[1]; ms[2] = sum[2]; }
@@ -1763,12 +1780,12 @@ attn_status_t hip_check(hipError_t e, const char* what) {
 // D was computed beforehand (from the forward output); k_dq then stores
 // dS/scale in place of P*dP, or accumulates dQ from dS alone.
 template <int DP, bool DK>
-static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
+static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st, bool first) {
   // paired (plain causal): block p serves tile p and its mirror, so each grid halves
   auto blocks = [&](int ntiles) { return a.pair ? (ntiles + 1) / 2 : ntiles; };
   const int BRq = Pair<DP>::ROLE ? 64 : 128;
   const int nqt = blocks((a.S + BRq - 1) / BRq);
-  attn_status_t rc = profile_mark(st, true);
+  attn_status_t rc = first ? profile_mark(st, true) : ATTN_OK;
   if (rc != ATTN_OK) return rc;
   if (a.scratch)
     hipLaunchKernelGGL((k_dq<DP, false, DK>), dim3(nqt * a.H), dim3(256), 0, st, a);
@@ -1784,7 +1801,8 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_dkdv<DP>, dim3(nkt * a.KV), dim3(256), 0, st, a);
   rc = hip_check(hipGetLastError(), "launching the dK/dV kernel");
   if (rc == ATTN_OK && a.scratch && a.hsplit > 1)
-    rc = launch_sumparts(a.part, a.hsplit - 1, (long long)a.S * a.KV * a.d, a.dK, a.dV, st);
+    rc = launch_sumparts(a.part, a.hsplit - 1, a.S, a.KV * a.d, (long long)a.KVs * a.d, a.dK,
+                         a.dV, st);
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK || !a.scratch) return rc;
   const int BRs = DP > 128 ? 64 : 128;
@@ -1795,20 +1813,24 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st) {
 }
 
 template <bool DK>
-static attn_status_t launch_bwd(const BwdArgs& a, int dp, hipStream_t st) {
+static attn_status_t launch_bwd(const BwdArgs& a, int dp, hipStream_t st, bool first) {
   switch (dp) {
-    case 32: return launch_dqkv<32, DK>(a, st);
-    case 64: return launch_dqkv<64, DK>(a, st);
-    case 96: return launch_dqkv<96, DK>(a, st);
-    case 128: return launch_dqkv<128, DK>(a, st);
-    case 192: return launch_dqkv<192, DK>(a, st);
-    default: return launch_dqkv<256, DK>(a, st);
+    case 32: return launch_dqkv<32, DK>(a, st, first);
+    case 64: return launch_dqkv<64, DK>(a, st, first);
+    case 96: return launch_dqkv<96, DK>(a, st, first);
+    case 128: return launch_dqkv<128, DK>(a, st, first);
+    case 192: return launch_dqkv<192, DK>(a, st, first);
+    default: return launch_dqkv<256, DK>(a, st, first);
   }
 }
 
-// The library's own stream-ordered memory pool for the per-call workspace:
-// it keeps freed memory for reuse, so large workspaces cost no mapping work
-// after the first call.  One pool per device, created on first use.
+// The library's own stream-ordered memory pool for the per-call workspaces.
+// Freed workspace stays in the pool for later calls, up to ATTN_POOL_KEEP
+// bytes (so a call of S=4096 with 32 heads, 2 GiB, maps nothing new after the
+// first); the pool returns whatever it holds above that to the device at the
+// caller's next synchronisation (its release threshold).  One pool per
+// device, created on first use.
+#define ATTN_POOL_KEEP (4ull << 30)
 static std::mutex g_pool_mu;
 static std::map<int, hipMemPool_t> g_pools;
 
@@ -1829,7 +1851,7 @@ attn_status_t device_pool(hipMemPool_t* out) {
   hipMemPool_t pool;
   rc = hip_check(hipMemPoolCreate(&pool, &props), "hipMemPoolCreate");
   if (rc != ATTN_OK) return rc;
-  uint64_t keep = UINT64_MAX;
+  uint64_t keep = ATTN_POOL_KEEP;
   rc = hip_check(hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep),
                  "hipMemPoolSetAttribute");
   if (rc != ATTN_OK) return rc;
@@ -1845,65 +1867,93 @@ static long long scratch_bound(long long nblk, int H) {
   return nblk * (nblk + 1) / 2 * H * ATTN_TILE_FLOATS * (long long)sizeof(float);
 }
 
-// Scratch budget in bytes: ATTNBWD_SCRATCH_MB (MiB, a decimal number) if set
-// (0 disables the stored tiles), else 32 GiB.
-static long long scratch_budget() {
-  const char* e = getenv("ATTNBWD_SCRATCH_MB");
-  if (e && *e) {
-    const double mb = atof(e);
-    return mb > 0 ? (long long)(mb * (double)(1ll << 20)) : 0;
-  }
-  return 32ll << 30;
+// The most bytes of stored tiles one call may take (attn_set_scratch_limit).
+static std::atomic<long long> g_scratch_limit{32ll << 30};
+
+extern "C" attn_status_t attn_set_scratch_limit(size_t bytes, size_t* previous) {
+  g_err[0] = 0;
+  const long long v = bytes > (size_t)LLONG_MAX ? LLONG_MAX : (long long)bytes;
+  const long long old = g_scratch_limit.exchange(v);
+  if (previous) *previous = (size_t)old;
+  return ATTN_OK;
 }
 
-// How attn_bwd runs a problem: with the stored P / P*dP tiles when their
-// bound fits the budget (tile indices then also stay below 2^31), else with
-// the scores recomputed by the key-major kernel; how many workgroups share a
-// key tile's heads in k_dkdv_p; and the layout of the per-call workspace:
-// D [S, H], per-block seg min/max and slot offsets, the scratch, then the
-// partial dK, dV of the head splits after the first.
+// How attn_bwd runs a problem.  The stored P / P*dP tiles are taken for
+// `chunk` heads at a time: all heads when their causal bound fits the limit,
+// else as many whole KV groups as fit, else the largest divisor of a group's
+// size that fits (the chunks then run one after another, each adding its
+// share into dK, dV); when not even one head's tiles fit, the key-major pass
+// recomputes the scores instead (chunk = n_heads, nothing stored).  hsplit:
+// how many workgroups share a key tile's heads in k_dkdv_p (the most any
+// chunk takes).  Workspace layout: D [S, H], per-block seg min/max and slot
+// offsets, the scratch of one chunk, then the partial dK, dV of the head
+// splits after the first ([S, KV, d] slices).
 struct Plan {
   bool stored = false;
+  int chunk = 0;
   int hsplit = 1;
   size_t off_blk = 0, off_slot = 0, off_scr = 0, off_part = 0, bytes = 0;
 };
 
-// may_split: the call is unpaired (a seg given, or pairing off).  Paired
-// tiles carry equal work; unpaired, under a document mask, the first key tile
-// of a long document can hold more work than a CU's share of the whole pass,
-// so k_dkdv_p splits each group's heads over workgroups until the launch has
-// ~1024 of them (S=16384, 2 KV heads, documents: the longest workgroup came
-// down from 1.3 to 1.12 times the mean load of a CU).
-static Plan make_plan(int S, int H, int KV, int d, bool may_split) {
+// Heads per chunk when `fit` heads' tiles fit the limit (0: none).
+static int chunk_heads(int H, int KV, long long fit) {
+  const int g = H / KV;
+  if (fit >= H) return H;
+  if (fit >= g) return (int)(fit / g) * g;
+  for (int c = (int)fit; c >= 1; --c)
+    if (g % c == 0) return c;
+  return 0;
+}
+
+// Unpaired calls (a seg given): paired tiles carry equal work; unpaired,
+// under a document mask, the first key tile of a long document can hold more
+// work than a CU's share of the whole pass, so k_dkdv_p splits each group's
+// heads over workgroups until the launch has ~1024 of them (S=16384, 2 KV
+// heads, documents: the longest workgroup came down from 1.3 to 1.12 times
+// the mean load of a CU).  Hc heads over KVc KV heads in this launch.
+static int head_splits(int S, int Hc, int KVc) {
+  const long long blocks = ((long long)S + 63) / 64 * KVc;
+  const int gc = Hc / KVc;
+  int hs = 1;
+  while (blocks * hs < 1024 && gc % (2 * hs) == 0) hs *= 2;
+  return hs;
+}
+
+static Plan make_plan(int S, int H, int KV, int d, bool may_split, long long limit) {
   Plan p;
   const long long nblk = ((long long)S + 31) / 32;
-  const long long need = scratch_bound(nblk, H);
-  const long long budget = std::min(scratch_budget(), 0x7fffffffll * ATTN_TILE_FLOATS * 4);
-  p.stored = need > 0 && need <= budget;
+  const long long per_head = scratch_bound(nblk, 1);
+  // tile indices (slot * heads + head) stay below 2^31
+  const long long budget = std::min(limit, 0x7fffffffll * ATTN_TILE_FLOATS * 4);
+  p.chunk = per_head > 0 ? chunk_heads(H, KV, budget / per_head) : 0;
+  p.stored = p.chunk > 0;
+  if (!p.stored) p.chunk = H;
+  const long long need = p.stored ? per_head * p.chunk : 0;
   const size_t nD = (size_t)S * H;
   p.off_blk = (nD * sizeof(float) + 255) & ~(size_t)255;
   p.off_slot = (p.off_blk + 2 * nblk * sizeof(uint32_t) + 255) & ~(size_t)255;
   p.off_scr = (p.off_slot + (nblk + 1) * sizeof(long long) + 255) & ~(size_t)255;
-  p.off_part = (p.off_scr + (p.stored ? (size_t)need : 0) + 255) & ~(size_t)255;
+  p.off_part = (p.off_scr + (size_t)need + 255) & ~(size_t)255;
   if (p.stored && may_split) {
-    const long long blocks = ((long long)S + 63) / 64 * KV;
     const int g = H / KV;
-    while (blocks * p.hsplit < 1024 && g % (2 * p.hsplit) == 0) p.hsplit *= 2;
+    const int last = H % p.chunk ? H % p.chunk : p.chunk;  // a smaller last chunk
+    p.hsplit = std::max(head_splits(S, p.chunk, std::max(1, p.chunk / g)),
+                        head_splits(S, last, std::max(1, last / g)));
   }
   p.bytes = p.hsplit > 1 ? p.off_part + (size_t)2 * (p.hsplit - 1) * S * KV * d * sizeof(float)
-                         : p.off_scr + (p.stored ? (size_t)need : 0);
+                         : p.off_scr + (size_t)need;
   return p;
 }
 
 extern "C" attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads, int head_dim,
-                                       size_t* workspace_bytes, int* stored_tiles) {
+                                       size_t* workspace_bytes, int* stored_heads) {
   g_err[0] = 0;
   attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, 1.f);
   if (rc != ATTN_OK) return rc;
   // the most a call of this size takes: an unpaired one, with head splits
-  const Plan p = make_plan(seq_len, n_heads, n_kv_heads, head_dim, true);
+  const Plan p = make_plan(seq_len, n_heads, n_kv_heads, head_dim, true, g_scratch_limit.load());
   if (workspace_bytes) *workspace_bytes = seq_len ? p.bytes : 0;
-  if (stored_tiles) *stored_tiles = p.stored ? 1 : 0;
+  if (stored_heads) *stored_heads = p.stored ? p.chunk : 0;
   return ATTN_OK;
 }
 
@@ -1923,10 +1973,13 @@ attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* blk_min, uint32_
   return hip_check(hipGetLastError(), "launching k_prep");
 }
 
-attn_status_t launch_sumparts(const float* part, int splits, long long n, float* dK, float* dV,
-                              hipStream_t st) {
-  const int blocks = (int)std::min<long long>((n / 4 + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_sumparts, dim3(blocks), dim3(256), 0, st, part, splits, n, dK, dV);
+attn_status_t launch_sumparts(const float* part, int splits, long long rows, int width,
+                              long long stride, float* dK, float* dV, hipStream_t st) {
+  int tpr = 1;
+  while (tpr < width / 4 && tpr < 256) tpr <<= 1;
+  const int blocks = (int)std::min<long long>((rows + 256 / tpr - 1) / (256 / tpr), 8192);
+  hipLaunchKernelGGL(k_sumparts, dim3(blocks), dim3(256), 0, st, part, splits, rows, width, stride,
+                     dK, dV);
   return hip_check(hipGetLastError(), "launching k_sumparts");
 }
 
@@ -1940,15 +1993,63 @@ attn_status_t launch_rowdot(const float* O, const float* dO, float* D, long long
   return hip_check(hipGetLastError(), "launching k_rowdot");
 }
 
-// ATTNBWD_PAIR=0 serves every tile from its own block even for plain causal
-// calls; anything else (or unset) pairs them.
-bool pairing_enabled() {
-  const char* e = getenv("ATTNBWD_PAIR");
-  return !(e && e[0] == '0' && e[1] == 0);
+// The backward on a planned workspace `wsb` (pl.bytes): the block metadata,
+// D from the forward output when O is given, then the passes, in head chunks
+// when the plan stores tiles for fewer than all heads.  rope: dQ and dK are
+// rotated back in the write-back (rope_bwd).
+static attn_status_t run_planned(const float* Q, const float* K, const float* V, const float* O,
+                                 const float* dO, const float* LSE, const uint32_t* seg,
+                                 float* dQ, float* dK, float* dV, int S, int H, int KV, int d,
+                                 float scale, const Plan& pl, char* wsb, hipStream_t st, int rope,
+                                 float rope_base, int pos_offset) {
+  const long long nblk = ((long long)S + 31) / 32;
+  BwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.LSE = LSE; a.seg = seg;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.Dws = reinterpret_cast<float*>(wsb);
+  a.blk_min = reinterpret_cast<uint32_t*>(wsb + pl.off_blk);
+  a.blk_max = a.blk_min + nblk;
+  a.slot_off = reinterpret_cast<long long*>(wsb + pl.off_slot);
+  a.scratch = pl.stored ? reinterpret_cast<float*>(wsb + pl.off_scr) : nullptr;
+  a.S = S; a.H = H; a.KV = KV; a.d = d; a.scale = scale;
+  a.Hs = H; a.KVs = KV;
+  // plain causal: every tile's work falls linearly with its index, so a tile
+  // and its mirror sum to the same work
+  a.pair = seg == nullptr;
+  a.hsplit = 1;
+  a.part = pl.hsplit > 1 ? reinterpret_cast<float*>(wsb + pl.off_part) : nullptr;
+  a.rope = rope;
+  a.rope_pos = pos_offset;
+  a.rope_base = (double)rope_base;
+
+  const int dp = padded_dim(d);
+  attn_status_t rc = launch_prep(seg, S, a.blk_min, a.blk_max, a.slot_off, st);
+  if (rc == ATTN_OK && O) rc = launch_rowdot(O, dO, a.Dws, (long long)S * H, d, st);
+  const int g = H / KV;
+  for (int h0 = 0; h0 < H && rc == ATTN_OK; h0 += pl.chunk) {
+    // heads [h0, h0 + hn) over KV heads [kv0, kv0 + c.KV): whole groups, or
+    // a share of one group's heads (the chunk then divides the group)
+    const int hn = std::min(pl.chunk, H - h0), kv0 = h0 / g;
+    BwdArgs c = a;
+    c.H = hn;
+    c.KV = std::max(1, hn / g);
+    c.Q = Q + (size_t)h0 * d; c.dO = dO + (size_t)h0 * d; c.dQ = dQ + (size_t)h0 * d;
+    c.LSE = LSE + h0; c.Dws = a.Dws + h0;
+    c.K = K + (size_t)kv0 * d; c.V = V + (size_t)kv0 * d;
+    c.dK = dK + (size_t)kv0 * d; c.dV = dV + (size_t)kv0 * d;
+    if (pl.hsplit > 1) {
+      c.hsplit = std::min(pl.hsplit, head_splits(S, c.H, c.KV));
+      c.part = a.part + (size_t)kv0 * d;
+    }
+    rc = O ? launch_bwd<true>(c, dp, st, h0 == 0) : launch_bwd<false>(c, dp, st, h0 == 0);
+  }
+  return rc;
 }
 
 // The backward, with D computed by the kernels (O == NULL) or read off the
-// forward output O; rope: dQ and dK rotated back afterwards (rope_bwd).
+// forward output O, on a workspace from the library's pool.  If the pool
+// cannot supply the stored-tile workspace (the device is out of memory), the
+// call runs the recompute path, which needs only D and the block metadata.
 static attn_status_t run_bwd(const float* Q, const float* K, const float* V, const float* O,
                              const float* dO, const float* LSE, const uint32_t* seg, float* dQ,
                              float* dK, float* dV, int seq_len, int n_heads, int n_kv_heads,
@@ -1962,39 +2063,22 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   if (seq_len == 0) return ATTN_OK;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int dp = padded_dim(head_dim);
-  const long long nblk = ((long long)seq_len + 31) / 32;
-  // plain causal: every tile's work falls linearly with its index, so a tile
-  // and its mirror sum to the same work (ATTNBWD_PAIR=0 turns this off)
-  const bool pair = seg == nullptr && pairing_enabled();
-  const Plan pl = make_plan(seq_len, n_heads, n_kv_heads, head_dim, !pair);
+  Plan pl = make_plan(seq_len, n_heads, n_kv_heads, head_dim, seg != nullptr,
+                      g_scratch_limit.load());
   hipMemPool_t pool;
   rc = device_pool(&pool);
   if (rc != ATTN_OK) return rc;
   void* ws = nullptr;
-  rc = hip_check(hipMallocFromPoolAsync(&ws, pl.bytes, pool, st), "hipMallocFromPoolAsync(workspace)");
+  hipError_t e = hipMallocFromPoolAsync(&ws, pl.bytes, pool, st);
+  if (e == hipErrorOutOfMemory && pl.stored) {
+    (void)hipGetLastError();  // the failed allocation is not a launch error
+    pl = make_plan(seq_len, n_heads, n_kv_heads, head_dim, seg != nullptr, 0);
+    e = hipMallocFromPoolAsync(&ws, pl.bytes, pool, st);
+  }
+  rc = hip_check(e, "hipMallocFromPoolAsync(workspace)");
   if (rc != ATTN_OK) return rc;
-  char* wsb = static_cast<char*>(ws);
-
-  BwdArgs a;
-  a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.LSE = LSE; a.seg = seg;
-  a.dQ = dQ; a.dK = dK; a.dV = dV;
-  a.Dws = reinterpret_cast<float*>(wsb);
-  a.blk_min = reinterpret_cast<uint32_t*>(wsb + pl.off_blk);
-  a.blk_max = a.blk_min + nblk;
-  a.slot_off = reinterpret_cast<long long*>(wsb + pl.off_slot);
-  a.scratch = pl.stored ? reinterpret_cast<float*>(wsb + pl.off_scr) : nullptr;
-  a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim; a.scale = scale;
-  a.pair = pair;
-  a.hsplit = pl.hsplit;
-  a.part = pl.hsplit > 1 ? reinterpret_cast<float*>(wsb + pl.off_part) : nullptr;
-  a.rope = rope;
-  a.rope_pos = pos_offset;
-  a.rope_base = (double)rope_base;
-
-  rc = launch_prep(seg, seq_len, a.blk_min, a.blk_max, a.slot_off, st);
-  if (rc == ATTN_OK && O) rc = launch_rowdot(O, dO, a.Dws, (long long)seq_len * n_heads, head_dim, st);
-  if (rc == ATTN_OK) rc = O ? launch_bwd<true>(a, dp, st) : launch_bwd<false>(a, dp, st);
+  rc = run_planned(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
+                   scale, pl, static_cast<char*>(ws), st, rope, rope_base, pos_offset);
   attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");
   return rc != ATTN_OK ? rc : rc2;
 }

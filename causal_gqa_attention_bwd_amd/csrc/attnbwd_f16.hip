@@ -750,7 +750,7 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   hipLaunchKernelGGL(k_kv16<DP>, dim3(kv_grid), dim3(256), 0, st, f);
   rc = hip_check(hipGetLastError(), "launching k_kv16");
   if (rc == ATTN_OK && f.splits > 1) {
-    rc = launch_sumparts(f.part, f.splits, (long long)f.S * f.KV * f.d, f.dK, f.dV, st);
+    rc = launch_sumparts(f.part, f.splits, f.S, f.KV * f.d, (long long)f.KV * f.d, f.dK, f.dV, st);
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
@@ -797,7 +797,7 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   // (one per CU, two up to 64 columns): more rounds only add partial sums.
   // Under a document mask the key tiles' work differs widely, and the splits
   // go on to ~1024 workgroups, which balance it (measured at S=4096 and S=16384)
-  const bool pair = seg == nullptr && pairing_enabled();
+  const bool pair = seg == nullptr;
   const int g = n_heads / n_kv_heads;
   const int nkt = (seq_len + 127) / 128;
   const long long kv_blocks = (long long)(pair ? (nkt + 1) / 2 : nkt) * n_kv_heads;

@@ -146,8 +146,6 @@ ATTN_INTERNAL attn_status_t device_pool(hipMemPool_t* out);
 // Record one profile event on st when the measurement hooks are on; `first`
 // opens the record of a new call.
 ATTN_INTERNAL attn_status_t profile_mark(hipStream_t st, bool first = false);
-// Whether plain causal calls pair each tile with its mirror (ATTNBWD_PAIR).
-ATTN_INTERNAL bool pairing_enabled();
 // k_prep: per 32-row query block seg min / max (and the tile slot offsets).
 ATTN_INTERNAL attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* blk_min,
                                         uint32_t* blk_max, long long* slot_off, hipStream_t st);
@@ -155,6 +153,7 @@ ATTN_INTERNAL attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* bl
 ATTN_INTERNAL attn_status_t launch_rowdot(const float* O, const float* dO, float* D, long long rows,
                                           int d, hipStream_t st);
 // k_sumparts: dK += sum of part[2 s], dV += sum of part[2 s + 1] over the
-// splits s in order; n = S * KV * d floats per slice.
-ATTN_INTERNAL attn_status_t launch_sumparts(const float* part, int splits, long long n, float* dK,
-                                            float* dV, hipStream_t st);
+// splits s in order, on `rows` rows of `width` floats that sit `stride`
+// floats apart (in dK, dV and each rows * stride slice of part).
+ATTN_INTERNAL attn_status_t launch_sumparts(const float* part, int splits, long long rows, int width,
+                                            long long stride, float* dK, float* dV, hipStream_t st);

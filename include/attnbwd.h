@@ -43,7 +43,8 @@
  * next synchronisation.  Launch-time errors return ATTN_ERR_HIP.
  *
  * Threads.  Reentrant.  Global state: the per-device memory pools (created
- * once, under a lock) and, per thread, the text of the last error and the
+ * once, under a lock), the scratch limit (an atomic, set by
+ * attn_set_scratch_limit) and, per thread, the text of the last error and the
  * event log of the measurement hooks.
  */
 #ifndef ATTNBWD_H
@@ -78,24 +79,30 @@ typedef enum {
  *
  * Workspace.  Each call takes one stream-ordered workspace from a private
  * per-device memory pool (hipMallocFromPoolAsync on `stream`, released with
- * hipFreeAsync on `stream` before returning; the pool keeps freed memory for
- * later calls until the process ends).  It holds the row term D
- * (seq_len * n_heads * 4 bytes), per-32-row block metadata, and -- when it
- * fits the budget -- a scratch of the probabilities P and the products P*dP
- * of every visible (32-query block, 32-key block, head) tile, written by the
- * first pass and read by the key-major pass instead of recomputing the
- * scores.  The scratch is sized by the causal bound, 8 KiB per block pair
- * and head: 2 GiB at seq_len 4096 with 32 heads, 16 GiB at 16384 with 16.
- * The budget is 32 GiB, or ATTNBWD_SCRATCH_MB MiB (a decimal number) when
- * that environment variable is set, read at every call; above it (or at 0)
- * there is no scratch and the key-major pass recomputes the scores.  With
- * the scratch, a call given a seg whose key-major pass would have fewer
- * than 1024 workgroups (64-key tiles x KV heads) splits each group's heads
- * over 2^k workgroups (k as large as that bound and the group size allow);
- * the first adds into dK, dV, and the workspace then also holds the others'
- * partial dK and dV: 2 * (2^k - 1) * seq_len * n_kv_heads * head_dim * 4
- * bytes (32 MiB at seq_len 16384, 2 KV heads, head_dim 256, 2 splits).
- * attn_bwd_plan reports the choice and the largest size for a problem.
+ * hipFreeAsync on `stream` before returning).  The pool keeps freed memory
+ * for later calls up to 4 GiB; whatever it holds above that goes back to the
+ * device at the caller's next synchronisation.  The workspace holds the row
+ * term D (seq_len * n_heads * 4 bytes), per-32-row block metadata, and a
+ * scratch of the probabilities P and the products P*dP of every visible
+ * (32-query block, 32-key block, head) tile, written by the first pass and
+ * read by the key-major pass instead of recomputing the scores.  The scratch
+ * is sized by the causal bound, 8 KiB per block pair and head: 2 GiB at
+ * seq_len 4096 with 32 heads, 16 GiB at 16384 with 16.  Its limit is 32 GiB
+ * (attn_set_scratch_limit changes it).  When the tiles of all heads exceed
+ * the limit, the passes run in head chunks one after another, each on the
+ * same scratch: as many whole KV groups as fit, or else the largest share of
+ * one group's heads (a divisor of n_heads / n_kv_heads) that fits; each
+ * chunk adds its part into dK, dV.  When not even one head's tiles fit, or
+ * the pool cannot supply the workspace (out of device memory), the call
+ * recomputes the scores in the key-major pass instead and the workspace is
+ * only D and the metadata.  With the scratch, a call given a seg whose
+ * key-major pass would have fewer than 1024 workgroups (64-key tiles x KV
+ * heads of a chunk) splits each group's heads over 2^k workgroups (k as
+ * large as that bound and the group size allow); the first adds into dK, dV,
+ * and the workspace then also holds the others' partial dK and dV:
+ * 2 * (2^k - 1) * seq_len * n_kv_heads * head_dim * 4 bytes (32 MiB at
+ * seq_len 16384, 2 KV heads, head_dim 256, 2 splits).  attn_bwd_plan reports
+ * the choice and the largest size for a problem.
  *
  * seq_len == 0 returns ATTN_OK and enqueues nothing.
  */
@@ -237,14 +244,26 @@ attn_status_t attn_bwd_decode(const float* q, const float* K, const float* V, co
 
 /*
  * attn_bwd_plan -- host-side query (no GPU work): the most workspace bytes
- * one attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes (that
- * of a call with a seg, with head splits where they apply; plain causal
- * calls take no splits), and whether its key-major pass reads stored
- * probability tiles (1) or recomputes them (0).  Either output pointer may
- * be NULL.  Same argument checks as attn_bwd.
+ * one attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes under
+ * the current scratch limit (that of a call with a seg, with head splits
+ * where they apply; plain causal calls take no splits), and how its
+ * key-major pass gets the probabilities: *stored_heads = the number of heads
+ * whose tiles one chunk stores (n_heads when the call runs in one piece), or
+ * 0 when the scores are recomputed.  Either output pointer may be NULL.
+ * Same argument checks as attn_bwd.
  */
 attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads, int head_dim,
-                            size_t* workspace_bytes, int* stored_tiles);
+                            size_t* workspace_bytes, int* stored_heads);
+
+/*
+ * attn_set_scratch_limit -- the most bytes of stored probability tiles one
+ * attn_bwd, attn_bwd_o or attn_bwd_rope call may take (default 32 GiB, about
+ * 11% of the 288 GB of HBM3E); 0 turns the stored tiles off (the key-major
+ * pass then recomputes the scores).  Process-wide, read when a call is
+ * planned; calls already enqueued keep their workspace.  The previous limit
+ * goes to *previous when it is not NULL.  Always ATTN_OK.
+ */
+attn_status_t attn_set_scratch_limit(size_t bytes, size_t* previous);
 
 /*
  * attn_fwd_lse -- the forward pass that produces the backward's inputs:

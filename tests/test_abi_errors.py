@@ -89,3 +89,40 @@ def test_rope_entry_rejects_bad_rotation_arguments(base, pos, text):
     st = lib.attn_bwd_rope(*args)
     assert st == INVALID, (st, binding.last_error())
     assert text in binding.last_error() or "pos" in binding.last_error()
+
+
+def _host_problem(S=8, H=2, KV=1, d=16):
+    import torch
+    z = lambda *s: torch.zeros(*s, dtype=torch.float32)  # noqa: E731
+    return dict(Q=z(S, H, d), K=z(S, KV, d), V=z(S, KV, d), O=z(S, H, d), dO=z(S, H, d),
+                LSE=z(S, H), dQ=z(S, H, d), dK=z(S, KV, d), dV=z(S, KV, d))
+
+
+@pytest.mark.parametrize("entry", ["attn_bwd", "attn_bwd_o", "attn_bwd_rope", "attn_bwd_f16",
+                                   "attn_bwd_short", "attn_fwd_lse", "attn_bwd_decode"])
+def test_binding_rejects_host_tensors_before_any_launch(entry):
+    # host tensors carry host addresses; handed to a kernel they would fault
+    # the GPU, so the binding refuses them with ValueError and calls nothing
+    t = _host_problem()
+    calls = {
+        "attn_bwd": lambda: binding.attn_bwd(t["Q"], t["K"], t["V"], t["dO"], t["LSE"], None,
+                                             t["dQ"], t["dK"], t["dV"], 0.25),
+        "attn_bwd_o": lambda: binding.attn_bwd_o(t["Q"], t["K"], t["V"], t["O"], t["dO"],
+                                                 t["LSE"], None, t["dQ"], t["dK"], t["dV"], 0.25),
+        "attn_bwd_rope": lambda: binding.attn_bwd_rope(t["Q"], t["K"], t["V"], None, t["dO"],
+                                                       t["LSE"], None, t["dQ"], t["dK"], t["dV"],
+                                                       0.25, 1e4, 0),
+        "attn_bwd_f16": lambda: binding.attn_bwd_f16(t["Q"], t["K"], t["V"], None, t["dO"],
+                                                     t["LSE"], None, t["dQ"], t["dK"], t["dV"],
+                                                     0.25),
+        "attn_bwd_short": lambda: binding.attn_bwd_short(t["Q"], t["K"], t["V"], None, t["dO"],
+                                                         t["LSE"], None, t["dQ"], t["dK"],
+                                                         t["dV"], 0.25),
+        "attn_fwd_lse": lambda: binding.attn_fwd_lse(t["Q"], t["K"], t["V"], None, None, t["LSE"],
+                                                     0.25),
+        "attn_bwd_decode": lambda: binding.attn_bwd_decode(t["Q"][0], t["K"], t["V"],
+                                                           t["LSE"].T.contiguous(), t["dO"][0],
+                                                           t["dQ"][0], t["dK"], t["dV"], 0.25),
+    }
+    with pytest.raises(ValueError, match="GPU tensors only"):
+        calls[entry]()

@@ -4,6 +4,8 @@ import ctypes
 import os
 import re
 
+import pytest
+
 from causal_gqa_attention_bwd_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -46,7 +48,24 @@ def up(n):
     return (n + 255) // 256 * 256
 
 
-def test_plan_sizes_the_workspace(monkeypatch):
+@pytest.fixture
+def limit():
+    saved = []
+
+    def set_limit(nbytes):
+        prev = binding.set_scratch_limit(int(nbytes))
+        if not saved:
+            saved.append(prev)
+
+    yield set_limit
+    if saved:
+        binding.set_scratch_limit(saved[0])
+
+
+DEFAULT_LIMIT = 32 << 30
+
+
+def test_plan_sizes_the_workspace(limit):
     # host-only query: D [S,H], block metadata, and the P / P*dP tile scratch
     # (two 32x32 fp32 tiles per (query block, key block, head) of the causal
     # triangle), each part 256-byte aligned, then -- the most a call takes is
@@ -54,32 +73,41 @@ def test_plan_sizes_the_workspace(monkeypatch):
     # key tiles x 8 KV heads = 512 workgroups, so the 4 heads of a group go
     # to 2 workgroups; the first adds into dK, dV, the second writes an
     # [S, KV, d] slice of dK and one of dV
-    monkeypatch.delenv("ATTNBWD_SCRATCH_MB", raising=False)
+    limit(DEFAULT_LIMIT)
     S, H = 4096, 32
     nblk = S // 32
     meta = up(up(up(S * H * 4) + 2 * nblk * 4) + (nblk + 1) * 8)
     part = 2 * 1 * S * 8 * 128 * 4
-    assert binding.bwd_plan(S, H, 8, 128) == (meta + causal_pairs(nblk) * H * 8192 + part, True)
+    assert binding.bwd_plan_heads(S, H, 8, 128) == (meta + causal_pairs(nblk) * H * 8192 + part, H)
     # a group of one head cannot split
     assert binding.bwd_plan(S, 8, 8, 128) == (
         up(up(up(S * 8 * 4) + 2 * nblk * 4) + (nblk + 1) * 8) + causal_pairs(nblk) * 8 * 8192, True)
-    monkeypatch.setenv("ATTNBWD_SCRATCH_MB", "0")
-    assert binding.bwd_plan(S, H, 8, 128) == (meta, False)
+    limit(0)
+    assert binding.bwd_plan_heads(S, H, 8, 128) == (meta, 0)
 
 
-def test_plan_recomputes_above_the_budget(monkeypatch):
-    # 16384 rows, 16 heads: the tiles need 16.03 GiB, within the default
-    # budget; a smaller budget switches to recomputed scores
-    monkeypatch.delenv("ATTNBWD_SCRATCH_MB", raising=False)
-    S, H = 16384, 16
-    need = causal_pairs(S // 32) * H * 8192
-    nbytes, stored = binding.bwd_plan(S, H, 2, 256)
-    assert stored and nbytes > need
-    monkeypatch.setenv("ATTNBWD_SCRATCH_MB", repr(need / 2**20))
-    assert binding.bwd_plan(S, H, 2, 256)[1]
-    monkeypatch.setenv("ATTNBWD_SCRATCH_MB", repr((need - 1) / 2**20))
-    nbytes, stored = binding.bwd_plan(S, H, 2, 256)
-    assert not stored and nbytes < 2 * S * H * 4
+def test_plan_takes_head_chunks_below_the_limit(limit):
+    # 16384 rows, 16 heads in 2 groups of 8: all tiles need 16.03 GiB, within
+    # the default limit; below it the tiles are stored for as many whole
+    # groups as fit, else for the largest divisor of a group's 8 heads that
+    # fits, else not at all (recomputed scores: D and the metadata only)
+    S, H, KV, d = 16384, 16, 2, 256
+    per_head = causal_pairs(S // 32) * 8192
+    limit(DEFAULT_LIMIT)
+    nbytes, heads = binding.bwd_plan_heads(S, H, KV, d)
+    assert heads == H and nbytes > H * per_head
+    for fit, chunk in ((16, 16), (15, 8), (8, 8), (7, 4), (4, 4), (3, 2), (2, 2), (1, 1)):
+        limit(fit * per_head)
+        nbytes, heads = binding.bwd_plan_heads(S, H, KV, d)
+        assert heads == chunk, (fit, heads)
+        assert chunk * per_head < nbytes < chunk * per_head + (S * H * 4 + (1 << 20)) + \
+            2 * 7 * S * KV * d * 4
+    limit(per_head - 1)
+    nbytes, heads = binding.bwd_plan_heads(S, H, KV, d)
+    assert heads == 0 and nbytes < 2 * S * H * 4
+    # whole groups of a GQA 4:1 problem, with a smaller last chunk
+    limit(9 * causal_pairs(128) * 8192)
+    assert binding.bwd_plan_heads(4096, 32, 8, 128)[1] == 8
 
 
 def test_plan_rejects_bad_shapes():

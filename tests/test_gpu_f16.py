@@ -17,8 +17,8 @@ Covered: the small workloads whole, every padded head-dim class with ragged
 tails and every mask kind (plain causal, documents, arbitrary starts, empty
 rows), with and without the forward output, nonzero initial outputs (+=),
 the paired schedule of plain causal calls against the unpaired one (bit for
-bit), repeatability, and the two large workloads on sampled rows in the
-launch configuration bench.py times.
+bit), repeatability, and the two large workloads element by element over
+whole tensors in the launch configuration bench.py times.
 """
 import numpy as np
 import pytest
@@ -26,7 +26,7 @@ import pytest
 import oracle
 from causal_gqa_attention_bwd_amd.workloads import make_inputs, random_problem
 from tests.gpu_helpers import TOL, gpu_bwd
-from tests.test_gpu_fullsize import sample_rows
+from tests.fullsize_ref import reference, rel_errs
 from tests.test_gpu_parity import EDGE, check_full, make_seg
 
 pytestmark = pytest.mark.gpu
@@ -84,28 +84,15 @@ def test_f16_paired_equals_unpaired_and_repeats(shape):
 
 @pytest.mark.parametrize("with_o", [False, True], ids=["rowterm", "fwd_out"])
 @pytest.mark.parametrize("wid", [4, 5])
-def test_f16_fullsize_sampled(wid, with_o):
-    x = make_inputs(wid)
+def test_f16_fullsize_whole_tensor(wid, with_o):
+    # every element of dQ, dK, dV against the oracle's backward (the oracle's
+    # forward O and LSE of every row as inputs), at the spec bar
+    x, O, lse, ref = reference(wid)
     w = x["workload"]
-    q_rows, k_rows = sample_rows(x, np.random.default_rng(7200 + wid))
-    need = oracle.rows_needed(x["seg"], w.S, q_rows, k_rows)
-    say(f"[gpu] workload {wid} f16: oracle forward on {len(need)} rows")
-    o_need, lse_need = oracle.attn_fwd_rows(x["Q"], x["K"], x["V"], x["seg"], x["scale"], need,
-                                            want_o=True)
-    n_vis = np.maximum(np.arange(w.S) - x["seg"].astype(np.int64) + 1, 1)
-    lse = np.repeat(np.log(n_vis).astype(np.float32)[:, None], w.H, axis=1)
-    lse[need] = lse_need
-    O = None
-    if with_o:
-        O = np.zeros(x["Q"].shape, np.float32)  # rows no compared output depends on: D = 0
-        O[need] = o_need
-    say(f"[gpu] workload {wid} f16: oracle backward on {len(q_rows)} / {len(k_rows)} rows")
-    rq, rk, rv = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], x["dO"], lse, x["seg"], x["scale"],
-                                      q_rows, k_rows, O=O)
-    say(f"[gpu] workload {wid}: attn_bwd_f16 S={w.S} H={w.H} KV={w.KV} d={w.d}")
-    dQ, dK, dV = gpu_bwd(x, lse, O=O, use_seg=bool(np.any(x["seg"])), f16=True)
-    for name, got, ref in (("dQ", dQ[q_rows], rq), ("dK", dK[k_rows], rk), ("dV", dV[k_rows], rv)):
-        assert np.all(np.isfinite(got))
-        e = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
-        say(f"[gpu] workload {wid} f16: {name} sampled rel err {e:.2e}")
-        assert e <= TOL, f"workload {wid}: {name} rel err {e:.3e} > {TOL}"
+    say(f"[gpu] workload {wid}: attn_bwd_f16 S={w.S} H={w.H} KV={w.KV} d={w.d} "
+        f"O={'given' if with_o else 'none'}, every element")
+    got = gpu_bwd(x, lse, O=O if with_o else None, use_seg=bool(np.any(x["seg"])), f16=True)
+    errs = rel_errs(got, ref)
+    say(f"[gpu] workload {wid} f16: rel err " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for name, e in errs.items():
+        assert e <= TOL, f"workload {wid} f16: {name} rel err {e:.3e} > {TOL}"

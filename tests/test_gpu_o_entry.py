@@ -2,15 +2,13 @@
 against the oracle's O entry, on the same seeded inputs and the same fp32 O:
 the workloads that finish quickly, edge shapes of every head-dim class, both
 ways of running the key-major pass, accumulation into nonzero outputs, a
-perturbed O (which the result must follow, so the kernels read D off O), and
-sampled rows of the two large workloads."""
+perturbed O (which the result must follow, so the kernels read D off O).
+The two large workloads are compared element by element in
+test_gpu_fullsize.py."""
 import numpy as np
 import pytest
 
-import oracle
 from causal_gqa_attention_bwd_amd.workloads import make_inputs, random_problem
-from tests.gpu_helpers import TOL, gpu_bwd
-from tests.test_gpu_fullsize import sample_rows
 from tests.test_gpu_parity import check_full, make_seg
 
 pytestmark = pytest.mark.gpu
@@ -38,9 +36,9 @@ def test_o_entry_workloads(wid):
 
 @pytest.mark.parametrize("case", EDGE_O, ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
 @pytest.mark.parametrize("mb", ["default", "0"])
-def test_o_entry_edge_shapes(case, mb, monkeypatch):
+def test_o_entry_edge_shapes(case, mb, scratch_limit):
     if mb != "default":
-        monkeypatch.setenv("ATTNBWD_SCRATCH_MB", mb)
+        scratch_limit(0)
     S, H, KV, d, kind = case
     rng = np.random.default_rng(6000 + S + d)
     p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
@@ -48,9 +46,9 @@ def test_o_entry_edge_shapes(case, mb, monkeypatch):
 
 
 @pytest.mark.parametrize("mb", ["default", "0"])
-def test_o_entry_follows_a_perturbed_O(mb, monkeypatch):
+def test_o_entry_follows_a_perturbed_O(mb, scratch_limit):
     if mb != "default":
-        monkeypatch.setenv("ATTNBWD_SCRATCH_MB", mb)
+        scratch_limit(0)
     x = make_inputs(3)
     rng = np.random.default_rng(6003)
     shift = (0.5 * rng.standard_normal(x["Q"].shape)).astype(np.float32)
@@ -62,29 +60,3 @@ def test_o_entry_accumulates():
     rng = np.random.default_rng(6002)
     init = [rng.standard_normal(x[k].shape).astype(np.float32) for k in ("Q", "K", "V")]
     check_full(x, "workload 2 += (O entry)", init=init, with_o=True)
-
-
-@pytest.mark.parametrize("wid", [4, 5])
-def test_o_entry_fullsize_sampled(wid):
-    x = make_inputs(wid)
-    w = x["workload"]
-    q_rows, k_rows = sample_rows(x, np.random.default_rng(7100 + wid))
-    need = oracle.rows_needed(x["seg"], w.S, q_rows, k_rows)
-    say(f"[gpu] workload {wid}: oracle forward (O, LSE) on {len(need)} rows")
-    o_need, lse_need = oracle.attn_fwd_rows(x["Q"], x["K"], x["V"], x["seg"], x["scale"], need,
-                                            want_o=True)
-    n_vis = np.maximum(np.arange(w.S) - x["seg"].astype(np.int64) + 1, 1)
-    lse = np.repeat(np.log(n_vis).astype(np.float32)[:, None], w.H, axis=1)
-    lse[need] = lse_need
-    O = np.zeros(x["Q"].shape, np.float32)   # rows no compared output depends on: D = 0
-    O[need] = o_need
-    say(f"[gpu] workload {wid}: oracle backward (O entry) on {len(q_rows)} / {len(k_rows)} rows")
-    rq, rk, rv = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], x["dO"], lse, x["seg"], x["scale"],
-                                      q_rows, k_rows, O=O)
-    say(f"[gpu] workload {wid}: attn_bwd_o S={w.S} H={w.H} KV={w.KV} d={w.d}")
-    dQ, dK, dV = gpu_bwd(x, lse, O=O, use_seg=bool(np.any(x["seg"])))
-    for name, got, ref in (("dQ", dQ[q_rows], rq), ("dK", dK[k_rows], rk), ("dV", dV[k_rows], rv)):
-        assert np.all(np.isfinite(got))
-        e = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
-        say(f"[gpu] workload {wid}: {name} sampled rel err {e:.2e}")
-        assert e <= TOL, f"workload {wid}: {name} rel err {e:.3e} > {TOL}"

@@ -51,9 +51,9 @@ def problem(shape):
 @pytest.mark.parametrize("entry", ["plain", "o", "rope"])
 @pytest.mark.parametrize("mode", ["stored", "recompute"])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda c: "S%dH%dKV%dd%d" % c)
-def test_paired_equals_unpaired(shape, mode, entry, monkeypatch):
+def test_paired_equals_unpaired(shape, mode, entry, scratch_limit):
     if mode == "recompute":
-        monkeypatch.setenv("ATTNBWD_SCRATCH_MB", "0")
+        scratch_limit(0)
     p = problem(shape)
     O, lse = oracle.attn_fwd(p["Q"], p["K"], p["V"], None, p["scale"])
     rng = np.random.default_rng(9200 + shape[0])

@@ -32,9 +32,9 @@ def test_rope_workloads(wid):
 
 @pytest.mark.parametrize("case", ROPE_EDGE, ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
 @pytest.mark.parametrize("mode", ["stored", "recompute", "stored_o", "recompute_o"])
-def test_rope_edge_shapes(case, mode, monkeypatch):
+def test_rope_edge_shapes(case, mode, scratch_limit):
     if mode.startswith("recompute"):
-        monkeypatch.setenv("ATTNBWD_SCRATCH_MB", "0")
+        scratch_limit(0)
     S, H, KV, d, kind = case
     rng = np.random.default_rng(8000 + S + d)
     p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
@@ -44,7 +44,7 @@ def test_rope_edge_shapes(case, mode, monkeypatch):
 
 
 @pytest.mark.parametrize("mode", ["stored", "recompute"])
-def test_rope_large_offset(mode, monkeypatch):
+def test_rope_large_offset(mode, scratch_limit):
     if mode == "recompute":
-        monkeypatch.setenv("ATTNBWD_SCRATCH_MB", "0")
+        scratch_limit(0)
     check_full(make_inputs(3), f"workload 3 rope offset 1e6 {mode}", rope=(10000.0, 1_000_000))

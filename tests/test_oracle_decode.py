@@ -6,7 +6,8 @@ score gradients, pass 2 the key-major dK and dV).  CPU only.
 1. Finite differences: with P = softmax(scale q.k) over the history (computed
    here in numpy), the gradients of L = sum_h dO_h . (sum_j P_hj v_j) with
    respect to q, K and V are the oracle's dq, dK, dV.
-2. Agreement with the main backward (itself pinned in test_oracle_pins.py): a
+2. Agreement with the main backward (itself pinned in test_oracle_fd.py,
+   test_oracle_invariants.py, test_oracle_dense.py and test_oracle_golden.py): a
    plain causal problem whose dO is zero except on its last row s* gives, in
    the main oracle, dK and dV equal to the decode backward's for the query
    q = Q[s*] with P from the same LSE, dQ[s*] equal to its dq, and dQ = 0
