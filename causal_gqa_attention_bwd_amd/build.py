@@ -1,10 +1,14 @@
 """Build the HIP library in-tree: libattnbwd.so next to this file (gfx950 only).
 
 Each source compiles to its own object in parallel (_build/ next to this
-file), then one link makes the shared library."""
+file, keeping the compiler's gfx950 assembly), then one link makes the
+shared library.  Before the link the assembly goes through
+codegen_check.scan: a library in which the register allocator placed a copy
+inside a divergent branch's join block is refused."""
 from __future__ import annotations
 
 import os
+import shutil
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -37,11 +41,12 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, extra: list | None = None) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    os.makedirs(OBJDIR, exist_ok=True)
     pid = os.getpid()
-    objs = [os.path.join(OBJDIR, os.path.basename(s) + ".%d.o" % pid) for s in SRCS]
-    cmds = [[hipcc, *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-c", "-o", o, s]
-            for s, o in zip(SRCS, objs)]
+    work = os.path.join(OBJDIR, str(pid))  # objects and the compiler's temporaries
+    os.makedirs(work, exist_ok=True)
+    objs = [os.path.join(work, os.path.basename(s)[:-4] + ".o") for s in SRCS]
+    cmds = [[hipcc, *HIPCC_FLAGS, *(extra or []), "-save-temps=obj", "-I", INCLUDE, "-c", "-o",
+             o, s] for s, o in zip(SRCS, objs)]
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         results = list(ex.map(lambda c: _run(c, verbose), cmds))
     failed = False
@@ -53,6 +58,8 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
     try:
         if failed:
             raise RuntimeError("hipcc failed")
+        check_assembly([os.path.join(work, os.path.basename(s)[:-4] + "-hip-amdgcn-amd-amdhsa-gfx950.s")
+                        for s in SRCS])
         rc, err = _run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
                        verbose)
         if err.strip():
@@ -61,10 +68,23 @@ def build(verbose: bool = False, extra: list | None = None) -> str:
             raise RuntimeError(f"linking {LIB} failed ({rc})")
         os.replace(tmp, LIB)
     finally:
-        for o in objs:
-            if os.path.exists(o):
-                os.remove(o)
+        shutil.rmtree(work, ignore_errors=True)
     return LIB
+
+
+def check_assembly(paths):
+    """Refuse the build when a join block of the gfx950 assembly holds a
+    vector instruction before the execution mask is restored."""
+    from causal_gqa_attention_bwd_amd.codegen_check import scan
+    bad = []
+    for p in paths:
+        if not os.path.exists(p):
+            raise RuntimeError(f"the compiler left no assembly at {p}")
+        bad += [(os.path.basename(p), *hit) for hit in scan(open(p).read())]
+    if bad:
+        text = "\n".join(f"  {f}: {fn} line {line}: {ins[:3]}" for f, fn, line, ins in bad)
+        raise RuntimeError("vector instructions between a join label and the restore of the "
+                           "execution mask (a miscompile this build refuses):\n" + text)
 
 
 if __name__ == "__main__":

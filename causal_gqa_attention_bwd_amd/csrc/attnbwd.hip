@@ -76,6 +76,8 @@ struct BwdArgs {
   float scale;
   int pair;              // 1: block p serves tiles p and n-1-p (equal causal work)
   int rope;              // 1: rotate dQ, dK back by RoPE after the += (rope_bwd)
+  int rope_old;          // k_dkdv_p with rope: 1 rotates dK's old contents with the sum (the
+                         // first chunk to write these rows), 0 adds only the rotated sum
   int rope_pos;          // position of row 0 (the page's pos_offset)
   double rope_base;      // frequency base
   int hsplit;            // k_dkdv_p: blocks sharing one key tile's heads (1, or 2^k | g)
@@ -1251,17 +1253,31 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
       }
     }
   }
+  // The write-back goes through buffers over this key tile's rows (from the
+  // KV head's first column): rows past S and columns past head_dim get an
+  // offset beyond the range, so their loads read zero and their stores are
+  // dropped, with no divergent branch in the epilogue.
+  const int col0 = dcol0 + NB * l32;
+  const uint32_t tbytes = (uint32_t)(((size_t)(min(BC, S - j0) - 1) * kstride + d) * 4);
+  uint32_t offs[16][NB];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rr = kb * 32 + crow(r, hf);  // row within the tile
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      offs[r][nb] = (j0 + rr < S && col0 + nb < d)
+                        ? (uint32_t)(((size_t)rr * kstride + col0 + nb) * 4) : ATTN_BUF_OOB;
+  }
+  double fq[NB];  // RoPE frequency of each of this lane's columns
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) fq[nb] = a.rope ? rope_freq(col0 + nb, d, a.rope_base) : 0.0;
   if (qs == 0 && split > 0) {
   // splits after the first: the partial sums scale * accK (rotated back by
   // RoPE, which is linear) and accV into this split's slices of part;
   // k_sumparts adds them to what the first split wrote
-  const size_t slice = (size_t)S * kstride;
-  float* __restrict__ pK = a.part + (size_t)(2 * split - 2) * slice + (size_t)kvh * d;
-  float* __restrict__ pV = a.part + (size_t)(2 * split - 1) * slice + (size_t)kvh * d;
-  const int col0 = dcol0 + NB * l32;
-  double fq[NB];  // RoPE frequency of each of this lane's columns
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) fq[nb] = a.rope ? rope_freq(col0 + nb, d, a.rope_base) : 0.0;
+  const size_t slice = (size_t)S * kstride, tile0 = (size_t)j0 * kstride + (size_t)kvh * d;
+  const auto rK = out_rsrc(a.part + (size_t)(2 * split - 2) * slice + tile0, tbytes);
+  const auto rV = out_rsrc(a.part + (size_t)(2 * split - 1) * slice + tile0, tbytes);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = j0 + kb * 32 + crow(r, hf);
@@ -1277,53 +1293,49 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (row < S && col0 + nb < d) {
-        const size_t off = (size_t)row * kstride + col0 + nb;
-        pK[off] = vk[nb];
-        pV[off] = accV[nb][r];
-      }
+      buf_st(rK, offs[r][nb], vk[nb]);
+      buf_st(rV, offs[r][nb], accV[nb][r]);
     }
   }
   } else if (qs == 0) {  // one split, or the first of several  // the other query block's waves only contributed partial sums
   // dK += scale * accK, dV += accV: all old values are read first, then all written
-  float* __restrict__ dKh = a.dK + (size_t)kvh * d;
-  float* __restrict__ dVh = a.dV + (size_t)kvh * d;
-  const int col0 = dcol0 + NB * l32;
+  const size_t tile0 = (size_t)j0 * kstride + (size_t)kvh * d;
+  const auto rK = out_rsrc(a.dK + tile0, tbytes);
+  const auto rV = out_rsrc(a.dV + tile0, tbytes);
   float oldK[16][NB], oldV[16][NB];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = j0 + kb * 32 + crow(r, hf);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const bool ok = row < S && col0 + nb < d;
-      const size_t off = (size_t)row * kstride + col0 + nb;
-      oldK[r][nb] = ok ? dKh[off] : 0.f;
-      oldV[r][nb] = ok ? dVh[off] : 0.f;
+      oldK[r][nb] = buf_ld(rK, offs[r][nb]);
+      oldV[r][nb] = buf_ld(rV, offs[r][nb]);
     }
   }
-  double fq[NB];  // RoPE frequency of each of this lane's columns
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) fq[nb] = a.rope ? rope_freq(col0 + nb, d, a.rope_base) : 0.0;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = j0 + kb * 32 + crow(r, hf);
     float vk[NB];
+    // a later chunk of the same dK rows adds R^T (sum) to what an earlier
+    // chunk left (already rotated); otherwise dK = R^T (dK + sum dS^T Q)
+    const bool add_after = a.rope && !a.rope_old;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) vk[nb] = oldK[r][nb] + a.scale * accK[nb][r];
-    if (a.rope) {  // dK = R^T (dK + sum dS^T Q)
+    for (int nb = 0; nb < NB; ++nb)
+      vk[nb] = (add_after ? 0.f : oldK[r][nb]) + a.scale * accK[nb][r];
+    if (a.rope) {
       float pv[NB];
       rope_partners_perm<NB>(vk, l32, pv);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
         vk[nb] = rope_back(vk[nb], pv[nb], col0 + nb, (long long)row + a.rope_pos, fq[nb]);
     }
+    if (add_after) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vk[nb] += oldK[r][nb];
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      if (row < S && col0 + nb < d) {
-        const size_t off = (size_t)row * kstride + col0 + nb;
-        dKh[off] = vk[nb];
-        dVh[off] = oldV[r][nb] + accV[nb][r];
-      }
+      buf_st(rK, offs[r][nb], vk[nb]);
+      buf_st(rV, offs[r][nb], oldV[r][nb] + accV[nb][r]);
     }
   }
   }  // qs == 0
@@ -2019,6 +2031,7 @@ static attn_status_t run_planned(const float* Q, const float* K, const float* V,
   a.hsplit = 1;
   a.part = pl.hsplit > 1 ? reinterpret_cast<float*>(wsb + pl.off_part) : nullptr;
   a.rope = rope;
+  a.rope_old = 1;
   a.rope_pos = pos_offset;
   a.rope_base = (double)rope_base;
 
@@ -2037,6 +2050,7 @@ static attn_status_t run_planned(const float* Q, const float* K, const float* V,
     c.LSE = LSE + h0; c.Dws = a.Dws + h0;
     c.K = K + (size_t)kv0 * d; c.V = V + (size_t)kv0 * d;
     c.dK = dK + (size_t)kv0 * d; c.dV = dV + (size_t)kv0 * d;
+    c.rope_old = h0 % g == 0;  // later shares of a group add to rotated dK rows
     if (pl.hsplit > 1) {
       c.hsplit = std::min(pl.hsplit, head_splits(S, c.H, c.KV));
       c.part = a.part + (size_t)kv0 * d;

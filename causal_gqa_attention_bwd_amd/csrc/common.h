@@ -38,6 +38,20 @@ __device__ __forceinline__ f32x16 zero16() {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// A raw buffer over `bytes` bytes at p for an epilogue's reads and writes:
+// a load at an offset at or past the end reads zero and a store there is
+// dropped (the hardware range check), so ragged rows and columns need no
+// divergent branch around them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)bytes, ATTN_BUF_WORD3);
+}
+__device__ __forceinline__ float buf_ld(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_st(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+
 // Buffer resource of `nbytes` bytes at `base` (nbytes = 0: every load reads zeros).
 __device__ __forceinline__ i32x4 buf_rsrc(const void* base, uint32_t nbytes) {
   const uint64_t p = (uint64_t)base;
