@@ -13,7 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_o", "attn_bwd_plan",
+EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_noalloc", "attn_bwd_o",
+            "attn_bwd_plan",
             "attn_bwd_rope", "attn_bwd_short", "attn_fwd_lse", "attn_last_error",
             "attn_profile_begin", "attn_profile_end", "attn_set_scratch_limit")
 
@@ -38,6 +39,8 @@ def load():
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd.restype = I
+    lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
+    lib.attn_bwd_noalloc.restype = I
     lib.attn_bwd_o.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_o.restype = I
     lib.attn_bwd_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, F, I, P]
@@ -153,6 +156,17 @@ def attn_bwd(Q, K, V, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
                          _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                          _stream(stream))
     _raise_on(st, "attn_bwd")
+
+
+def attn_bwd_noalloc(Q, K, V, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
+    """attn_bwd on the library's fixed 32 MiB device workspace, allocating
+    nothing (the C ABI's attn_bwd_noalloc); calls that overlap on one device
+    race on that workspace."""
+    S, H, KV, d = _bwd_args(Q, K, V, None, dO, LSE, seg, dQ, dK, dV)
+    st = load().attn_bwd_noalloc(_ptr(Q), _ptr(K), _ptr(V), _ptr(dO), _ptr(LSE), _ptr(seg),
+                                 _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
+                                 _stream(stream))
+    _raise_on(st, "attn_bwd_noalloc")
 
 
 def attn_bwd_o(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):

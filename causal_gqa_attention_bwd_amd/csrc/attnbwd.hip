@@ -2097,6 +2097,85 @@ static attn_status_t run_bwd(const float* Q, const float* K, const float* V, con
   return rc != ATTN_OK ? rc : rc2;
 }
 
+// ---------------------------------------------------------------------------
+// The entry that allocates nothing (attn_bwd_noalloc): its workspace is this
+// file-scope device array, one per device, held from the library's load on
+// that device until the process ends.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): it looks up the array's device address once per device and passes
+// that.
+// ---------------------------------------------------------------------------
+#define ATTN_NOALLOC_BYTES (32u << 20)
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_BYTES];
+static std::mutex g_scratch_mu;
+static std::map<int, char*> g_scratch_ptr;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on each device, with that device current).
+static attn_status_t noalloc_scratch(char** out) {
+  int dev = 0;
+  attn_status_t rc = hip_check(hipGetDevice(&dev), "hipGetDevice");
+  if (rc != ATTN_OK) return rc;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return ATTN_OK;
+  }
+  void* ptr = nullptr;
+  rc = hip_check(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+  if (rc != ATTN_OK) return rc;
+  g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  *out = static_cast<char*>(ptr);
+  return ATTN_OK;
+}
+
+// A plan whose workspace fits `avail` bytes: the stored tiles of as many heads
+// as fit beside D and the metadata (head splits first allowed, then not),
+// else the recompute path; false when not even D and the metadata fit.
+static bool plan_within(int S, int H, int KV, int d, bool may_split, size_t avail, Plan* out) {
+  for (int split = may_split ? 1 : 0; split >= 0; --split) {
+    long long limit = (long long)avail;
+    for (int it = 0; it < 64; ++it) {
+      const Plan p = make_plan(S, H, KV, d, split != 0, limit);
+      if (p.bytes <= avail) {
+        *out = p;
+        return true;
+      }
+      if (!p.stored) break;
+      limit = std::max(0ll, limit - (long long)(p.bytes - avail));  // shrink by the excess
+    }
+  }
+  return false;
+}
+
+extern "C" attn_status_t attn_bwd_noalloc(const float* Q, const float* K, const float* V,
+                                          const float* dO, const float* LSE, const uint32_t* seg,
+                                          float* dQ, float* dK, float* dV, int seq_len,
+                                          int n_heads, int n_kv_heads, int head_dim, float scale,
+                                          void* stream) {
+  g_err[0] = 0;
+  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, scale);
+  if (rc != ATTN_OK) return rc;
+  const void* ptrs[] = {Q, K, V, dO, LSE, seg, dQ, dK, dV};
+  for (const void* p : ptrs)
+    if (misaligned(p)) return fail(ATTN_ERR_UNSUPPORTED, "a tensor pointer is not 16-byte aligned");
+  if (seq_len == 0) return ATTN_OK;
+  Plan pl;
+  if (!plan_within(seq_len, n_heads, n_kv_heads, head_dim, seg != nullptr, ATTN_NOALLOC_BYTES, &pl))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "attn_bwd_noalloc: seq_len %d with %d heads needs more than its %u-byte scratch "
+                "(the row term alone is seq_len * n_heads * 4 bytes)",
+                seq_len, n_heads, ATTN_NOALLOC_BYTES);
+  char* ws = nullptr;
+  rc = noalloc_scratch(&ws);
+  if (rc != ATTN_OK) return rc;
+  return run_planned(Q, K, V, nullptr, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads,
+                     head_dim, scale, pl, ws, reinterpret_cast<hipStream_t>(stream), 0, 0.f, 0);
+}
+
 extern "C" attn_status_t attn_bwd(const float* Q, const float* K, const float* V, const float* dO,
                                   const float* LSE, const uint32_t* seg, float* dQ, float* dK,
                                   float* dV, int seq_len, int n_heads, int n_kv_heads,

@@ -243,6 +243,31 @@ attn_status_t attn_bwd_decode(const float* q, const float* K, const float* V, co
                               float scale, void* stream);
 
 /*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Same arguments, layouts, += semantics, mask and
+ * results as attn_bwd; it calls no hipMalloc, hipFree or pool allocation.
+ * Its workspace is a fixed 32 MiB device array inside the library, one per
+ * device (taken when the library's code loads on that device, held until the
+ * process ends; its address is looked up on the first call on each device).
+ * The workspace holds D and the block metadata and, when they fit beside
+ * them, the stored probability tiles of as many heads as fit (run in head
+ * chunks as above); otherwise the key-major pass recomputes the scores.
+ * Limit: seq_len * n_heads * 4 bytes of row term plus about seq_len / 2
+ * bytes of metadata must fit in 32 MiB (seq_len * n_heads up to about 8.3
+ * million); larger problems return ATTN_ERR_UNSUPPORTED before any GPU work.
+ * Every call on a device shares that device's array, and nothing in it needs
+ * clearing between calls (each call writes what it reads): calls that may
+ * overlap on one device -- on different streams, or from several threads --
+ * race on it and must be serialised by the caller.  Errors as attn_bwd.
+ */
+attn_status_t attn_bwd_noalloc(const float* Q, const float* K, const float* V, const float* dO,
+                               const float* LSE, const uint32_t* seg,
+                               float* dQ, float* dK, float* dV,
+                               int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                               float scale, void* stream);
+
+/*
  * attn_bwd_plan -- host-side query (no GPU work): the most workspace bytes
  * one attn_bwd (or attn_bwd_o, attn_bwd_rope) call of this size takes under
  * the current scratch limit (that of a call with a seg, with head splits

@@ -62,6 +62,14 @@ CASES = [
     ("attn_bwd_f16", bwd_args(d=8), UNSUPPORTED, "head_dim"),
     ("attn_bwd_f16", bwd_args(mis="seg"), UNSUPPORTED, "aligned"),
     ("attn_bwd_f16", bwd_args(S=0, with_o=False), OK, ""),
+    # attn_bwd_noalloc (Q, K, V, dO, LSE, seg, dQ, dK, dV: no O)
+    ("attn_bwd_noalloc", [A] * 5 + [None] + [A] * 3 + [262144, 64, 8, 64, 0.125, None],
+     UNSUPPORTED, "scratch"),
+    ("attn_bwd_noalloc", [A] * 5 + [None] + [A, A, None] + [8, 2, 1, 64, 0.125, None], INVALID,
+     "NULL"),
+    ("attn_bwd_noalloc", [A] * 5 + [None] + [A] * 3 + [8, 3, 2, 64, 0.125, None], INVALID,
+     "multiple"),
+    ("attn_bwd_noalloc", [A] * 5 + [None] + [A] * 3 + [0, 2, 1, 64, 0.125, None], OK, ""),
     # attn_bwd_o
     ("attn_bwd_o", bwd_args(null="O"), INVALID, "NULL"),
     ("attn_bwd_o", bwd_args(S=-4), INVALID, "negative"),
@@ -99,7 +107,8 @@ def _host_problem(S=8, H=2, KV=1, d=16):
 
 
 @pytest.mark.parametrize("entry", ["attn_bwd", "attn_bwd_o", "attn_bwd_rope", "attn_bwd_f16",
-                                   "attn_bwd_short", "attn_fwd_lse", "attn_bwd_decode"])
+                                   "attn_bwd_short", "attn_bwd_noalloc", "attn_fwd_lse",
+                                   "attn_bwd_decode"])
 def test_binding_rejects_host_tensors_before_any_launch(entry):
     # host tensors carry host addresses; handed to a kernel they would fault
     # the GPU, so the binding refuses them with ValueError and calls nothing
@@ -118,6 +127,9 @@ def test_binding_rejects_host_tensors_before_any_launch(entry):
         "attn_bwd_short": lambda: binding.attn_bwd_short(t["Q"], t["K"], t["V"], None, t["dO"],
                                                          t["LSE"], None, t["dQ"], t["dK"],
                                                          t["dV"], 0.25),
+        "attn_bwd_noalloc": lambda: binding.attn_bwd_noalloc(t["Q"], t["K"], t["V"], t["dO"],
+                                                             t["LSE"], None, t["dQ"], t["dK"],
+                                                             t["dV"], 0.25),
         "attn_fwd_lse": lambda: binding.attn_fwd_lse(t["Q"], t["K"], t["V"], None, None, t["LSE"],
                                                      0.25),
         "attn_bwd_decode": lambda: binding.attn_bwd_decode(t["Q"][0], t["K"], t["V"],
