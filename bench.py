@@ -395,6 +395,9 @@ def main():
     ap.add_argument("--f16", action="store_true",
                     help="time attn_bwd_f16 (fp16 matrix-core operands, fp32 accumulation; with "
                          "--o-entry the forward output is passed)")
+    ap.add_argument("--scratch-limit-mb", type=float, default=None,
+                    help="set the library's stored-tile scratch limit (MiB; 0: recompute the "
+                         "scores) before timing")
     ap.add_argument("--no-extra", dest="extra", action="store_false",
                     help="skip the extra timings (S=16384 documents in fp32, S=4096 with fp16 "
                          "operands) that the default run adds to config.extra")
@@ -410,6 +413,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.scratch_limit_mb is not None:
+        from causal_gqa_attention_bwd_amd import binding
+        binding.set_scratch_limit(int(args.scratch_limit_mb * (1 << 20)))
 
     entry = ("attn_bwd_short" if args.short else "attn_bwd_f16" if args.f16 else
              "attn_bwd_rope" if args.rope else "attn_bwd_o" if args.o_entry else "attn_bwd")

@@ -39,6 +39,10 @@ WORKLOADS = {
     3: Workload(3, "s1024_h8_kv8_d64_docs_u64_512", 1024, 8, 8, 64, "uniform"),
     4: Workload(4, "s4096_h32_kv8_d128_causal", 4096, 32, 8, 128, "single", 0.1),
     5: Workload(5, "s16384_h16_kv2_d256_docs_geom2048", 16384, 16, 2, 256, "geometric"),
+    # the S=4096 workload's heads at eight times the length: its stored tiles
+    # (137 GB for all heads) exceed any scratch limit, so it measures the head
+    # chunks; not one of the five parity workloads
+    6: Workload(6, "s32768_h32_kv8_d128_causal", 32768, 32, 8, 128, "single", 0.1),
 }
 
 
