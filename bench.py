@@ -137,8 +137,8 @@ def parity_errors(sample, ref, entry, with_o, rope=None):
         binding.attn_bwd(*args, t["dO"], t["LSE"], seg, *out, sc)
     elif entry == "attn_bwd_o":
         binding.attn_bwd_o(*args, O, t["dO"], t["LSE"], seg, *out, sc)
-    elif entry == "attn_bwd_rope":
-        binding.attn_bwd_rope(*args, O, t["dO"], t["LSE"], seg, *out, sc, rope[0], rope[1])
+    elif entry.endswith("_rope"):
+        getattr(binding, entry)(*args, O, t["dO"], t["LSE"], seg, *out, sc, rope[0], rope[1])
     else:
         getattr(binding, entry)(*args, O, t["dO"], t["LSE"], seg, *out, sc)
     torch.cuda.synchronize()
@@ -175,8 +175,8 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     stored = heads > 0
     dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
     f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + 2 * w.S * w.H * 4
-    if entry == "attn_bwd_f16":
-        log(f"bench: attn_bwd_f16, fp16 copies {f16_ws / 2**30:.2f} GiB")
+    if entry.startswith("attn_bwd_f16"):
+        log(f"bench: {entry}, fp16 copies {f16_ws / 2**30:.2f} GiB")
     elif entry != "attn_bwd_short":
         log(f"bench: workspace at most {ws_bytes / 2**30:.2f} GiB (attn_bwd_plan), "
             + (f"stored probability tiles for {heads} heads at a time" if stored
@@ -192,8 +192,8 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
             binding.attn_bwd(*a, t["dO"], lse, seg, dQ, dK, dV, scale)
         elif entry == "attn_bwd_o":
             binding.attn_bwd_o(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale)
-        elif entry == "attn_bwd_rope":
-            binding.attn_bwd_rope(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale, 10000.0, 0)
+        elif entry.endswith("_rope"):
+            getattr(binding, entry)(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale, 10000.0, 0)
         else:
             getattr(binding, entry)(*a, O, t["dO"], lse, seg, dQ, dK, dV, scale)
 
@@ -235,7 +235,7 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     if entry == "attn_bwd_short":
         passes = ([("k_short", ms_q, 14.0)] if with_o else
                   [("k_short_rowterm", ms_q, 4.0), ("k_short", ms_k, 14.0)])
-    elif entry == "attn_bwd_f16":
+    elif entry.startswith("attn_bwd_f16"):
         passes = [("k_cvt16", ms_q, 0.0 if with_o else 4.0), ("k_kv16", ms_k, 8.0),
                   ("k_q16", ms_s, 6.0)]
     elif stored:
@@ -249,23 +249,24 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     kms = kms_sum / ncalls
     kflops = per_pair * w.d * w.H * npairs
     kach = kflops / (kms * 1e-3) / 1e12
-    peak = PEAK_FP16_MFMA if entry == "attn_bwd_f16" else PEAK_FP32_MFMA
+    peak = PEAK_FP16_MFMA if entry.startswith("attn_bwd_f16") else PEAK_FP32_MFMA
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(kach / peak, 4),
                 "traffic": read_traffic(kname, w.name), "avg_launch_ms": round(kms, 4)}
     # general path: attn_bwd_plan's figure, the most a call of this size takes
     # (with a seg: head-split partial sums); fp16: the operand copies, D and
     # LSE*log2e, before any partial sums; short: the row term D
+    f16 = entry.startswith("attn_bwd_f16")
     ws_key = ("row_term_bytes" if entry == "attn_bwd_short" else
-              "fp16_copies_bytes" if entry == "attn_bwd_f16" else "workspace_bytes_max")
+              "fp16_copies_bytes" if f16 else "workspace_bytes_max")
     ws_val = (0 if entry == "attn_bwd_short" and with_o else
               w.S * w.H * 4 if entry == "attn_bwd_short" else
-              f16_ws if entry == "attn_bwd_f16" else ws_bytes)
+              f16_ws if f16 else ws_bytes)
     del t, dQ, dK, dV, lse, O
     torch.cuda.empty_cache()
     return dict(workload=w, inputs=x, ms_step=ms_step, tflops=tflops, flops=flops, npairs=npairs,
                 kernel_ms=kernel_ms, roofline=roofline, peak=peak,
-                stored=None if entry in ("attn_bwd_f16", "attn_bwd_short") else stored,
+                stored=None if f16 or entry == "attn_bwd_short" else stored,
                 ws_key=ws_key, ws_bytes=ws_val)
 
 
@@ -418,7 +419,8 @@ def main():
         from causal_gqa_attention_bwd_amd import binding
         binding.set_scratch_limit(int(args.scratch_limit_mb * (1 << 20)))
 
-    entry = ("attn_bwd_short" if args.short else "attn_bwd_f16" if args.f16 else
+    entry = ("attn_bwd_short" if args.short else
+             ("attn_bwd_f16_rope" if args.rope else "attn_bwd_f16") if args.f16 else
              "attn_bwd_rope" if args.rope else "attn_bwd_o" if args.o_entry else "attn_bwd")
     r = time_entry(args.workload, entry, args.o_entry, args.steps, args.warmup, args.calib_copy_mb)
     w, x = r["workload"], r["inputs"]

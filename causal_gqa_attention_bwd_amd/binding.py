@@ -13,7 +13,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattnbwd.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
-EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_noalloc", "attn_bwd_o",
+EXPORTED = ("attn_bwd", "attn_bwd_decode", "attn_bwd_f16", "attn_bwd_f16_rope", "attn_bwd_noalloc",
+            "attn_bwd_o",
             "attn_bwd_plan",
             "attn_bwd_rope", "attn_bwd_short", "attn_fwd_lse", "attn_last_error",
             "attn_profile_begin", "attn_profile_end", "attn_set_scratch_limit")
@@ -47,6 +48,8 @@ def load():
     lib.attn_bwd_rope.restype = I
     lib.attn_bwd_f16.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_f16.restype = I
+    lib.attn_bwd_f16_rope.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, F, I, P]
+    lib.attn_bwd_f16_rope.restype = I
     lib.attn_bwd_short.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, F, P]
     lib.attn_bwd_short.restype = I
     lib.attn_bwd_decode.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, F, P]
@@ -200,6 +203,18 @@ def attn_bwd_f16(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
                              _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d, float(scale),
                              _stream(stream))
     _raise_on(st, "attn_bwd_f16")
+
+
+def attn_bwd_f16_rope(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, rope_base, pos_offset,
+                      stream=None):
+    """attn_bwd_f16 with the RoPE backward on dQ and dK fused into the
+    write-back (the C ABI's attn_bwd_f16_rope): dQ <- R^T(dQ + g)."""
+    S, H, KV, d = _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV)
+    st = load().attn_bwd_f16_rope(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE),
+                                  _ptr(seg), _ptr(dQ), _ptr(dK), _ptr(dV), S, H, KV, d,
+                                  float(scale), float(rope_base), int(pos_offset),
+                                  _stream(stream))
+    _raise_on(st, "attn_bwd_f16_rope")
 
 
 def attn_bwd_short(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):

@@ -275,26 +275,6 @@ struct SpreadLoads {
   }
 };
 
-// ---------------------------------------------------------------------------
-// RoPE backward in the epilogues (page "llm.istanbul --
-// 10_backward_attention.wgsl", kernels rope_q_backward / rope_k_backward):
-// the pair of columns (2p, 2p+1) of a row at position pos turns back by
-// angle = pos * base^(-2p/d): (g0, g1) -> (g0 c + g1 s, -g0 s + g1 c).  The
-// angle and its sine and cosine are taken in fp64 (positions reach 2^31; an
-// fp32 angle would be off by ~1e-3 rad at a few thousand).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ double rope_freq(int col, int d, double base) {
-  return pow(base, -2.0 * (double)(col >> 1) / (double)d);
-}
-// This column's value after the backward rotation, from its own value and its
-// pair partner's.
-__device__ __forceinline__ float rope_back(float mine, float partner, int col, long long pos,
-                                           double freq) {
-  double sn, cs;
-  sincos((double)pos * freq, &sn, &cs);
-  return (col & 1) ? (float)(-(double)partner * sn + (double)mine * cs)
-                   : (float)((double)mine * cs + (double)partner * sn);
-}
 // Pair partners of a lane's NB values in the permuted column layout
 // (value nb of lane l sits in column c0 + NB*(l%32) + nb, c0 even): the other
 // column of a pair is in the same lane or, for odd NB, in lane l +- 1.
@@ -367,7 +347,8 @@ __global__ __launch_bounds__(1024) void k_prep(const uint32_t* seg, int S, uint3
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_sumparts(const float* __restrict__ part, int splits,
                                                   long long rows, int width, long long stride,
-                                                  float* dK, float* dV) {
+                                                  float* dK, float* dV, int rope, int d,
+                                                  int rope_pos, double rope_base) {
   const size_t slice = (size_t)rows * stride;
   // tpr threads (a power of two, at most 256) per row, 256 / tpr rows per block
   const int w4 = width / 4;
@@ -384,6 +365,15 @@ __global__ __launch_bounds__(256) void k_sumparts(const float* __restrict__ part
         const float4 pv = *reinterpret_cast<const float4*>(part + (size_t)(2 * s + 1) * slice + off);
         k.x += pk.x; k.y += pk.y; k.z += pk.z; k.w += pk.w;
         v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+      }
+      if (rope) {  // dK = R^T (dK + sum of the parts): the float4 holds two pairs
+        const int col = (4 * c4) % d;
+        const long long pos = r + rope_pos;
+        const double f0 = rope_freq(col, d, rope_base), f1 = rope_freq(col + 2, d, rope_base);
+        const float x0 = rope_back(k.x, k.y, col, pos, f0), y0 = rope_back(k.y, k.x, col + 1, pos, f0);
+        const float x1 = rope_back(k.z, k.w, col + 2, pos, f1);
+        const float y1 = rope_back(k.w, k.z, col + 3, pos, f1);
+        k.x = x0; k.y = y0; k.z = x1; k.w = y1;
       }
       *reinterpret_cast<float4*>(dK + off) = k;
       *reinterpret_cast<float4*>(dV + off) = v;
@@ -1986,12 +1976,13 @@ attn_status_t launch_prep(const uint32_t* seg, int S, uint32_t* blk_min, uint32_
 }
 
 attn_status_t launch_sumparts(const float* part, int splits, long long rows, int width,
-                              long long stride, float* dK, float* dV, hipStream_t st) {
+                              long long stride, float* dK, float* dV, hipStream_t st, int rope,
+                              int d, int rope_pos, double rope_base) {
   int tpr = 1;
   while (tpr < width / 4 && tpr < 256) tpr <<= 1;
   const int blocks = (int)std::min<long long>((rows + 256 / tpr - 1) / (256 / tpr), 8192);
   hipLaunchKernelGGL(k_sumparts, dim3(blocks), dim3(256), 0, st, part, splits, rows, width, stride,
-                     dK, dV);
+                     dK, dV, rope, d, rope_pos, rope_base);
   return hip_check(hipGetLastError(), "launching k_sumparts");
 }
 

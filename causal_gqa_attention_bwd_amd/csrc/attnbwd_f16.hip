@@ -164,6 +164,9 @@ struct F16Args {
   int splits;                          // k_kv16: workgroups sharing one key tile's heads
   int kv_work;                         // k_kv16: (key tile, KV head, split) triples
   float* part;                         // [2 * splits][S, KV, d] partial dK, dV (splits > 1)
+  int rope;                            // 1: dQ, dK rotated back by RoPE in the write-back
+  int rope_pos;                        // position of row 0 (the page's pos_offset)
+  double rope_base;                    // frequency base
 };
 
 struct CvtArgs {
@@ -240,7 +243,7 @@ struct QGeom {
   static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
 
-template <int DP, bool DONLY>
+template <int DP, bool DONLY, bool ROPE>
 __global__ __launch_bounds__(256, (QGeom<DP, DONLY>::WAVES_PER_SIMD)) void k_q16(F16Args a) {
   using G = QGeom<DP, DONLY>;
   using RT = typename G::RT;
@@ -395,7 +398,7 @@ __global__ __launch_bounds__(256, (QGeom<DP, DONLY>::WAVES_PER_SIMD)) void k_q16
     if constexpr (DONLY) {
       const float Dt = Dacc + __shfl_xor(Dacc, 32);  // the half-waves saw disjoint keys
       if (q_ok && hf == 0) a.D[(size_t)q * H + h] = Dt;
-    } else {
+    } else if constexpr (!ROPE) {
       float* dQh = a.dQ + (size_t)h * a.d;
       const size_t qstride = (size_t)H * a.d;
 #pragma unroll
@@ -406,6 +409,29 @@ __global__ __launch_bounds__(256, (QGeom<DP, DONLY>::WAVES_PER_SIMD)) void k_q16
           const int row = i0 + 32 * wave + crow(r, hf);
           if (row < S && col < a.d) dQh[(size_t)row * qstride + col] += a.scale * acc[o][r];
         }
+      }
+    } else {
+      // dQ = R^T (dQ + scale * acc), the pair partner column in lane l ^ 1,
+      // through a buffer over this wave's rows: rows past S and columns past
+      // head_dim read zero and drop their stores, so every lane reaches the
+      // partner exchange
+      const size_t qstride = (size_t)H * a.d;
+      const int r0 = i0 + 32 * wave, nrows = max(0, min(32, S - r0));
+      const auto rq = out_rsrc(a.dQ + (size_t)h * a.d + (size_t)r0 * qstride,
+                               nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * qstride + a.d) * 4) : 0u);
+#pragma unroll
+      for (int o = 0; o < NO; ++o) {
+        const int col = 32 * o + l32;
+        const double fq = rope_freq(col, a.d, a.rope_base);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = crow(r, hf);
+          const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * qstride + col) * 4)
+                                                         : ATTN_BUF_OOB;
+          const float v = buf_ld(rq, off) + a.scale * acc[o][r];
+          buf_st(rq, off, rope_back(v, __shfl_xor(v, 1), col, (long long)r0 + rr + a.rope_pos, fq));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one output tile at a time
       }
     }
   };
@@ -455,7 +481,7 @@ struct KvGeom {
   static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
 
-template <int DP>
+template <int DP, bool ROPE>
 __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
   using G = KvGeom<DP>;
   using RT = typename G::RT;
@@ -690,28 +716,38 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
     __syncthreads();  // every wave done with the ring before it is reused
 
     // rows key j0 + 32w + crow(r, hf), the part's columns: += into dK, dV (one
-    // split), or this split's partial sums into part (several)
+    // split; with RoPE dK = R^T (dK + scale * accK), the pair partner in lane
+    // l ^ 1), or this split's partial sums into part (several; k_sumparts
+    // then adds and rotates).  Through buffers over the wave's rows: rows
+    // past S and columns past head_dim read zero and drop their stores.
     const size_t kstride = (size_t)KV * a.d;
     const size_t slice = (size_t)S * kstride;
-    float* outK = a.splits == 1 ? a.dK : a.part + (size_t)(2 * split) * slice;
-    float* outV = a.splits == 1 ? a.dV : a.part + (size_t)(2 * split + 1) * slice;
-    outK += (size_t)kvh * a.d;
-    outV += (size_t)kvh * a.d;
+    const int r0 = j0 + 32 * wave, nrows = max(0, min(32, S - r0));
+    const uint32_t rbytes =
+        nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * kstride + a.d) * 4) : 0u;
+    const size_t base = (size_t)kvh * a.d + (size_t)r0 * kstride;
+    const auto rK = out_rsrc((a.splits == 1 ? a.dK : a.part + (size_t)(2 * split) * slice) + base,
+                             rbytes);
+    const auto rV = out_rsrc((a.splits == 1 ? a.dV : a.part + (size_t)(2 * split + 1) * slice) + base,
+                             rbytes);
 #pragma unroll
     for (int o = 0; o < NOW; ++o) {
       const int col = cpart * G::DW + 32 * o + l32;
+      const double fq = ROPE ? rope_freq(col, a.d, a.rope_base) : 0.0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = j0 + 32 * wave + crow(r, hf);
-        if (row < S && col < a.d) {
-          const size_t off = (size_t)row * kstride + col;
-          if (a.splits == 1) {
-            outK[off] += a.scale * accK[o][r];
-            outV[off] += accV[o][r];
-          } else {
-            outK[off] = a.scale * accK[o][r];
-            outV[off] = accV[o][r];
-          }
+        const int rr = crow(r, hf);
+        const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * kstride + col) * 4)
+                                                       : ATTN_BUF_OOB;
+        if (a.splits == 1) {
+          float vk = buf_ld(rK, off) + a.scale * accK[o][r];
+          if constexpr (ROPE)
+            vk = rope_back(vk, __shfl_xor(vk, 1), col, (long long)r0 + rr + a.rope_pos, fq);
+          buf_st(rK, off, vk);
+          buf_st(rV, off, buf_ld(rV, off) + accV[o][r]);
+        } else {
+          buf_st(rK, off, a.scale * accK[o][r]);
+          buf_st(rV, off, accV[o][r]);
         }
       }
     }
@@ -741,20 +777,27 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   if (O) {
     rc = launch_rowdot(O, dO, f.D, (long long)f.S * f.H, f.d, st);
   } else {
-    hipLaunchKernelGGL((k_q16<DP, true>), dim3(nqt * f.H), dim3(256), 0, st, f);
+    hipLaunchKernelGGL((k_q16<DP, true, false>), dim3(nqt * f.H), dim3(256), 0, st, f);
     rc = hip_check(hipGetLastError(), "launching k_q16 (row term)");
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
   const int kv_grid = KvGeom<DP>::NC == 2 ? (f.kv_work + 7) / 8 * 16 : f.kv_work;
-  hipLaunchKernelGGL(k_kv16<DP>, dim3(kv_grid), dim3(256), 0, st, f);
+  if (f.rope)
+    hipLaunchKernelGGL((k_kv16<DP, true>), dim3(kv_grid), dim3(256), 0, st, f);
+  else
+    hipLaunchKernelGGL((k_kv16<DP, false>), dim3(kv_grid), dim3(256), 0, st, f);
   rc = hip_check(hipGetLastError(), "launching k_kv16");
   if (rc == ATTN_OK && f.splits > 1) {
-    rc = launch_sumparts(f.part, f.splits, f.S, f.KV * f.d, (long long)f.KV * f.d, f.dK, f.dV, st);
+    rc = launch_sumparts(f.part, f.splits, f.S, f.KV * f.d, (long long)f.KV * f.d, f.dK, f.dV, st,
+                         f.rope, f.d, f.rope_pos, f.rope_base);
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
-  hipLaunchKernelGGL((k_q16<DP, false>), dim3(nqt * f.H), dim3(256), 0, st, f);
+  if (f.rope)
+    hipLaunchKernelGGL((k_q16<DP, false, true>), dim3(nqt * f.H), dim3(256), 0, st, f);
+  else
+    hipLaunchKernelGGL((k_q16<DP, false, false>), dim3(nqt * f.H), dim3(256), 0, st, f);
   rc = hip_check(hipGetLastError(), "launching k_q16");
   if (rc == ATTN_OK) rc = profile_mark(st);
   return rc;
@@ -762,13 +805,12 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
-                                      const float* dO, const float* LSE, const uint32_t* seg,
-                                      float* dQ, float* dK, float* dV, int seq_len, int n_heads,
-                                      int n_kv_heads, int head_dim, float scale, void* stream) {
-  clear_error();
-  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
-    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+// The fp16-operand backward; rope: dQ and dK rotated back in the write-back.
+static attn_status_t run_f16(const float* Q, const float* K, const float* V, const float* O,
+                             const float* dO, const float* LSE, const uint32_t* seg, float* dQ,
+                             float* dK, float* dV, int seq_len, int n_heads, int n_kv_heads,
+                             int head_dim, float scale, void* stream, int rope, float rope_base,
+                             int pos_offset) {
   attn_status_t rc = check_common(seq_len, n_heads, n_kv_heads, head_dim, scale);
   if (rc != ATTN_OK) return rc;
   const void* ptrs[] = {Q, K, V, O, dO, LSE, seg, dQ, dK, dV};
@@ -836,6 +878,9 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   f.splits = splits;
   f.kv_work = (int)(kv_blocks * splits);
   f.part = splits > 1 ? reinterpret_cast<float*>(w + off_part) : nullptr;
+  f.rope = rope;
+  f.rope_pos = pos_offset;
+  f.rope_base = (double)rope_base;
   CvtArgs c;
   c.Q = Q; c.dO = dO; c.K = K; c.V = V;
   c.LSE = LSE;
@@ -857,4 +902,33 @@ extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const floa
   }
   attn_status_t rc2 = hip_check(hipFreeAsync(ws, st), "hipFreeAsync(workspace)");
   return rc != ATTN_OK ? rc : rc2;
+}
+
+extern "C" attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
+                                      const float* dO, const float* LSE, const uint32_t* seg,
+                                      float* dQ, float* dK, float* dV, int seq_len, int n_heads,
+                                      int n_kv_heads, int head_dim, float scale, void* stream) {
+  clear_error();
+  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  return run_f16(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
+                 scale, stream, 0, 0.f, 0);
+}
+
+extern "C" attn_status_t attn_bwd_f16_rope(const float* Q, const float* K, const float* V,
+                                           const float* O, const float* dO, const float* LSE,
+                                           const uint32_t* seg, float* dQ, float* dK, float* dV,
+                                           int seq_len, int n_heads, int n_kv_heads, int head_dim,
+                                           float scale, float rope_base, int pos_offset,
+                                           void* stream) {
+  clear_error();
+  if (!Q || !K || !V || !dO || !LSE || !dQ || !dK || !dV)
+    return fail(ATTN_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  if (!(rope_base > 0.f) || !isfinite(rope_base))
+    return fail(ATTN_ERR_INVALID_ARG, "rope_base must be positive and finite (got %g)", (double)rope_base);
+  if (pos_offset < 0) return fail(ATTN_ERR_INVALID_ARG, "pos_offset must be >= 0 (got %d)", pos_offset);
+  if (seq_len > 0 && (long long)pos_offset + seq_len - 1 > 0x7fffffffll)
+    return fail(ATTN_ERR_INVALID_ARG, "pos_offset + seq_len exceeds 2^31");
+  return run_f16(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
+                 scale, stream, 1, rope_base, pos_offset);
 }

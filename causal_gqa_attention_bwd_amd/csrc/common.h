@@ -28,6 +28,26 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 // ---------------------------------------------------------------------------
+// RoPE backward in the epilogues (page "llm.istanbul --
+// 10_backward_attention.wgsl", kernels rope_q_backward / rope_k_backward):
+// the pair of columns (2p, 2p+1) of a row at position pos turns back by
+// angle = pos * base^(-2p/d): (g0, g1) -> (g0 c + g1 s, -g0 s + g1 c).  The
+// angle and its sine and cosine are taken in fp64 (positions reach 2^31; an
+// fp32 angle would be off by ~1e-3 rad at a few thousand).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double rope_freq(int col, int d, double base) {
+  return pow(base, -2.0 * (double)(col >> 1) / (double)d);
+}
+// This column's value after the backward rotation, from its own value and its
+// pair partner's.
+__device__ __forceinline__ float rope_back(float mine, float partner, int col, long long pos,
+                                           double freq) {
+  double sn, cs;
+  sincos((double)pos * freq, &sn, &cs);
+  return (col & 1) ? (float)(-(double)partner * sn + (double)mine * cs)
+                   : (float)((double)mine * cs + (double)partner * sn);
+}
+// ---------------------------------------------------------------------------
 // Direct buffer->LDS loads.  Each lane's 16 (or 4) bytes land at the wave's
 // LDS base + 16 (or 4) * lane; the global source of every lane is free, which
 // the kernels use for padding and zero fill: a lane whose offset lies beyond
@@ -168,6 +188,10 @@ ATTN_INTERNAL attn_status_t launch_rowdot(const float* O, const float* dO, float
                                           int d, hipStream_t st);
 // k_sumparts: dK += sum of part[2 s], dV += sum of part[2 s + 1] over the
 // splits s in order, on `rows` rows of `width` floats that sit `stride`
-// floats apart (in dK, dV and each rows * stride slice of part).
+// floats apart (in dK, dV and each rows * stride slice of part).  rope: dK
+// is then rotated back, dK = R^T (dK + sum), row r at position r + rope_pos
+// (head_dim d, base rope_base).
 ATTN_INTERNAL attn_status_t launch_sumparts(const float* part, int splits, long long rows, int width,
-                                            long long stride, float* dK, float* dV, hipStream_t st);
+                                            long long stride, float* dK, float* dV, hipStream_t st,
+                                            int rope = 0, int d = 0, int rope_pos = 0,
+                                            double rope_base = 0.0);

@@ -186,6 +186,26 @@ attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const
                            void* stream);
 
 /*
+ * attn_bwd_f16_rope -- attn_bwd_f16 followed by the RoPE backward of page
+ * "llm.istanbul -- 10_backward_attention.wgsl" (kernels rope_q_backward,
+ * rope_k_backward) on dQ and dK, fused into the write-back exactly as in
+ * attn_bwd_rope: dQ <- R^T (dQ + attention gradient), dK <- R^T (dK +
+ * attention gradient), dV <- dV + attention gradient, with angle = (s +
+ * pos_offset) * rope_base^(-2p/head_dim) for column pair (2p, 2p+1) of row
+ * s, taken in double precision.  Q and K are the rotated tensors the forward
+ * used.  When the key-major pass splits a KV group's heads, the partial sums
+ * are added and dK rotated in one pass after it.  Arguments, precision,
+ * workspace and errors as attn_bwd_f16, plus ATTN_ERR_INVALID_ARG for
+ * rope_base <= 0 or not finite, pos_offset < 0, or pos_offset + seq_len >
+ * 2^31.
+ */
+attn_status_t attn_bwd_f16_rope(const float* Q, const float* K, const float* V, const float* O,
+                                const float* dO, const float* LSE, const uint32_t* seg,
+                                float* dQ, float* dK, float* dV,
+                                int seq_len, int n_heads, int n_kv_heads, int head_dim, float scale,
+                                float rope_base, int pos_offset, void* stream);
+
+/*
  * attn_bwd_short -- the backward for short sequences (seq_len <= 1024): page
  * "llm.istanbul -- 10_backward_attention.wgsl", attention_backward_short and
  * attention_backward_short_dKdV, the page's variant for sequences of at most

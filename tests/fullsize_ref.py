@@ -42,3 +42,16 @@ def rel_errs(got, ref):
         num = float(np.max(np.abs(g.astype(np.float64) - r.astype(np.float64))))
         out[name] = num / max(float(np.max(np.abs(r))), 1e-30)
     return out
+
+
+@functools.lru_cache(maxsize=2)
+def rope_reference(wid, base, pos_offset):
+    """The oracle's dQ, dK, dV of workload wid with the page's RoPE backward
+    (base, pos_offset) applied to dQ and dK, on the oracle's LSE."""
+    x, _, lse, _ = reference(wid)
+    t0 = time.perf_counter()
+    say(f"[oracle] workload {wid}: backward with RoPE (base {base}, offset {pos_offset})")
+    grads = oracle.attn_bwd(x["Q"], x["K"], x["V"], x["dO"], lse, x["seg"], x["scale"],
+                            rope=(base, pos_offset))
+    say(f"[oracle] workload {wid}: backward with RoPE {time.perf_counter() - t0:.1f} s")
+    return grads

@@ -37,6 +37,10 @@ def gpu_bwd(p, lse, init=None, seg=None, use_seg=True, O=None, rope=None, f16=Fa
         binding.attn_bwd_short(t["Q"], t["K"], t["V"],
                                None if O is None else to_dev(O.astype(np.float32)), t["dO"], L, s,
                                *out, float(p["scale"]))
+    elif f16 and rope is not None:
+        binding.attn_bwd_f16_rope(t["Q"], t["K"], t["V"],
+                                  None if O is None else to_dev(O.astype(np.float32)), t["dO"], L,
+                                  s, *out, float(p["scale"]), float(rope[0]), int(rope[1]))
     elif f16:
         binding.attn_bwd_f16(t["Q"], t["K"], t["V"],
                              None if O is None else to_dev(O.astype(np.float32)), t["dO"], L, s,

@@ -91,10 +91,11 @@ def test_entry_rejects_bad_arguments_on_the_host(entry, args, status, text):
 
 @pytest.mark.parametrize("base,pos,text", [(0.0, 0, "rope_base"), (math.nan, 0, "rope_base"),
                                            (1e4, -1, "pos_offset"), (1e4, 2**31 - 4, "pos_offset")])
-def test_rope_entry_rejects_bad_rotation_arguments(base, pos, text):
+@pytest.mark.parametrize("entry", ["attn_bwd_rope", "attn_bwd_f16_rope"])
+def test_rope_entry_rejects_bad_rotation_arguments(base, pos, text, entry):
     lib = binding.load()
     args = bwd_args(S=8)[:-1] + [base, pos, None]
-    st = lib.attn_bwd_rope(*args)
+    st = getattr(lib, entry)(*args)
     assert st == INVALID, (st, binding.last_error())
     assert text in binding.last_error() or "pos" in binding.last_error()
 
@@ -107,8 +108,8 @@ def _host_problem(S=8, H=2, KV=1, d=16):
 
 
 @pytest.mark.parametrize("entry", ["attn_bwd", "attn_bwd_o", "attn_bwd_rope", "attn_bwd_f16",
-                                   "attn_bwd_short", "attn_bwd_noalloc", "attn_fwd_lse",
-                                   "attn_bwd_decode"])
+                                   "attn_bwd_f16_rope", "attn_bwd_short", "attn_bwd_noalloc",
+                                   "attn_fwd_lse", "attn_bwd_decode"])
 def test_binding_rejects_host_tensors_before_any_launch(entry):
     # host tensors carry host addresses; handed to a kernel they would fault
     # the GPU, so the binding refuses them with ValueError and calls nothing
@@ -124,6 +125,9 @@ def test_binding_rejects_host_tensors_before_any_launch(entry):
         "attn_bwd_f16": lambda: binding.attn_bwd_f16(t["Q"], t["K"], t["V"], None, t["dO"],
                                                      t["LSE"], None, t["dQ"], t["dK"], t["dV"],
                                                      0.25),
+        "attn_bwd_f16_rope": lambda: binding.attn_bwd_f16_rope(t["Q"], t["K"], t["V"], None,
+                                                               t["dO"], t["LSE"], None, t["dQ"],
+                                                               t["dK"], t["dV"], 0.25, 1e4, 0),
         "attn_bwd_short": lambda: binding.attn_bwd_short(t["Q"], t["K"], t["V"], None, t["dO"],
                                                          t["LSE"], None, t["dQ"], t["dK"],
                                                          t["dV"], 0.25),

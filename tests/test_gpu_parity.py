@@ -27,8 +27,9 @@ def check_full(p, tag, init=None, with_o=False, o_shift=None, rope=None, f16=Fal
         O = (O + o_shift).astype(np.float32)
     ref = oracle.attn_bwd(p["Q"], p["K"], p["V"], p["dO"], lse, p["seg"], p["scale"],
                           *(init if init is not None else ()), O=O if with_o else None, rope=rope)
-    entry = ("attn_bwd_short" if short else "attn_bwd_f16" if f16 else
-             "attn_bwd_o" if with_o else "attn_bwd")
+    entry = ("attn_bwd_short" if short else
+             ("attn_bwd_f16_rope" if rope is not None else "attn_bwd_f16") if f16 else
+             "attn_bwd_rope" if rope is not None else "attn_bwd_o" if with_o else "attn_bwd")
     say(f"[gpu] {tag}: {entry} S={p['Q'].shape[0]} H={p['Q'].shape[1]} "
         f"KV={p['K'].shape[1]} d={p['Q'].shape[2]}")
     got = gpu_bwd(p, lse, init=init, O=O if with_o else None, rope=rope, f16=f16, short=short)
