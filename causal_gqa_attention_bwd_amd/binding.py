@@ -219,7 +219,7 @@ def attn_bwd_f16_rope(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, rope_base, po
 
 def attn_bwd_short(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, scale, stream=None):
     """The short-sequence backward (the C ABI's attn_bwd_short; seq_len <= 1024,
-    head_dim <= 64): one launch when O (the forward output) is given, two when
+    head_dim <= 128): one launch when O (the forward output) is given, two when
     O is None."""
     S, H, KV, d = _bwd_args(Q, K, V, O, dO, LSE, seg, dQ, dK, dV)
     st = load().attn_bwd_short(_ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(LSE), _ptr(seg),

@@ -543,8 +543,12 @@ extern "C" attn_status_t attn_bwd_short(const float* Q, const float* K, const fl
   if (seq_len > SHORT_MAX_S)
     return fail(ATTN_ERR_UNSUPPORTED, "seq_len = %d is above %d (use attn_bwd or attn_bwd_o)",
                 seq_len, SHORT_MAX_S);
-  if (head_dim > 64)
-    return fail(ATTN_ERR_UNSUPPORTED, "head_dim = %d is above 64 (use attn_bwd or attn_bwd_o)",
+  // a wave keeps its rows' halves of K, V (key role) or Q, dO (query role)
+  // and two items' operand rows in registers, and each wave stages two
+  // 32-row tiles in LDS: above 128 columns neither fits (LDS alone would be
+  // 4 * 2 * 32 * (192 + 4) * 4 bytes = 200 KB at 192 columns)
+  if (head_dim > 128)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim = %d is above 128 (use attn_bwd or attn_bwd_o)",
                 head_dim);
   // the kernels address every tensor with 32-bit byte offsets
   if ((long long)seq_len * n_heads * head_dim * 4 >= (1LL << 31))
@@ -559,7 +563,15 @@ extern "C" attn_status_t attn_bwd_short(const float* Q, const float* K, const fl
   a.S = seq_len; a.H = n_heads; a.KV = n_kv_heads; a.d = head_dim;
   a.nqb = (seq_len + 31) / 32;
   a.scale = scale;
-  const int dp = head_dim <= 32 ? 32 : 64;
+  const int dp = head_dim <= 32 ? 32 : head_dim <= 64 ? 64 : head_dim <= 96 ? 96 : 128;
+  auto launch = [&](bool rowterm) {
+    switch (dp) {
+      case 32: return launch_short<32>(a, rowterm, st);
+      case 64: return launch_short<64>(a, rowterm, st);
+      case 96: return launch_short<96>(a, rowterm, st);
+      default: return launch_short<128>(a, rowterm, st);
+    }
+  };
   // head splits of the key role: the first key block of a long document
   // sees up to nqb query blocks times g heads, nqb g / 4 items per wave.
   // Split its heads (a power of two dividing g) while that chain is longer
@@ -589,10 +601,10 @@ extern "C" attn_status_t attn_bwd_short(const float* Q, const float* K, const fl
   }
   rc = profile_mark(st, true);
   if (rc == ATTN_OK && !O) {
-    rc = dp == 32 ? launch_short<32>(a, true, st) : launch_short<64>(a, true, st);
+    rc = launch(true);
     if (rc == ATTN_OK) rc = profile_mark(st);
   }
-  if (rc == ATTN_OK) rc = dp == 32 ? launch_short<32>(a, false, st) : launch_short<64>(a, false, st);
+  if (rc == ATTN_OK) rc = launch(false);
   if (rc == ATTN_OK && ksplit > 1) {
     const long long n = (long long)seq_len * n_kv_heads * head_dim;
     const int blocks = (int)std::min<long long>((n / 4 + 255) / 256, 2048);

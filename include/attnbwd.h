@@ -225,7 +225,7 @@ attn_status_t attn_bwd_f16_rope(const float* Q, const float* K, const float* V, 
  * partial dK, dV sums to a workspace of 2 * splits * seq_len * n_kv_heads *
  * head_dim * 4 bytes, and one more launch adds them in split order (still
  * deterministic).  Errors as attn_bwd, plus ATTN_ERR_UNSUPPORTED for
- * seq_len > 1024, head_dim > 64 (attn_bwd and attn_bwd_o take those), or
+ * seq_len > 1024, head_dim > 128 (attn_bwd and attn_bwd_o take those), or
  * seq_len * n_heads * head_dim * 4 >= 2^31.
  */
 attn_status_t attn_bwd_short(const float* Q, const float* K, const float* V, const float* O,

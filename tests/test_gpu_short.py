@@ -4,7 +4,7 @@ element: max|gpu - oracle| <= 2e-3 * max|oracle| per gradient (the fp32 path's
 bar; fp32 products and sums).
 
 Covered: the three short workloads whole, with and without O; every padded
-head-dim class (32, 64) with d = 16 .. 64; every mask kind (plain causal,
+head-dim class (32, 64, 96, 128) with d = 16 .. 128; every mask kind (plain causal,
 documents, arbitrary starts, rows that see no key); lengths 1, 2, ragged
 tails (33, 97, 1000) and the maximum 1024 with several waves' worth of blocks;
 KV groups of 1 .. 8 heads, with the key blocks' heads split over 1, 2, 4 and 8
@@ -14,7 +14,7 @@ S=1024 with 8 heads over one KV head); nonzero initial outputs
 (+=); repeatability (the
 sums have a fixed order, so two calls agree bit for bit); agreement of the O
 and row-term forms; and the size limits (ATTN_ERR_UNSUPPORTED above 1024
-positions or 64 columns).
+positions or 128 columns).
 """
 import numpy as np
 import pytest
@@ -42,6 +42,12 @@ SHORT_EDGE = [  # S, H, KV, d, mask
     (700, 12, 2, 48, "causal"),     # group of 6: two head splits of 3
     (1024, 16, 2, 64, "docs"),      # group of 8: four head splits
     (1024, 8, 1, 32, "docs"),       # group of 8: eight head splits
+    (130, 8, 2, 80, "docs"),        # 96-column tiles
+    (65, 2, 2, 96, "empty_rows"),
+    (321, 4, 1, 112, "arbitrary"),  # 128-column tiles
+    (1024, 8, 8, 128, "docs"),
+    (1024, 16, 2, 128, "causal"),   # group of 8 split over the key role
+    (3, 3, 3, 128, "singletons"),
 ]
 
 
@@ -84,7 +90,7 @@ def test_short_repeats_bit_for_bit():
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("S,d", [(1025, 32), (512, 80)])
+@pytest.mark.parametrize("S,d", [(1025, 32), (512, 144)])
 def test_short_rejects_sizes_beyond_its_limits(S, d):
     H = KV = 1
     z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=dev())
