@@ -19,8 +19,13 @@
  * Invisible (masked) pairs contribute exactly nothing for finite inputs: the
  * probability and score-gradient of an invisible pair are selected to zero
  * (never computed as a product with zero), so an overflowing exponential or a
- * -inf LSE there cannot reach a visible row.  A non-finite VALUE in an input
- * row (Q, K, V, dO) may still propagate to rows that share its tile.
+ * -inf LSE there cannot reach a visible row.  Non-finite input values (Q, K,
+ * V, dO, O) follow IEEE arithmetic (no NaN guards): they reach the outputs
+ * that depend on them, and may also reach rows that share a row tile with
+ * them (tiles are aligned blocks of at most 128 rows), since a masked entry
+ * enters a tile product with weight zero and 0 * NaN is NaN.  Rows of a
+ * document separated from the non-finite value by a boundary at a multiple
+ * of 128 rows are unaffected, bit for bit.
  *
  * Layouts (all fp32 unless noted, contiguous, row-major, no batch dimension --
  * packed documents replace batching):
