@@ -3,15 +3,14 @@ against the fp64 oracle.  The oracle computes the exact sums; the variant's
 error comes from rounding the product operands to fp16 (unit roundoff
 u = 2^-11, about 4.9e-4).
 
-Bars: the five workloads (whole, or on sampled rows at full size) are held to
-the same bar as the fp32 path, max|gpu - oracle| <= 2e-3 * max|oracle| per
-gradient (they measure 4e-4 .. 1.2e-3).  The small edge shapes are held to
-2e-2 (about 40 u): on rows that see one or two keys, under arbitrary
-document starts or with rows that see no key, dS = P (dP - D) is a small
-difference of nearly equal fp16 products and the error relative to the
-largest gradient grows to tens of u (measured at most 5.7e-3 here, at S = 2,
-and 1.56e-2 over 1000 seeded random shapes, with every token its own
-document).
+Bars: the five workloads (whole tensors, also at full size) are held to the
+same bar as the fp32 path, max|gpu - oracle| <= 2e-3 * max|oracle| per
+gradient (they measure 4e-4 .. 1.2e-3).  The small edge shapes, where rows
+see one or two keys and dS = P (dP - D) is a small difference of nearly equal
+fp16 products, are held element by element to twice the first-order fp16
+rounding bound derived from the inputs before the run (tests/f16_bounds.py),
+including the shapes with every token its own document, whose dQ and dK are
+zero in exact arithmetic.
 
 Covered: the small workloads whole, every padded head-dim class with ragged
 tails and every mask kind (plain causal, documents, arbitrary starts, empty
@@ -31,13 +30,46 @@ from tests.test_gpu_parity import EDGE, check_full, make_seg
 
 pytestmark = pytest.mark.gpu
 
-TOL_F16_EDGE = 2e-2  # edge shapes: about 40 fp16 unit roundoffs (see above)
+U16 = 2.0 ** -11     # fp16 unit roundoff
 # With every token its own document, dQ and dK are zero in exact arithmetic,
 # but with fp16 operands P = 1 holds only up to the fp16 rounding of the
 # recomputed score against the given LSE, so they carry residues of order
-# u * |score| * |dP| * |K|, which no fraction of the largest gradient bounds;
-# that case is held to the bar through the fp32 entries only.
-EDGE_F16 = [c for c in EDGE if c[4] != "singletons"]
+# u * |score| * |dP| * |K|, which no fraction of the largest gradient bounds:
+# those shapes get the element-wise bound derived in singleton_bounds below.
+SINGLETONS = [c for c in EDGE if c[4] == "singletons"]
+
+
+def singleton_bounds(p):
+    """Element-wise bounds on |dQ|, |dK| (zero in exact arithmetic) and on
+    |dV - exact dV| when every token is its own document, from fp16 operand
+    rounding (u = 2^-11; fp32 sums and exponentials add terms of 1e-7).
+
+    Row s sees only key s (head h, KV head kv = h / g), P = 1 exactly.  With
+    the operands rounded, the score moves by at most a = 2u scale sum_i
+    |q_i k_i| and dP by at most 2u b, b = sum_i |dO_i v_i|, so P = 1 + e with
+    |e| <= a (to first order), and dS/scale = P (dP - D) is at most
+    |dP| a + 2u b whether D comes from the same P and dP (D = P dP) or from
+    the forward output (D = dO . v exactly).  Then |dQ_s| <= scale |dS/scale|
+    |K_s|, |dK_s| <= scale sum_h |dS/scale|_h |Q_s,h|, and |dV_s - sum_h dO_s,h|
+    <= sum_h (a + 2u) |dO_s,h|, each times (1 + 3u) for the rounding of the
+    last product's operands; a factor 2 covers second-order terms."""
+    Q, K, V, dO = (np.asarray(p[k], np.float64) for k in ("Q", "K", "V", "dO"))
+    S, H, d = Q.shape
+    KV = K.shape[1]
+    g = H // KV
+    sc = float(p["scale"])
+    Kh = np.repeat(K, g, axis=1)            # [S, H, d]: the key of each head's group
+    Vh = np.repeat(V, g, axis=1)
+    a = 2 * U16 * sc * np.sum(np.abs(Q * Kh), axis=2)          # [S, H]
+    b = np.sum(np.abs(dO * Vh), axis=2)
+    dP = np.sum(dO * Vh, axis=2)
+    ds = np.abs(dP) * a + 2 * U16 * b                           # bound on |dS/scale|
+    f = 2 * (1 + 3 * U16)
+    bq = f * sc * ds[:, :, None] * np.abs(Kh)                   # [S, H, d]
+    bk = f * sc * (ds[:, :, None] * np.abs(Q)).reshape(S, KV, g, d).sum(axis=2)
+    bv = f * ((a + 2 * U16)[:, :, None] * np.abs(dO)).reshape(S, KV, g, d).sum(axis=2)
+    exact_dv = dO.reshape(S, KV, g, d).sum(axis=2)
+    return bq, bk, bv, exact_dv
 
 
 def say(msg):
@@ -51,13 +83,14 @@ def test_f16_workload_parity(wid, with_o):
 
 
 @pytest.mark.parametrize("with_o", [False, True], ids=["rowterm", "fwd_out"])
-@pytest.mark.parametrize("case", EDGE_F16, ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
 def test_f16_edge_parity(case, with_o):
+    # every element within twice its fp16 rounding bound (tests/f16_bounds.py)
     S, H, KV, d, kind = case
     rng = np.random.default_rng(3000 + S + d)
     p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
     check_full(p, "edge f16 " + "S%dH%dKV%dd%d_%s" % case, with_o=with_o, f16=True,
-               tol=TOL_F16_EDGE)
+               f16_bound=True)
 
 
 def test_f16_accumulates():
@@ -96,3 +129,22 @@ def test_f16_fullsize_whole_tensor(wid, with_o):
     say(f"[gpu] workload {wid} f16: rel err " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     for name, e in errs.items():
         assert e <= TOL, f"workload {wid} f16: {name} rel err {e:.3e} > {TOL}"
+
+
+@pytest.mark.parametrize("with_o", [False, True], ids=["rowterm", "fwd_out"])
+@pytest.mark.parametrize("case", SINGLETONS, ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
+def test_f16_singletons_within_the_rounding_bound(case, with_o):
+    # every token its own document: dQ = dK = 0 and dV = sum of dO over the
+    # group in exact arithmetic; the fp16 operands leave residues that must
+    # stay inside the element-wise rounding bounds derived up front
+    S, H, KV, d, kind = case
+    rng = np.random.default_rng(3000 + S + d)
+    p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
+    O, lse = oracle.attn_fwd(p["Q"], p["K"], p["V"], p["seg"], p["scale"], want_o=True)
+    dQ, dK, dV = gpu_bwd(p, lse, O=O if with_o else None, f16=True)
+    bq, bk, bv, exact_dv = singleton_bounds(p)
+    say(f"[gpu] singletons f16 S{S} H{H} KV{KV} d{d}: |dQ|/bound {np.max(np.abs(dQ) / bq):.2f}, "
+        f"|dK|/bound {np.max(np.abs(dK) / bk):.2f}, |dV err|/bound {np.max(np.abs(dV - exact_dv) / bv):.2f}")
+    assert np.all(np.abs(dQ) <= bq)
+    assert np.all(np.abs(dK) <= bk)
+    assert np.all(np.abs(dV - exact_dv) <= bv)

@@ -3,7 +3,8 @@ RoPE backward fused into the write-back of dQ and dK) against the oracle's
 composition R^T(init + gradient), at the fp16 bars of test_gpu_f16.py: the
 five workloads (the two large ones element by element over whole tensors)
 within 2e-3 of the largest gradient, the small edge shapes of every head-dim
-class within the edge bar.  Covered: with and without the forward output,
+class element by element within twice their fp16 rounding bound (turned by
+the rotation: each column of a pair gets the pair's summed bound).  Covered: with and without the forward output,
 nonzero initial outputs (which the rotation turns too), a large
 pos_offset, plain causal calls whose key-major pass splits each group's
 heads (the partial sums are then added and dK rotated after the pass) and
@@ -14,7 +15,6 @@ import pytest
 from causal_gqa_attention_bwd_amd.workloads import make_inputs, random_problem
 from tests.fullsize_ref import reference, rel_errs, rope_reference
 from tests.gpu_helpers import TOL, gpu_bwd
-from tests.test_gpu_f16 import TOL_F16_EDGE
 from tests.test_gpu_parity import check_full, make_seg
 from tests.test_gpu_rope import ROPE_EDGE
 
@@ -42,7 +42,7 @@ def test_f16_rope_edge_shapes(case, with_o):
     p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
     init = [rng.standard_normal(p[k].shape).astype(np.float32) for k in ("Q", "K", "V")]
     check_full(p, "edge f16 rope " + "S%dH%dKV%dd%d_%s" % case, init=init, with_o=with_o,
-               f16=True, rope=(500.0, 13), tol=TOL_F16_EDGE)
+               f16=True, rope=(500.0, 13), f16_bound=True)
 
 
 def test_f16_rope_large_offset():

@@ -17,11 +17,13 @@ def say(msg):
 
 
 def check_full(p, tag, init=None, with_o=False, o_shift=None, rope=None, f16=False, tol=TOL,
-               short=False):
+               short=False, f16_bound=False):
     """GPU vs oracle on the whole problem.  with_o: through attn_bwd_o with the
     oracle's forward output (plus o_shift, if given) on both sides.  rope =
     (base, pos_offset): through attn_bwd_rope.  f16: through attn_bwd_f16 (with
-    the forward output when with_o).  short: through attn_bwd_short (likewise)."""
+    the forward output when with_o).  short: through attn_bwd_short (likewise).
+    f16_bound: hold every element to twice the fp16 rounding bound derived in
+    tests/f16_bounds.py (instead of tol times the largest gradient)."""
     O, lse = oracle.attn_fwd(p["Q"], p["K"], p["V"], p["seg"], p["scale"], want_o=with_o)
     if with_o and o_shift is not None:
         O = (O + o_shift).astype(np.float32)
@@ -53,6 +55,23 @@ def check_full(p, tag, init=None, with_o=False, o_shift=None, rope=None, f16=Fal
     # relative) -- the absolute bound on a zero tensor is then 2e-6 of the
     # largest gradient for fp32 operands (16 units of rounding) and 1e-3 for
     # fp16 operands (2 units).
+    if f16_bound:
+        from tests.f16_bounds import U32, f16_bounds, rotated
+        bounds = f16_bounds(p, lse, O if with_o else None)
+        if rope is not None:
+            d = p["Q"].shape[2]
+            bounds = (rotated(bounds[0], d), rotated(bounds[1], d), bounds[2])
+        worst = 0.0
+        for (name, g, w), b in zip(pairs, bounds):
+            allowed = 2.0 * b + 4.0 * U32 * (np.abs(w) + 1e-30)
+            ratio = float(np.max(np.abs(g - w) / allowed)) if w.size else 0.0
+            worst = max(worst, ratio)
+            errs[name] = ratio
+        say(f"[gpu] {tag}: |err| / (2 x fp16 rounding bound) " +
+            ", ".join(f"{k}={v:.3f}" for k, v in errs.items()))
+        for name, r in errs.items():
+            assert r <= 1.0, f"{tag}: {name} exceeds twice its fp16 rounding bound ({r:.3f})"
+        return got, ref
     overall = max(float(np.max(np.abs(w))) if w.size else 0.0 for _, _, w in pairs)
     floor = 5e-2 if f16 else 1e-3
     for name, g, w in pairs:
