@@ -679,6 +679,229 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_dqw: k_dq's storing mode above 128 columns (DP = 192, 256), sized for two
+// workgroups per CU.  Same work per (query tile of 64 rows, head): waves 2qb
+// (role 0: S = K Q^T, Q in registers) and 2qb + 1 (role 1: dP = V dO^T) of
+// query block qb.  The LDS holds a K/V key tile in two column chunks, each
+// with the columns both half-waves contract at one time (half-wave hf takes
+// columns hf*TH + t; chunk c holds t in [c*TH/2, (c+1)*TH/2)), double
+// buffered: 68 KB.  Role 0 forms P and hands it to role 1 through LDS (8 KB,
+// one direction); role 1 forms P*dP (with D given: dS/scale = P (dP - D)) and
+// the row term.  Role 0 stores the P tiles, role 1 the P*dP tiles, each
+// right after the barrier that follows them.  Two workgroups per CU put two
+// waves on each SIMD (one workgroup of four waves with the whole tile in LDS
+// left one), so one wave's products run while the other exponentiates,
+// exchanges or waits at a barrier.
+// ---------------------------------------------------------------------------
+template <int DP>
+struct WideGeom {
+  static constexpr int TH = DP / 2;        // contraction columns per half-wave
+  static constexpr int CC = TH / 2;        // per half-wave per chunk
+  static constexpr int DC = 2 * CC;        // columns of a chunk row (both halves)
+  static constexpr int LDC = DC + 4;       // LDS pitch of a chunk row
+  using T = PadTile<32, DC>;
+  static constexpr int CT = T::FLOATS;     // floats of a staged 32-row chunk tile
+};
+
+// Per-lane global byte offsets of the granules this wave loads into one
+// column chunk of a 32-row tile: LDS granule g of a row holds columns
+// c*CC + 4g (half 0, g < CC/4) or TH + c*CC + 4(g - CC/4) (half 1); columns at
+// or past d, the pad granule and rows past 32 read zeros (offset beyond the
+// buffer).
+template <int DP>
+struct ChunkLoader {
+  using W = WideGeom<DP>;
+  using T = typename W::T;
+  uint32_t off[2][T::CPW];
+  __device__ __forceinline__ void init(size_t stride, int d, int wave, int lane) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int i = 0; i < T::CPW; ++i) {
+        const int p = (wave + 4 * i) * 64 + lane;
+        const int row = p / T::GPR, g = p % T::GPR;
+        const int col = g < W::CC / 4 ? c * W::CC + 4 * g : W::TH + c * W::CC + 4 * (g - W::CC / 4);
+        const bool ok = row < 32 && g < W::DC / 4 && col < d;
+        off[c][i] = ok ? (uint32_t)(((size_t)row * stride + col) * 4) : ATTN_BUF_OOB;
+      }
+  }
+  __device__ __forceinline__ void load(int c, int i, const i32x4& r, uint32_t lds_byte,
+                                       int wave) const {
+    const int chunk = wave + 4 * i;
+    if (4 * (i + 1) <= T::NCH || chunk < T::NCH) dma16(r, off[c][i], lds_byte + chunk * 1024);
+  }
+};
+
+// Buffer resource of rows [r0, min(r0 + 32, S)) of a [S, stride] matrix
+// starting at `base` (the head's first column); empty when !live.
+__device__ __forceinline__ i32x4 rows32_rsrc(const float* base, int r0, int S, size_t stride,
+                                             int d, bool live = true) {
+  const int rows = live ? min(S - r0, 32) : 0;
+  const uint32_t nbytes = rows > 0 ? (uint32_t)(((size_t)(rows - 1) * stride + d) * 4) : 0u;
+  return buf_rsrc(live ? base + (size_t)r0 * stride : base, nbytes);
+}
+
+template <int DP, bool DK>
+__global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
+  using W = WideGeom<DP>;
+  constexpr int BR = 64, BC = 32, TH = W::TH, CC = W::CC, LDC = W::LDC, CT = W::CT;
+  constexpr int CPW = W::T::CPW;
+  __shared__ __attribute__((aligned(1024))) float sKV[2][2 * CT];  // stages of (K chunk, V chunk)
+  __shared__ __attribute__((aligned(16))) float sX[2 * 16 * 64];   // P of each query block
+  __shared__ uint32_t sMin[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int role = wave & 1, qb = wave >> 1;
+  const int S = a.S, H = a.H, d = a.d;
+  const int g = H / a.KV;
+  const int qt_hi = (S - 1) / BR;
+  ChunkLoader<DP> ld;
+  ld.init((size_t)a.KVs * d, d, wave, lane);
+  auto tile = [&](const int qt) __attribute__((always_inline)) {
+  const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
+  const int i0 = qt * BR;
+  const int q = i0 + qb * 32 + l32;
+  const bool q_ok = q < S;
+  const size_t qstride = (size_t)a.Hs * d, kstride = (size_t)a.KVs * d;
+  const float sc2 = a.scale * ATTN_LOG2E;
+  const float* Kh = a.K + (size_t)kvh * d;
+  const float* Vh = a.V + (size_t)kvh * d;
+
+  // B operands: this lane's row of Q (role 0) or dO (role 1), half-wave hf's columns
+  float qr[TH];
+  load_row<TH>((role ? a.dO : a.Q) + (size_t)q * qstride + (size_t)h * d, hf * TH, d, q_ok, qr);
+  pin_agpr<TH>(qr);
+  const float lse2 = q_ok ? a.LSE[(size_t)q * a.Hs + h] * ATTN_LOG2E : 0.f;
+  const float Dk = (DK && q_ok) ? a.Dws[(size_t)q * a.Hs + h] : 0.f;
+  const uint32_t sq = (q_ok && a.seg) ? a.seg[q] : 0u;
+
+  uint32_t mn = q_ok ? sq : 0xffffffffu, mx = q_ok ? sq : 0u;
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o));
+  }
+  if (lane == 0) sMin[wave] = mn;
+  __syncthreads();
+  uint32_t tmin = sMin[0];
+#pragma unroll
+  for (int w = 1; w < 4; ++w) tmin = min(tmin, sMin[w]);
+  const int qblk = (i0 >> 5) + qb;
+  const int q_first = i0 + qb * 32;
+  const bool store = q_first < S;
+  const int kb_lo = store ? (int)(a.blk_min[qblk] / 32) : 0;
+  const long long slot0 = store ? a.slot_off[qblk] - kb_lo : 0;
+  const int st_base = 64 * (4 * (l32 >> 3) + (l32 & 3)) + 32 * ((l32 >> 2) & 1) + 4 * hf;
+  const bool rows_full = q_first + 31 < S;
+  const int last_q = min(i0 + BR, S) - 1;
+  const int kt_lo = (int)(min(tmin, (uint32_t)last_q) / BC), kt_hi = last_q / BC;
+  float Dp = 0.f;
+
+  const uint32_t lds_kv = lds_addr(&sKV[0][0]);
+  {  // chunk 0 of the first key tile into buffer 0
+    const i32x4 rk = rows32_rsrc(Kh, kt_lo * BC, S, kstride, d);
+    const i32x4 rv = rows32_rsrc(Vh, kt_lo * BC, S, kstride, d);
+#pragma unroll
+    for (int i = 0; i < CPW; ++i) {
+      ld.load(0, i, rk, lds_kv, wave);
+      ld.load(0, i, rv, lds_kv + CT * 4, wave);
+    }
+  }
+  // the previous tile's P (role 0) or P*dP (role 1), stored after the barrier
+  // that follows it
+  bool pend = false;
+  float* pend_at = nullptr;
+  f32x16 pv;
+  auto flush = [&]() {
+    if (!pend) return;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pend_at[role * 1024 + 8 * (r >> 2) + (r & 3)] = pv[r];
+    pend = false;
+  };
+  for (int kt = kt_lo; kt <= kt_hi; ++kt) {
+    // the two column chunks of key tile kt: stage 2 (kt - kt_lo) + c sits in
+    // buffer c
+    f32x16 c0 = zero16(), c1 = zero16();
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      tile_barrier();  // chunk c resident; everyone done with the stage before
+      if (c == 0) flush();
+      // the next stage's loads into the other buffer (none after the last),
+      // spread over the products below
+      const bool more = c == 0 || kt < kt_hi;
+      const int nkt = c == 0 ? kt : kt + 1;
+      const i32x4 rk = rows32_rsrc(Kh, nkt * BC, S, kstride, d, more);
+      const i32x4 rv = rows32_rsrc(Vh, nkt * BC, S, kstride, d, more);
+      const uint32_t nxt = lds_kv + (c ^ 1) * (2 * CT * 4);
+      auto issue = [&](int j) {
+        if (j < CPW) ld.load(c ^ 1, j, rk, nxt, wave);
+        else ld.load(c ^ 1, j - CPW, rv, nxt + CT * 4, wave);
+      };
+      const SpreadLoads<2 * CPW, CC / 4, decltype(issue)> spread{issue};
+      // this chunk's contraction steps t = c CC + u, from the chunk row's
+      // half-wave hf part
+      const float* ap = &sKV[c][role * CT] + l32 * LDC + hf * CC;
+#pragma unroll
+      for (int u = 0; u < CC; u += 4) {
+        const float4 a4 = *reinterpret_cast<const float4*>(ap + u);
+        c0 = mfma32(a4.x, qr[c * CC + u], c0);
+        c1 = mfma32(a4.y, qr[c * CC + u + 1], c1);
+        spread(u / 4);
+        c0 = mfma32(a4.z, qr[c * CC + u + 2], c0);
+        c1 = mfma32(a4.w, qr[c * CC + u + 3], c1);
+      }
+    }
+    // the key tile is complete: role 0 holds S^T, role 1 dP^T (lane <-> query,
+    // register r <-> key j0 + crow(r, hf))
+    f32x16 x = c0 + c1;
+    const int j0 = kt * BC;
+    const bool full = rows_full && q_first >= j0 + 31 && mx <= (uint32_t)j0;
+    float* xch = sX + (qb * 16) * 64 + lane;
+    if (role == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + crow(r, hf);
+        const bool vis = full || (q_ok && key <= q && (uint32_t)key >= sq);
+        const float e = __builtin_amdgcn_exp2f(fmaf(x[r], sc2, -lse2));
+        x[r] = vis ? e : 0.f;
+        xch[r * 64] = x[r];
+      }
+    }
+    lds_barrier();  // role 0's P of this tile is in LDS
+    if (role == 1) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = j0 + crow(r, hf);
+        const bool vis = full || (q_ok && key <= q && (uint32_t)key >= sq);
+        const float p = xch[r * 64];  // role 0 of this block wrote it
+        const float pdp = vis ? p * (DK ? x[r] - Dk : x[r]) : 0.f;
+        if constexpr (!DK) Dp += pdp;
+        x[r] = pdp;
+      }
+    }
+    pend = store && kt >= kb_lo && kt <= qblk;
+    pend_at = pend ? a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base : nullptr;
+    pv = x;
+  }
+  tile_barrier();  // the last (empty) loads have landed before the LDS is reused or released
+  flush();
+  if constexpr (!DK) {
+    const float Dq = Dp + __shfl_xor(Dp, 32);
+    if (q_ok && hf == 0 && role == 1) a.Dws[(size_t)q * a.Hs + h] = Dq;
+  }
+  };
+  // longest rows first; paired: then the mirror tile
+  const int first = qt_hi - (int)(blockIdx.x / H), second = mirror_tile(first, qt_hi + 1, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // the first tile is done with the LDS
+    tile(second);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_dkdv: dK and dV, one workgroup per (key tile of BC = 64 rows, KV head).
 // Wave w: key block kb = w / 2 (32 keys), and either query block qs = w % 2
 // of each 64-row query tile (DP <= 128) or role w % 2 of the one 32-row query
@@ -1789,7 +2012,9 @@ static attn_status_t launch_dqkv(const BwdArgs& a, hipStream_t st, bool first) {
   const int nqt = blocks((a.S + BRq - 1) / BRq);
   attn_status_t rc = first ? profile_mark(st, true) : ATTN_OK;
   if (rc != ATTN_OK) return rc;
-  if (a.scratch)
+  if (a.scratch && DP > 128)
+    hipLaunchKernelGGL((k_dqw<DP, DK>), dim3(nqt * a.H), dim3(256), 0, st, a);
+  else if (a.scratch)
     hipLaunchKernelGGL((k_dq<DP, false, DK>), dim3(nqt * a.H), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((k_dq<DP, true, DK>), dim3(nqt * a.H), dim3(256), 0, st, a);
