@@ -222,7 +222,7 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     tflops = flops / (ms_step * 1e-3) / 1e12
     # the passes, with the algorithmic flops per visible (pair, head) of each
     # (2*d per contraction): with stored tiles k_dq forms S = Q.K^T and
-    # dP = dO.V^T, k_dkdv_p P^T.dO and dS^T.Q, k_dqs dS.K; recomputing, k_dq
+    # dP = dO.V^T (k_dqw above 128 columns), k_dkdv_p P^T.dO and dS^T.Q, k_dqs dS.K; recomputing, k_dq
     # forms Q.K^T, dO.V^T and dS.K (with the row term), k_dkdv all four
     # (the O entry's row-term kernel, k_rowdot, runs before the first pass and
     # is in ms_per_step only)
@@ -239,24 +239,30 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
         passes = [("k_cvt16", ms_q, 0.0 if with_o else 4.0), ("k_kv16", ms_k, 8.0),
                   ("k_q16", ms_s, 6.0)]
     elif stored:
-        passes = [("k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0), ("k_dqs", ms_s, 2.0)]
+        # above 128 columns the query-major pass that stores the tiles is k_dqw
+        passes = [("k_dqw" if w.d > 128 else "k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0),
+                  ("k_dqs", ms_s, 2.0)]
     else:
         passes = [("k_dq", ms_q, 6.0), ("k_dkdv", ms_k, 8.0)]
     kernel_ms = {n: round(tt / ncalls, 4) for n, tt, _ in passes}
 
-    # dominant kernel: algorithmic flops per launch / its measured average duration
+    # dominant kernel: algorithmic flops per launch / its measured average
+    # duration; with stored tiles in head chunks each pass launches once per
+    # chunk, and a launch covers that chunk's heads (the average is taken)
+    f16 = entry.startswith("attn_bwd_f16")
+    launches = (w.H + heads - 1) // heads if stored and not f16 and entry != "attn_bwd_short" else 1
     kname, kms_sum, per_pair = max(passes, key=lambda p: p[1])
-    kms = kms_sum / ncalls
-    kflops = per_pair * w.d * w.H * npairs
+    kms = kms_sum / (ncalls * launches)
+    kflops = per_pair * w.d * w.H * npairs / launches
     kach = kflops / (kms * 1e-3) / 1e12
     peak = PEAK_FP16_MFMA if entry.startswith("attn_bwd_f16") else PEAK_FP32_MFMA
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(kach / peak, 4),
-                "traffic": read_traffic(kname, w.name), "avg_launch_ms": round(kms, 4)}
+                "traffic": read_traffic(kname, w.name), "avg_launch_ms": round(kms, 4),
+                "launches_per_step": launches}
     # general path: attn_bwd_plan's figure, the most a call of this size takes
     # (with a seg: head-split partial sums); fp16: the operand copies, D and
     # LSE*log2e, before any partial sums; short: the row term D
-    f16 = entry.startswith("attn_bwd_f16")
     ws_key = ("row_term_bytes" if entry == "attn_bwd_short" else
               "fp16_copies_bytes" if f16 else "workspace_bytes_max")
     ws_val = (0 if entry == "attn_bwd_short" and with_o else
