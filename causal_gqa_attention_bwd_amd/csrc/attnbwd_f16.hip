@@ -18,7 +18,8 @@
 //   k_kv16    key-major, one workgroup per (128-key tile, KV head, head
 //             split, column part), owns its dK / dV rows and sums its heads:
 //             S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q.  4
-//             products per visible pair.
+//             products per visible pair.  k_kv16r: the same with each key
+//             block's work split over two waves by role (up to 128 columns).
 //   k_q16     query-major, one workgroup per (128-query tile, head): S^T, dP^T,
 //             dS, dQ += dS K.  3 products per visible pair.
 // Executed products per visible pair: 7 with the forward output, 9 without
@@ -760,6 +761,386 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
 }
 
 // ---------------------------------------------------------------------------
+// k_kv16r: the key-major pass of k_kv16 with the work of each key block
+// split by role over two waves, so that two waves share each SIMD and one
+// wave's products run while the other exponentiates.  One workgroup of eight
+// waves per (128-key tile, KV head, head split, column part), as k_kv16.
+// Waves 0..3 (role P) own key block w: per step they form S = Q K^T, P
+// (masked), write P in fp16 to LDS and accumulate dV += P^T dO.  Waves 4..7
+// (role dS) own key block w - 4 and run one step behind: they form
+// dP = dO V^T, read that step's P back, form dS/scale = P (dP - D) and
+// accumulate dK/scale += (dS/scale)^T Q.  P reaches dS rounded to fp16, as
+// it enters dV.  A step's stage stays in the ring until the lagging role has
+// used it; one barrier per step orders the stage loads, the P hand-over and
+// the reuse of both.  The role-dS waves issue the ring's loads.
+// ---------------------------------------------------------------------------
+template <int DP>
+struct KvrGeom {
+  static constexpr int NC = DP > 128 ? 2 : 1;  // output column parts
+  static constexpr int DW = DP / NC;
+  static constexpr int NOW = DW / 32;
+  using RT = Tile16<32, DP / 8>;
+  static constexpr int OFF_DO = RT::BYTES;
+  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE*log2e, D, seg, max seg (256 B each)
+  static constexpr int STAGE = OFF_ROW + 4 * 256;
+  static constexpr int PBYTES = 2 * 4 * 2048;    // P hand-over: [step parity][key block]
+  static constexpr int NBUF = (150 * 1024 - PBYTES) / STAGE >= 6 ? 6 : (150 * 1024 - PBYTES) / STAGE;
+  static constexpr int LPS = 2 * RT::CPW + 1;    // loads per loading wave per step
+  static_assert(NBUF >= 3, "the ring holds the lagging step, the current one and one ahead");
+  static_assert((NBUF - 3) * LPS < 64, "loads in flight fit vmcnt");
+};
+
+template <int DP, bool ROPE>
+__global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
+  using G = KvrGeom<DP>;
+  using RT = typename G::RT;
+  constexpr int NT = DP / 16, NOW = G::NOW, NBUF = G::NBUF, STAGE = G::STAGE;
+  // output tiles whose B operands are read before the exponentials (the rest
+  // right after them): all of them up to 64 columns; at 96 and 128 columns
+  // prefetching spills registers, and none is read ahead (measured at 128
+  // columns: no prefetch 0.410 ms, one tile 0.415, two 0.432)
+  constexpr int PF = NOW <= 2 ? NOW : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE + G::PBYTES];
+  char* const pbuf0 = smem + NBUF * STAGE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int role = wave >> 2, kb = wave & 3;  // role 0: S, P, dV; role 1: dP, dS, dK
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int S = a.S, H = a.H, KV = a.KV;
+  const int g = H / KV, gs = g / a.splits;
+  int b = (int)blockIdx.x, cpart = 0;
+  if constexpr (G::NC == 2) {
+    cpart = (b >> 3) & 1;
+    b = ((b >> 4) << 3) | (b & 7);
+    if (b >= a.kv_work) return;
+  }
+  const int kvh = b % KV;
+  b /= KV;
+  const int split = b % a.splits;
+  const int first_tile = b / a.splits;
+  const int nblk = (S + 31) / 32;
+  const float sc2 = a.scale * ATTN_LOG2E;
+  const uint32_t smem0 = lds_addr(smem);
+  Loader16<32, DP / 8> ldr;
+  ldr.init(DP * 2, kb, lane);  // used by the role-dS waves (loader index kb)
+
+  auto tile = [&](const int kt) __attribute__((always_inline)) {
+    const int j0 = kt * 128;
+    const int k0 = j0 + 32 * kb;
+    const int key = k0 + l32;  // < Sp: the copies hold zero rows up to Sp
+    // role P holds its keys' K rows (B operand of S = Q K^T), role dS their V
+    // rows (B operand of dP = dO V^T)
+    h8 xreg[NT];
+    const size_t boff = ((size_t)kvh * a.Sp + key) * DP + 8 * hf;
+    const _Float16* xsrc = role == 0 ? a.Kh : a.Vh;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) xreg[t] = *reinterpret_cast<const h8*>(xsrc + boff + 16 * t);
+    wait_vm<0>();
+    f32x16 acc[NOW];  // role P: dV; role dS: dK / scale
+#pragma unroll
+    for (int o = 0; o < NOW; ++o) {
+      acc[o] = zero16();
+      asm volatile("" : "+v"(acc[o]));
+    }
+
+    const uint32_t khi = (uint32_t)min(j0 + 127, S - 1);
+    int segb = j0 >> 5;
+    auto seg_mask = [&](int bb) -> uint64_t {
+      const int qb = bb + lane;
+      return __ballot(qb < nblk && a.blk_min[qb] <= khi);
+    };
+    uint64_t mask = segb < nblk ? seg_mask(segb) : 0ull;
+    auto next_block = [&](int prev) -> int {
+      if (prev >= segb) {
+        const int sh = prev - segb + 1;
+        mask = sh >= 64 ? 0ull : (mask >> sh) << sh;
+      }
+      while (mask == 0ull) {
+        segb += 64;
+        if (segb >= nblk) return -1;
+        mask = seg_mask(segb);
+      }
+      return segb + (int)__builtin_ctzll(mask);
+    };
+    auto next_step = [&](int& qb, int& hh) {
+      if (qb < 0) return;
+      if (++hh == gs) {
+        hh = 0;
+        qb = next_block(qb);
+      }
+    };
+
+    // the role-dS waves load a step's stage (loader wave index kb)
+    auto issue = [&](int qb, int hh, int buf) {
+      const int head = kvh * g + split * gs + hh;
+      const uint32_t st = smem0 + (uint32_t)(buf * STAGE);
+      const size_t roff = ((size_t)head * a.Sp + (size_t)qb * 32) * DP;
+      ldr.load(buf_rsrc(a.Qh + roff, 32 * DP * 2), st, kb);
+      ldr.load(buf_rsrc(a.dOh + roff, 32 * DP * 2), st + G::OFF_DO, kb);
+      const int rows = min(32, S - qb * 32);
+      const bool rok = hf == 0 && l32 < rows;
+      const uint32_t roff4 = rok ? (uint32_t)(l32 * H + head) * 4u : ATTN_BUF_OOB;
+      const uint32_t rbytes = (uint32_t)(rows * H * 4);
+      if (kb == 0) dma4(buf_rsrc(a.LSE2 + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW);
+      else if (kb == 1) dma4(buf_rsrc(a.D + (size_t)qb * 32 * H, rbytes), roff4, st + G::OFF_ROW + 256);
+      else if (kb == 2)
+        dma4(buf_rsrc(a.seg ? (const void*)(a.seg + (size_t)qb * 32) : (const void*)a.LSE,
+                      a.seg ? (uint32_t)rows * 4u : 0u),
+             rok ? (uint32_t)l32 * 4u : ATTN_BUF_OOB, st + G::OFF_ROW + 512);
+      else dma4(buf_rsrc(a.seg ? (const void*)(a.blk_max + qb) : (const void*)a.LSE,
+                         a.seg ? 4u : 0u),
+                lane == 0 ? 0u : ATTN_BUF_OOB, st + G::OFF_ROW + 768);
+    };
+
+    // role P, step (qb, buf): S, P (written to the hand-over slot), dV.  The
+    // operand reads are issued ahead of their products (scheduling barriers
+    // keep the compiler from sinking them): all of S's, then, before the
+    // exponentials, all of dV's
+    auto compute_p = [&](int qb, int buf, int par) {
+      const int q0 = qb * 32;
+      if (k0 > q0 + 31) return;  // every key of the block after every query
+      const char* st = smem + buf * STAGE;
+      const uint32_t mx = __builtin_amdgcn_readfirstlane(
+          *reinterpret_cast<const uint32_t*>(st + G::OFF_ROW + 768));
+      const bool full = (k0 + 31 <= q0) & (q0 + 31 < S) & (mx <= (uint32_t)k0);
+      // S's operand reads in groups of at most 8, each issued ahead of its products
+      f32x16 s = zero16();
+#pragma unroll
+      for (int t0 = 0; t0 < NT; t0 += 8) {
+        h8 qop[8];
+#pragma unroll
+        for (int t = 0; t < 8 && t0 + t < NT; ++t)
+          qop[t] = *reinterpret_cast<const h8*>(st + RT::at(l32, 2 * (t0 + t) + hf));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8 && t0 + t < NT; ++t) s = mfma16(qop[t], xreg[t0 + t], s);
+      }
+      h8 ov[NOW][2];
+      auto read_ov = [&](int o) __attribute__((always_inline)) {
+        const int n0 = cpart * G::DW + 32 * o;
+        ov[o][0] = tr_operand<RT>(st + G::OFF_DO, 4 * hf, 8 + 4 * hf, n0, lane);
+        ov[o][1] = tr_operand<RT>(st + G::OFF_DO, 16 + 4 * hf, 24 + 4 * hf, n0, lane);
+      };
+#pragma unroll
+      for (int o = 0; o < PF; ++o) read_ov(o);
+      float lse[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(st + G::OFF_ROW + 4 * (8 * a4 + 4 * hf));
+        lse[4 * a4] = l4.x; lse[4 * a4 + 1] = l4.y; lse[4 * a4 + 2] = l4.z; lse[4 * a4 + 3] = l4.w;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r]));
+      } else {
+        uint32_t sg[16];
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const uint4 s4 =
+              *reinterpret_cast<const uint4*>(st + G::OFF_ROW + 512 + 4 * (8 * a4 + 4 * hf));
+          sg[4 * a4] = s4.x; sg[4 * a4 + 1] = s4.y; sg[4 * a4 + 2] = s4.z; sg[4 * a4 + 3] = s4.w;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qq = q0 + crow(r, hf);
+          const bool vis = (qq < S) & (key <= qq) & ((uint32_t)key >= sg[r]);
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[r], sc2, -lse[r]));
+          s[r] = vis ? e : 0.f;
+        }
+      }
+      const h8 p0 = pack8(s, 0), p1 = pack8(s, 1);
+      char* pb = pbuf0 + (par * 4 + kb) * 2048;
+      *reinterpret_cast<h8*>(pb + 16 * lane) = p0;
+      *reinterpret_cast<h8*>(pb + 1024 + 16 * lane) = p1;
+#pragma unroll
+      for (int o = PF; o < NOW; ++o) read_ov(o);
+#pragma unroll
+      for (int o = 0; o < NOW; ++o) {
+        acc[o] = mfma16(p0, ov[o][0], acc[o]);
+        acc[o] = mfma16(p1, ov[o][1], acc[o]);
+        asm volatile("" : "+v"(acc[o]));
+      }
+    };
+
+    // role dS, in the order that puts its products beside role P's
+    // exponentials: first dS/scale = P (dP - D) of step i - 1 and its
+    // products dK/scale += (dS/scale)^T Q (ds_finish), then dP = dO V^T of
+    // step i (ds_start), kept in registers for the next iteration
+    f32x16 dpc = zero16();
+    auto ds_start = [&](int qb, int buf) {
+      if (k0 > qb * 32 + 31) return;
+      const char* st = smem + buf * STAGE;
+      dpc = zero16();
+#pragma unroll
+      for (int t0 = 0; t0 < NT; t0 += 8) {
+        h8 dop[8];
+#pragma unroll
+        for (int t = 0; t < 8 && t0 + t < NT; ++t)
+          dop[t] = *reinterpret_cast<const h8*>(st + G::OFF_DO + RT::at(l32, 2 * (t0 + t) + hf));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 8 && t0 + t < NT; ++t) dpc = mfma16(dop[t], xreg[t0 + t], dpc);
+      }
+    };
+    auto ds_finish = [&](int qb, int buf, int par) {
+      if (k0 > qb * 32 + 31) return;
+      const char* st = smem + buf * STAGE;
+      h8 qv[NOW][2];
+      auto read_qv = [&](int o) __attribute__((always_inline)) {
+        const int n0 = cpart * G::DW + 32 * o;
+        qv[o][0] = tr_operand<RT>(st, 4 * hf, 8 + 4 * hf, n0, lane);
+        qv[o][1] = tr_operand<RT>(st, 16 + 4 * hf, 24 + 4 * hf, n0, lane);
+      };
+      const char* pb = pbuf0 + (par * 4 + kb) * 2048;
+      const h8 p0 = *reinterpret_cast<const h8*>(pb + 16 * lane);
+      const h8 p1 = *reinterpret_cast<const h8*>(pb + 1024 + 16 * lane);
+      float dv[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 d4 =
+            *reinterpret_cast<const float4*>(st + G::OFF_ROW + 256 + 4 * (8 * a4 + 4 * hf));
+        dv[4 * a4] = d4.x; dv[4 * a4 + 1] = d4.y; dv[4 * a4 + 2] = d4.z; dv[4 * a4 + 3] = d4.w;
+      }
+#pragma unroll
+      for (int o = 0; o < PF; ++o) read_qv(o);
+      __builtin_amdgcn_sched_barrier(0);
+      const f32x8 pf0 = __builtin_convertvector(p0, f32x8);
+      const f32x8 pf1 = __builtin_convertvector(p1, f32x8);
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = (r < 8 ? pf0[r] : pf1[r - 8]) * (dpc[r] - dv[r]);
+      const h8 d0 = pack8(ds, 0), d1 = pack8(ds, 1);
+#pragma unroll
+      for (int o = PF; o < NOW; ++o) read_qv(o);
+#pragma unroll
+      for (int o = 0; o < NOW; ++o) {
+        acc[o] = mfma16(d0, qv[o][0], acc[o]);
+        acc[o] = mfma16(d1, qv[o][1], acc[o]);
+        asm volatile("" : "+v"(acc[o]));
+      }
+    };
+
+    // the ring: role P computes step i in stage buf, role dS step i - 1 in
+    // stage pbuf; steps i + 1 .. i + NBUF - 3 are in flight, and after the
+    // barrier step i + NBUF - 2 is issued into the stage of step i - 2.  Each
+    // role runs its own copy of the loop (same steps, same barriers), so that
+    // each loop has a single path through its products.
+    auto ring = [&](auto&& work) __attribute__((always_inline)) {
+      int rq[NBUF - 1], rh[NBUF - 1];  // steps i .. i + NBUF - 2 (rq = -1: none)
+      rq[0] = next_block(-1);
+      rh[0] = 0;
+#pragma unroll
+      for (int k = 1; k < NBUF - 1; ++k) {
+        rq[k] = rq[k - 1];
+        rh[k] = rh[k - 1];
+        next_step(rq[k], rh[k]);
+      }
+      if (role == 1) {
+#pragma unroll
+        for (int k = 0; k < NBUF - 2; ++k)
+          if (rq[k] >= 0) issue(rq[k], rh[k], k);
+      }
+      int pq = -1, pbuf = 0, buf = 0, par = 0;
+      while (rq[0] >= 0 || pq >= 0) {
+        if (role == 1) {
+          // this wave's loads of step i have landed once at most those of the
+          // later issued steps (i + 1 .. i + NBUF - 3) are outstanding
+          int ahead = 0;
+#pragma unroll
+          for (int k = 1; k < NBUF - 2; ++k) ahead += rq[k] >= 0;
+          if constexpr (NBUF >= 6) {
+            if (ahead >= 3) wait_vm<3 * G::LPS>();
+            else if (ahead == 2) wait_vm<2 * G::LPS>();
+            else if (ahead == 1) wait_vm<G::LPS>();
+            else wait_vm<0>();
+          } else if constexpr (NBUF == 5) {
+            if (ahead >= 2) wait_vm<2 * G::LPS>();
+            else if (ahead == 1) wait_vm<G::LPS>();
+            else wait_vm<0>();
+          } else if constexpr (NBUF == 4) {
+            if (ahead >= 1) wait_vm<G::LPS>();
+            else wait_vm<0>();
+          } else {
+            wait_vm<0>();
+          }
+        }
+        // step i resident; P of step i - 1 written; step i - 2's stage and
+        // hand-over slot done with
+        asm volatile("s_barrier" ::: "memory");
+        if (role == 1 && rq[NBUF - 2] >= 0)
+          issue(rq[NBUF - 2], rh[NBUF - 2], (buf + NBUF - 2) % NBUF);
+        work(rq[0], buf, par, pq, pbuf);
+        pq = rq[0];
+        pbuf = buf;
+        int nq = rq[NBUF - 2], nh = rh[NBUF - 2];
+        next_step(nq, nh);
+#pragma unroll
+        for (int k = 0; k < NBUF - 2; ++k) {
+          rq[k] = rq[k + 1];
+          rh[k] = rh[k + 1];
+        }
+        rq[NBUF - 2] = nq;
+        rh[NBUF - 2] = nh;
+        buf = (buf + 1) % NBUF;
+        par ^= 1;
+      }
+    };
+    if (role == 0)
+      ring([&](int q, int bf, int pr, int, int) {
+        if (q >= 0) compute_p(q, bf, pr);
+      });
+    else
+      ring([&](int q, int bf, int pr, int pq, int pbf) {
+        if (pq >= 0) ds_finish(pq, pbf, pr ^ 1);
+        if (q >= 0) ds_start(q, bf);
+      });
+    __syncthreads();  // every wave done with the ring before it is reused
+
+    // rows key k0 + crow(r, hf), the part's columns: role P adds dV, role dS
+    // scale * dK (with RoPE dK = R^T (dK + scale * acc)), or this split's
+    // partial sums into part
+    const size_t kstride = (size_t)KV * a.d;
+    const size_t slice = (size_t)S * kstride;
+    const int nrows = max(0, min(32, S - k0));
+    const uint32_t rbytes =
+        nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * kstride + a.d) * 4) : 0u;
+    const size_t base = (size_t)kvh * a.d + (size_t)k0 * kstride;
+    float* const whole = role == 0 ? a.dV : a.dK;
+    const auto rO = out_rsrc((a.splits == 1 ? whole : a.part + (size_t)(2 * split + (role == 0)) * slice) +
+                                 base,
+                             rbytes);
+    const float f = role == 0 ? 1.f : a.scale;
+#pragma unroll
+    for (int o = 0; o < NOW; ++o) {
+      const int col = cpart * G::DW + 32 * o + l32;
+      const double fq = ROPE ? rope_freq(col, a.d, a.rope_base) : 0.0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = crow(r, hf);
+        const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * kstride + col) * 4)
+                                                       : ATTN_BUF_OOB;
+        if (a.splits == 1) {
+          float v = buf_ld(rO, off) + f * acc[o][r];
+          if constexpr (ROPE) {
+            const float partner = __shfl_xor(v, 1);
+            if (role == 1) v = rope_back(v, partner, col, (long long)k0 + rr + a.rope_pos, fq);
+          }
+          buf_st(rO, off, v);
+        } else {
+          buf_st(rO, off, f * acc[o][r]);
+        }
+      }
+    }
+  };
+  const int first = first_tile;
+  const int second = mirror_tile(first, (S + 127) / 128, a.pair);
+  tile(first);
+  if (second >= 0) tile(second);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 template <int DP>
@@ -783,10 +1164,23 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
   const int kv_grid = KvGeom<DP>::NC == 2 ? (f.kv_work + 7) / 8 * 16 : f.kv_work;
-  if (f.rope)
-    hipLaunchKernelGGL((k_kv16<DP, true>), dim3(kv_grid), dim3(256), 0, st, f);
-  else
-    hipLaunchKernelGGL((k_kv16<DP, false>), dim3(kv_grid), dim3(256), 0, st, f);
+  // the role-split key-major kernel where its 256 registers per wave hold
+  // the work without spilling (up to 128 columns; at 128 with RoPE the
+  // write-back's rotation spills, 0.535 against 0.452 ms); else one wave per
+  // key block
+  if constexpr (DP <= 96) {
+    if (f.rope)
+      hipLaunchKernelGGL((k_kv16r<DP, true>), dim3(kv_grid), dim3(512), 0, st, f);
+    else
+      hipLaunchKernelGGL((k_kv16r<DP, false>), dim3(kv_grid), dim3(512), 0, st, f);
+  } else if (DP == 128 && !f.rope) {
+    hipLaunchKernelGGL((k_kv16r<128, false>), dim3(kv_grid), dim3(512), 0, st, f);
+  } else {
+    if (f.rope)
+      hipLaunchKernelGGL((k_kv16<DP, true>), dim3(kv_grid), dim3(256), 0, st, f);
+    else
+      hipLaunchKernelGGL((k_kv16<DP, false>), dim3(kv_grid), dim3(256), 0, st, f);
+  }
   rc = hip_check(hipGetLastError(), "launching k_kv16");
   if (rc == ATTN_OK && f.splits > 1) {
     rc = launch_sumparts(f.part, f.splits, f.S, f.KV * f.d, (long long)f.KV * f.d, f.dK, f.dV, st,
