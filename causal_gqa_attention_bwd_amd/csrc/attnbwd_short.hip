@@ -546,10 +546,14 @@ extern "C" attn_status_t attn_bwd_short(const float* Q, const float* K, const fl
   // a wave keeps its rows' halves of K, V (key role) or Q, dO (query role)
   // and two items' operand rows in registers, and each wave stages two
   // 32-row tiles in LDS: above 128 columns neither fits (LDS alone would be
-  // 4 * 2 * 32 * (192 + 4) * 4 bytes = 200 KB at 192 columns)
+  // 4 * 2 * 32 * (192 + 4) * 4 bytes = 200 KB at 192 columns).  Those head
+  // dims run the general path's kernels (the same sums; several launches and
+  // a workspace)
   if (head_dim > 128)
-    return fail(ATTN_ERR_UNSUPPORTED, "head_dim = %d is above 128 (use attn_bwd or attn_bwd_o)",
-                head_dim);
+    return O ? attn_bwd_o(Q, K, V, O, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads,
+                          head_dim, scale, stream)
+             : attn_bwd(Q, K, V, dO, LSE, seg, dQ, dK, dV, seq_len, n_heads, n_kv_heads, head_dim,
+                        scale, stream);
   // the kernels address every tensor with 32-bit byte offsets
   if ((long long)seq_len * n_heads * head_dim * 4 >= (1LL << 31))
     return fail(ATTN_ERR_UNSUPPORTED, "seq_len * n_heads * head_dim * 4 = %lld bytes is 2^31 or more",

@@ -229,9 +229,12 @@ attn_status_t attn_bwd_f16_rope(const float* Q, const float* K, const float* V, 
  * of two dividing n_heads / n_kv_heads, chosen from the shape alone), write
  * partial dK, dV sums to a workspace of 2 * splits * seq_len * n_kv_heads *
  * head_dim * 4 bytes, and one more launch adds them in split order (still
- * deterministic).  Errors as attn_bwd, plus ATTN_ERR_UNSUPPORTED for
- * seq_len > 1024, head_dim > 128 (attn_bwd and attn_bwd_o take those), or
- * seq_len * n_heads * head_dim * 4 >= 2^31.
+ * deterministic).  Above 128 columns (up to the 256 of every entry) the
+ * single-launch kernels do not fit a wave's registers, and the call runs
+ * attn_bwd_o (O given) or attn_bwd instead: the same results, with their
+ * launches and workspace.  Errors as attn_bwd, plus ATTN_ERR_UNSUPPORTED for
+ * seq_len > 1024, or, up to 128 columns, seq_len * n_heads * head_dim * 4 >=
+ * 2^31.
  */
 attn_status_t attn_bwd_short(const float* Q, const float* K, const float* V, const float* O,
                              const float* dO, const float* LSE, const uint32_t* seg,

@@ -43,7 +43,7 @@ CASES = [
     ("attn_bwd_short", bwd_args(H=3, KV=2), INVALID, "multiple"),
     ("attn_bwd_short", bwd_args(scale=math.inf), INVALID, "scale"),
     ("attn_bwd_short", bwd_args(S=1025), UNSUPPORTED, "1024"),
-    ("attn_bwd_short", bwd_args(d=144), UNSUPPORTED, "128"),
+    ("attn_bwd_short", bwd_args(d=272), UNSUPPORTED, "head_dim"),
     ("attn_bwd_short", bwd_args(d=24), UNSUPPORTED, "head_dim"),
     ("attn_bwd_short", bwd_args(mis="dK"), UNSUPPORTED, "aligned"),
     ("attn_bwd_short", bwd_args(S=1024, H=16384, KV=1, d=64), UNSUPPORTED, "2^31"),

@@ -4,7 +4,8 @@ element: max|gpu - oracle| <= 2e-3 * max|oracle| per gradient (the fp32 path's
 bar; fp32 products and sums).
 
 Covered: the three short workloads whole, with and without O; every padded
-head-dim class (32, 64, 96, 128) with d = 16 .. 128; every mask kind (plain causal,
+head-dim class (32, 64, 96, 128) with d = 16 .. 128, and above 128 columns (144,
+192, 256), where the entry runs the general path; every mask kind (plain causal,
 documents, arbitrary starts, rows that see no key); lengths 1, 2, ragged
 tails (33, 97, 1000) and the maximum 1024 with several waves' worth of blocks;
 KV groups of 1 .. 8 heads, with the key blocks' heads split over 1, 2, 4 and 8
@@ -13,8 +14,8 @@ per group, 4 at S=1024 with 4 (or 8 heads per group over 2 KV heads), 8 at
 S=1024 with 8 heads over one KV head); nonzero initial outputs
 (+=); repeatability (the
 sums have a fixed order, so two calls agree bit for bit); agreement of the O
-and row-term forms; and the size limits (ATTN_ERR_UNSUPPORTED above 1024
-positions or 128 columns).
+and row-term forms; and the size limit (ATTN_ERR_UNSUPPORTED above 1024
+positions).
 """
 import numpy as np
 import pytest
@@ -48,6 +49,12 @@ SHORT_EDGE = [  # S, H, KV, d, mask
     (1024, 8, 8, 128, "docs"),
     (1024, 16, 2, 128, "causal"),   # group of 8 split over the key role
     (3, 3, 3, 128, "singletons"),
+    # above 128 columns: the general path's kernels
+    (200, 4, 2, 144, "docs"),
+    (1024, 8, 2, 192, "causal"),
+    (513, 4, 1, 256, "arbitrary"),
+    (300, 2, 2, 256, "empty_rows"),
+    (64, 4, 2, 256, "singletons"),
 ]
 
 
@@ -90,7 +97,7 @@ def test_short_repeats_bit_for_bit():
             assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("S,d", [(1025, 32), (512, 144)])
+@pytest.mark.parametrize("S,d", [(1025, 32), (1025, 256)])
 def test_short_rejects_sizes_beyond_its_limits(S, d):
     H = KV = 1
     z = lambda *shape: torch.zeros(shape, dtype=torch.float32, device=dev())
