@@ -2135,14 +2135,16 @@ static int chunk_heads(int H, int KV, long long fit) {
 // Unpaired calls (a seg given): paired tiles carry equal work; unpaired,
 // under a document mask, the first key tile of a long document can hold more
 // work than a CU's share of the whole pass, so k_dkdv_p splits each group's
-// heads over workgroups until the launch has ~1024 of them (S=16384, 2 KV
+// heads over workgroups until the launch has ~2048 of them (S=16384, 2 KV
 // heads, documents: the longest workgroup came down from 1.3 to 1.12 times
-// the mean load of a CU).  Hc heads over KVc KV heads in this launch.
+// the mean load of a CU at ~1024; 4 splits instead of 2 then took k_dkdv_p
+// from 4.44 to 4.18 ms, 8 splits 4.28 ms).  Hc heads over KVc KV heads in
+// this launch.
 static int head_splits(int S, int Hc, int KVc) {
   const long long blocks = ((long long)S + 63) / 64 * KVc;
   const int gc = Hc / KVc;
   int hs = 1;
-  while (blocks * hs < 1024 && gc % (2 * hs) == 0) hs *= 2;
+  while (blocks * hs < 2048 && gc % (2 * hs) == 0) hs *= 2;
   return hs;
 }
 

@@ -101,12 +101,12 @@ typedef enum {
  * the pool cannot supply the workspace (out of device memory), the call
  * recomputes the scores in the key-major pass instead and the workspace is
  * only D and the metadata.  With the scratch, a call given a seg whose
- * key-major pass would have fewer than 1024 workgroups (64-key tiles x KV
+ * key-major pass would have fewer than 2048 workgroups (64-key tiles x KV
  * heads of a chunk) splits each group's heads over 2^k workgroups (k as
  * large as that bound and the group size allow); the first adds into dK, dV,
  * and the workspace then also holds the others' partial dK and dV:
- * 2 * (2^k - 1) * seq_len * n_kv_heads * head_dim * 4 bytes (32 MiB at
- * seq_len 16384, 2 KV heads, head_dim 256, 2 splits).  attn_bwd_plan reports
+ * 2 * (2^k - 1) * seq_len * n_kv_heads * head_dim * 4 bytes (192 MiB at
+ * seq_len 16384, 2 KV heads, head_dim 256, 4 splits).  attn_bwd_plan reports
  * the choice and the largest size for a problem.
  *
  * seq_len == 0 returns ATTN_OK and enqueues nothing.

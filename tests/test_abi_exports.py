@@ -71,13 +71,13 @@ def test_plan_sizes_the_workspace(limit):
     # triangle), each part 256-byte aligned, then -- the most a call takes is
     # an unpaired one -- the partial dK, dV of the key-major head splits: 64
     # key tiles x 8 KV heads = 512 workgroups, so the 4 heads of a group go
-    # to 2 workgroups; the first adds into dK, dV, the second writes an
-    # [S, KV, d] slice of dK and one of dV
+    # to 4 workgroups (about 2048 in all); the first adds into dK, dV, each
+    # of the other 3 writes an [S, KV, d] slice of dK and one of dV
     limit(DEFAULT_LIMIT)
     S, H = 4096, 32
     nblk = S // 32
     meta = up(up(up(S * H * 4) + 2 * nblk * 4) + (nblk + 1) * 8)
-    part = 2 * 1 * S * 8 * 128 * 4
+    part = 2 * 3 * S * 8 * 128 * 4
     assert binding.bwd_plan_heads(S, H, 8, 128) == (meta + causal_pairs(nblk) * H * 8192 + part, H)
     # a group of one head cannot split
     assert binding.bwd_plan(S, 8, 8, 128) == (
