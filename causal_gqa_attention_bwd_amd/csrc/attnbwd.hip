@@ -1403,14 +1403,6 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) pd[r] = fmaf(-p[r], Dv[8 * (r >> 2) + (r & 3)], pd[r]);
       }
-      // dS/scale replaces P*dP in the scratch for k_dqs (all waves read this
-      // item's tiles before the barrier above; one writer per tile).  With a
-      // given row term (DK) the tile already holds dS/scale.
-      if (!DK && (!DSPLIT || (wave & 1) == 0)) {
-        float* t = a.scratch + (size_t)cslot * ATTN_TILE_FLOATS + 1024 + lane;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) t[64 * r] = pd[r];
-      }
       // dV += P^T dO; the Q operands of the dK products and the next item's
       // loads go out between these products
 #pragma unroll
@@ -1422,11 +1414,18 @@ __global__ __launch_bounds__(256) void k_dkdv_p(BwdArgs a) {
         for (int nb = 0; nb < NB; ++nb) qv[r][nb] = row[nb];
         SpreadLoads<NLOAD, 16, decltype(issue)>{issue}(r);
       }
-      // dK += (dS/scale)^T Q
+      // dK += (dS/scale)^T Q.  dS/scale replaces P*dP in the scratch for
+      // k_dqs (all waves read this item's tiles before the barrier above; one
+      // writer per tile), stored between these products: stored before the
+      // dV products they held up the phase's start (S=4096: k_dkdv_p 1.28 ->
+      // 1.25 ms).  With a given row term (DK) the tile already holds dS/scale.
+      const bool wr = !DK && (!DSPLIT || (wave & 1) == 0);
+      float* const tds = a.scratch + (size_t)cslot * ATTN_TILE_FLOATS + 1024 + lane;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) accK[nb] = mfma32(pd[r], qv[r][nb], accK[nb]);
+        if (wr) tds[64 * r] = pd[r];
       }
     } else {
 #pragma unroll
