@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
   };
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     tile_barrier();  // tile kt resident; everyone done with tile kt-1
-    flush();
+    if constexpr (PG::ROLE) flush();
     const float* sK = &sKV[buf][0];
     const float* sV = &sKV[buf][TILE];
     const uint32_t nxt = lds_kv + (buf ^ 1) * (2 * TILE * 4);
@@ -559,7 +559,28 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
       if (j < NLOAD / 2) ld.load(j, rk, nxt, wave);
       else ld.load(j - NLOAD / 2, rv, nxt + TILE * 4, wave);
     };
-    const SpreadLoads<NLOAD, PG::TH / 4, decltype(issue)> spread{issue};
+    // Without roles the previous tile's stores (8 groups of four values) go
+    // out first, then the loads, spread over the score products: stored all
+    // at once after the barrier, they held up the first products (S=4096:
+    // 1.32 -> 1.17 ms)
+    auto issue2 = [&](int j) {
+      if constexpr (!PG::ROLE && !ACC) {
+        if (j < 8) {
+          if (pend) {
+            const f32x16& v = j < 4 ? pst : pdt;
+            const int m = j & 3;
+            *reinterpret_cast<float4*>(pend_at + (j < 4 ? 0 : 1024) + 8 * m) =
+                make_float4(v[4 * m], v[4 * m + 1], v[4 * m + 2], v[4 * m + 3]);
+          }
+          return;
+        }
+        issue(j - 8);
+      } else {
+        issue(j);
+      }
+    };
+    constexpr int NSP = (!PG::ROLE && !ACC) ? NLOAD + 8 : NLOAD;
+    const SpreadLoads<NSP, PG::TH / 4, decltype(issue2)> spread{issue2};
 
     // B operands of the accumulation below (independent of the scores): read
     // them now so that the accumulation runs without LDS waits
@@ -827,7 +848,7 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       tile_barrier();  // chunk c resident; everyone done with the stage before
-      if (c == 0) flush();
+      // the previous tile's stores (chunk 0, four groups of four values) and
       // the next stage's loads into the other buffer (none after the last),
       // spread over the products below
       const bool more = c == 0 || kt < kt_hi;
@@ -836,10 +857,18 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
       const i32x4 rv = rows32_rsrc(Vh, nkt * BC, S, kstride, d, more);
       const uint32_t nxt = lds_kv + (c ^ 1) * (2 * CT * 4);
       auto issue = [&](int j) {
-        if (j < CPW) ld.load(c ^ 1, j, rk, nxt, wave);
-        else ld.load(c ^ 1, j - CPW, rv, nxt + CT * 4, wave);
+        if (j < 4) {
+          if (c == 0 && pend) {
+            float* dst = pend_at + role * 1024 + 8 * j;
+            *reinterpret_cast<float4*>(dst) = make_float4(pv[4 * j], pv[4 * j + 1], pv[4 * j + 2], pv[4 * j + 3]);
+          }
+        } else if (j < 4 + CPW) {
+          ld.load(c ^ 1, j - 4, rk, nxt, wave);
+        } else {
+          ld.load(c ^ 1, j - 4 - CPW, rv, nxt + CT * 4, wave);
+        }
       };
-      const SpreadLoads<2 * CPW, CC / 4, decltype(issue)> spread{issue};
+      const SpreadLoads<4 + 2 * CPW, CC / 4, decltype(issue)> spread{issue};
       // this chunk's contraction steps t = c CC + u, from the chunk row's
       // half-wave hf part
       const float* ap = &sKV[c][role * CT] + l32 * LDC + hf * CC;
