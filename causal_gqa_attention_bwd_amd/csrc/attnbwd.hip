@@ -708,8 +708,10 @@ __global__ __launch_bounds__(256) void k_dq(BwdArgs a) {
 // columns hf*TH + t; chunk c holds t in [c*TH/2, (c+1)*TH/2)), double
 // buffered: 68 KB.  Role 0 forms P and hands it to role 1 through LDS (8 KB,
 // one direction); role 1 forms P*dP (with D given: dS/scale = P (dP - D)) and
-// the row term.  Role 0 stores the P tiles, role 1 the P*dP tiles, each
-// right after the barrier that follows them.  Two workgroups per CU put two
+// the row term one tile later, beside role 0's next products (S=16384,
+// d=256: 4.02 -> 3.85 ms against a barrier between the exponentials and
+// P*dP).  Role 0 stores the P tiles, role 1 the P*dP tiles, each spread over
+// the next tile's first products.  Two workgroups per CU put two
 // waves on each SIMD (one workgroup of four waves with the whole tile in LDS
 // left one), so one wave's products run while the other exponentiates,
 // exchanges or waits at a barrier.
@@ -830,8 +832,13 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
       ld.load(0, i, rv, lds_kv + CT * 4, wave);
     }
   }
-  // the previous tile's P (role 0) or P*dP (role 1), stored after the barrier
-  // that follows it
+  // Role 0 forms P of tile kt and hands it over in sX; role 1 forms P*dP of
+  // tile kt one tile later, at the start of tile kt + 1 (it keeps dP^T of kt
+  // in registers), so that its arithmetic runs beside role 0's products and
+  // no barrier sits between the exponentials and P*dP.  sX has one slot per
+  // query block: role 1 reads P of kt before the chunk-1 barrier of kt + 1,
+  // and role 0 writes P of kt + 1 after it.  Each role's values of a tile
+  // are stored during the next tile's chunk-0 products.
   bool pend = false;
   float* pend_at = nullptr;
   f32x16 pv;
@@ -841,6 +848,27 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
     for (int r = 0; r < 16; ++r) pend_at[role * 1024 + 8 * (r >> 2) + (r & 3)] = pv[r];
     pend = false;
   };
+  float* xch = sX + (qb * 16) * 64 + lane;
+  f32x16 xprev = zero16();  // role 1: dP^T of the previous tile
+  int kprev = -1;           // the previous tile (-1: none)
+  // role 1: P*dP (DK: P*(dP - D)) of tile kp from its P in sX and dP^T in xprev
+  auto finish_pdp = [&](int kp) __attribute__((always_inline)) {
+    const int jp = kp * BC;
+    const bool fullp = rows_full && q_first >= jp + 31 && mx <= (uint32_t)jp;
+    f32x16 y;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = jp + crow(r, hf);
+      const bool vis = fullp || (q_ok && key <= q && (uint32_t)key >= sq);
+      const float p = xch[r * 64];  // role 0 of this block wrote it
+      const float pdp = vis ? p * (DK ? xprev[r] - Dk : xprev[r]) : 0.f;
+      if constexpr (!DK) Dp += pdp;
+      y[r] = pdp;
+    }
+    pend = store && kp >= kb_lo && kp <= qblk;
+    pend_at = pend ? a.scratch + ((slot0 + kp) * H + h) * ATTN_TILE_FLOATS + st_base : nullptr;
+    pv = y;
+  };
   for (int kt = kt_lo; kt <= kt_hi; ++kt) {
     // the two column chunks of key tile kt: stage 2 (kt - kt_lo) + c sits in
     // buffer c
@@ -848,6 +876,8 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       tile_barrier();  // chunk c resident; everyone done with the stage before
+      // role 1, chunk 0: P*dP of the previous tile (its P is in sX now)
+      if (c == 0 && role == 1 && kprev >= 0) finish_pdp(kprev);
       // the previous tile's stores (chunk 0, four groups of four values) and
       // the next stage's loads into the other buffer (none after the last),
       // spread over the products below
@@ -881,13 +911,13 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
         c0 = mfma32(a4.z, qr[c * CC + u + 2], c0);
         c1 = mfma32(a4.w, qr[c * CC + u + 3], c1);
       }
+      if (c == 0) pend = false;  // chunk 0 issued the stores
     }
     // the key tile is complete: role 0 holds S^T, role 1 dP^T (lane <-> query,
     // register r <-> key j0 + crow(r, hf))
     f32x16 x = c0 + c1;
     const int j0 = kt * BC;
     const bool full = rows_full && q_first >= j0 + 31 && mx <= (uint32_t)j0;
-    float* xch = sX + (qb * 16) * 64 + lane;
     if (role == 0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -897,25 +927,20 @@ __global__ __launch_bounds__(256, 2) void k_dqw(BwdArgs a) {
         x[r] = vis ? e : 0.f;
         xch[r * 64] = x[r];
       }
+      pend = store && kt >= kb_lo && kt <= qblk;
+      pend_at = pend ? a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base : nullptr;
+      pv = x;
+    } else {
+      xprev = x;
     }
-    lds_barrier();  // role 0's P of this tile is in LDS
-    if (role == 1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = j0 + crow(r, hf);
-        const bool vis = full || (q_ok && key <= q && (uint32_t)key >= sq);
-        const float p = xch[r * 64];  // role 0 of this block wrote it
-        const float pdp = vis ? p * (DK ? x[r] - Dk : x[r]) : 0.f;
-        if constexpr (!DK) Dp += pdp;
-        x[r] = pdp;
-      }
-    }
-    pend = store && kt >= kb_lo && kt <= qblk;
-    pend_at = pend ? a.scratch + ((slot0 + kt) * H + h) * ATTN_TILE_FLOATS + st_base : nullptr;
-    pv = x;
+    kprev = kt;
   }
-  tile_barrier();  // the last (empty) loads have landed before the LDS is reused or released
+  tile_barrier();  // the last (empty) loads have landed; P of the last tile is in sX
   flush();
+  if (role == 1 && kprev >= 0) {
+    finish_pdp(kprev);
+    flush();
+  }
   if constexpr (!DK) {
     const float Dq = Dp + __shfl_xor(Dp, 32);
     if (q_ok && hf == 0 && role == 1) a.Dws[(size_t)q * a.Hs + h] = Dq;
