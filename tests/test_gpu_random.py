@@ -37,8 +37,11 @@ def draw(i):
     return p, init, f"random {i}: S={S} H={H} KV={KV} d={d} {kind}"
 
 
+# draw 2299 (S=686, H=4, KV=4, d=32, documents) has dV entries far smaller
+# than their nonzero initial values: there the fp32 rounding of the output
+# exceeds the gradient's own fp16 bound, which the allowance now counts
 @pytest.mark.parametrize("mode", ["plain", "o", "f16", "f16o"])
-@pytest.mark.parametrize("i", range(24))
+@pytest.mark.parametrize("i", list(range(24)) + [2299])
 def test_random_shape_parity(i, mode):
     p, init, tag = draw(i)
     f16 = mode.startswith("f16")
