@@ -2150,6 +2150,8 @@ static long long scratch_bound(long long nblk, int H) {
 // The most bytes of stored tiles one call may take (attn_set_scratch_limit).
 static std::atomic<long long> g_scratch_limit{32ll << 30};
 
+long long scratch_limit() { return g_scratch_limit.load(); }
+
 extern "C" attn_status_t attn_set_scratch_limit(size_t bytes, size_t* previous) {
   g_err[0] = 0;
   const long long v = bytes > (size_t)LLONG_MAX ? LLONG_MAX : (long long)bytes;

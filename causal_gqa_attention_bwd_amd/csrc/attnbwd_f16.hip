@@ -49,6 +49,7 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma16(const h8& a, const h8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -159,6 +160,15 @@ struct F16Args {
   const uint32_t* blk_min;             // [ceil(S/32)] min seg per 32-row query block
   const uint32_t* blk_max;             // [ceil(S/32)] max seg per 32-row query block
   const float* LSE2;                   // [S, H] LSE * log2(e) (k_cvt16)
+  const long long* slot_off;           // [ceil(S/32) + 1] first tile slot of each query block
+  // blk_min, blk_max and slot_off as one buffer from blk_min (the step's
+  // metadata is staged with one load): its size and the byte offsets of
+  // blk_max and slot_off in it
+  uint32_t meta_bytes, meta_max, meta_slot;
+  // the stored dS/scale tiles (fp16, 2 KiB per (slot, head): keys as rows,
+  // see ds_tile_row), written by the key-major pass and read by k_dqs16; NULL
+  // when they do not fit the scratch limit (k_q16 then recomputes dS)
+  _Float16* dS;
   int S, Sp, H, KV, d;
   float scale;
   int pair;                            // 1: block p serves tiles p and n-1-p (plain causal)
@@ -169,6 +179,54 @@ struct F16Args {
   int rope_pos;                        // position of row 0 (the page's pos_offset)
   double rope_base;                    // frequency base
 };
+
+// Where lane `lane` of the loading wave takes query block qb's staged
+// metadata from (one 4-byte load per lane into 256 bytes of the stage; lanes
+// 4.. deposit zeros): lane 0 the block's largest document start (0 without a
+// seg), lane 1 its smallest, lanes 2 and 3 its first tile slot (64-bit).
+__device__ __forceinline__ uint32_t meta_off(const F16Args& a, int qb, int lane) {
+  return lane == 0 ? a.meta_max + 4u * (uint32_t)qb
+       : lane == 1 ? 4u * (uint32_t)qb
+       : lane < 4  ? a.meta_slot + 8u * (uint32_t)qb + 4u * (uint32_t)(lane - 2)
+                   : ATTN_BUF_OOB;
+}
+
+// Stored dS/scale tiles.  The tile of (query block qb, key block kb, head h)
+// is tile slot slot_off[qb] + kb - blk_min[qb]/32 (the slots of k_prep: the
+// key blocks from the block's first document start to the diagonal), 2 KiB
+// at ((slot * H) + h) * 2 KiB.  A key-major lane l (key l%32, half hf =
+// l/32) holds dS/scale of queries crow(8s + j, hf), s = 0, 1, j = 0..7, as
+// the two packed operands of its dK product, and writes operand s as the 16
+// bytes at 1024 s + 16 l: each store is 1 KiB of consecutive bytes.  Read as
+// 32 key rows of 32 values, column c = 16 hf + 8 s + j of key row r is the
+// value at 1024 s + 16 (r + 32 hf) + 2 j, and it holds query ds_query(c) of
+// the block.
+__device__ __forceinline__ int ds_query(int c) {
+  return 16 * ((c >> 3) & 1) + 8 * ((c >> 2) & 1) + 4 * (c >> 4) + (c & 3);
+}
+
+// The dS/scale tile of key block kbk, head `head`, for the query block whose
+// staged metadata is at `meta` (see meta_off), or NULL when the key block
+// lies before the block's first document start (the tile has no slot, and
+// its dS is zero).
+__device__ __forceinline__ _Float16* ds_tile(const F16Args& a, const char* meta, int kbk, int head) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(
+                          (int)*reinterpret_cast<const uint32_t*>(meta + 4)) / 32u;
+  if ((uint32_t)kbk < lo) return nullptr;
+  const uint2 sl = *reinterpret_cast<const uint2*>(meta + 8);
+  const long long slot = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)sl.y) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)sl.x));
+  return a.dS + ((size_t)(slot + kbk - (long long)lo) * a.H + head) * 1024;
+}
+
+// Write a tile's two operands held by lane `lane` (see ds_query) to t.
+__device__ __forceinline__ void ds_write(_Float16* t, int lane, const h8& d0, const h8& d1) {
+  const auto r = out_rsrc(t, 2048u);
+  // non-temporal (read once, by another kernel)
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, d0), r, 16u * lane, 0, ATTN_CPOL_NT);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, d1), r, 16u * lane + 1024u, 0,
+                                         ATTN_CPOL_NT);
+}
 
 struct CvtArgs {
   const float *Q, *dO, *K, *V;
@@ -212,6 +270,49 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
   if (which == 0 && threadIdx.x < 32 && r0 + (int)threadIdx.x < a.S) {
     const size_t i = (size_t)(r0 + threadIdx.x) * a.H + head;
     a.LSE2[i] = a.LSE[i] * ATTN_LOG2E;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ += scale * acc for one wave's 32 query rows r0 + rowof(r) (register r of
+// each 32-column output tile o), or with RoPE dQ = R^T (dQ + scale * acc), the
+// pair partner column in lane l ^ 1, through a buffer over the wave's rows:
+// rows past S and columns past head_dim read zero and drop their stores, so
+// every lane reaches the partner exchange.
+// ---------------------------------------------------------------------------
+template <int NO, bool ROPE, class RowOf>
+__device__ __forceinline__ void dq_writeback(const F16Args& a, const f32x16 (&acc)[NO], int h, int r0,
+                                             int hf, int l32, RowOf rowof) {
+  const size_t qstride = (size_t)a.H * a.d;
+  if constexpr (!ROPE) {
+    float* dQh = a.dQ + (size_t)h * a.d;
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      const int col = 32 * o + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = r0 + rowof(r);
+        if (row < a.S && col < a.d) dQh[(size_t)row * qstride + col] += a.scale * acc[o][r];
+      }
+    }
+  } else {
+    const int nrows = max(0, min(32, a.S - r0));
+    const auto rq = out_rsrc(a.dQ + (size_t)h * a.d + (size_t)r0 * qstride,
+                             nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * qstride + a.d) * 4) : 0u);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      const int col = 32 * o + l32;
+      const double fq = rope_freq(col, a.d, a.rope_base);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = rowof(r);
+        const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * qstride + col) * 4)
+                                                       : ATTN_BUF_OOB;
+        const float v = buf_ld(rq, off) + a.scale * acc[o][r];
+        buf_st(rq, off, rope_back(v, __shfl_xor(v, 1), col, (long long)r0 + rr + a.rope_pos, fq));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one output tile at a time
+    }
   }
 }
 
@@ -399,42 +500,162 @@ __global__ __launch_bounds__(256, (QGeom<DP, DONLY>::WAVES_PER_SIMD)) void k_q16
     if constexpr (DONLY) {
       const float Dt = Dacc + __shfl_xor(Dacc, 32);  // the half-waves saw disjoint keys
       if (q_ok && hf == 0) a.D[(size_t)q * H + h] = Dt;
-    } else if constexpr (!ROPE) {
-      float* dQh = a.dQ + (size_t)h * a.d;
-      const size_t qstride = (size_t)H * a.d;
-#pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        const int col = 32 * o + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = i0 + 32 * wave + crow(r, hf);
-          if (row < S && col < a.d) dQh[(size_t)row * qstride + col] += a.scale * acc[o][r];
-        }
-      }
     } else {
-      // dQ = R^T (dQ + scale * acc), the pair partner column in lane l ^ 1,
-      // through a buffer over this wave's rows: rows past S and columns past
-      // head_dim read zero and drop their stores, so every lane reaches the
-      // partner exchange
-      const size_t qstride = (size_t)H * a.d;
-      const int r0 = i0 + 32 * wave, nrows = max(0, min(32, S - r0));
-      const auto rq = out_rsrc(a.dQ + (size_t)h * a.d + (size_t)r0 * qstride,
-                               nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * qstride + a.d) * 4) : 0u);
+      dq_writeback<NO, ROPE>(a, acc, h, i0 + 32 * wave, hf, l32, [&](int r) { return crow(r, hf); });
+    }
+  };
+  // longest rows first; paired: then the mirror tile
+  const int first = qt_hi - (int)(blockIdx.x / H);
+  const int second = mirror_tile(first, qt_hi + 1, a.pair);
+  tile(first);
+  if (second >= 0) {
+    __syncthreads();  // every wave done with the ring and sMin of the first tile
+    tile(second);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_dqs16: dQ from the stored dS/scale tiles (written by the key-major pass),
+// so that dS is not formed a second time.  Query-major, one workgroup per
+// (128-query tile, head), as k_q16; wave w owns query block i0/32 + w.  Per
+// key block of the tile, the K row tile (all four waves load a share) and
+// each wave's own dS tile of that key block stream through an LDS ring of
+// NBUF stages; the wave's product dQ += (dS/scale) K takes both operands from
+// transposing loads: the A operand from the dS tile (keys are its rows, the
+// lane's query its column), the B operand from the K row tile.  The dS
+// tile's columns hold the block's queries in the order ds_query gives, so
+// accumulator row m is query ds_query(m).  One product per visible pair; the
+// dS tiles (2 bytes per visible pair and head) are the kernel's HBM traffic.
+// ---------------------------------------------------------------------------
+template <int DP, bool ROPE>
+struct DqsGeom {
+  using KT = Tile16<32, DP / 8>;     // K row tile of a key block
+  using DT = Tile16<32, 4>;          // one wave's dS tile: 32 keys x 32 queries
+  static constexpr int OFF_DS = KT::BYTES;
+  static constexpr int STAGE = KT::BYTES + 4 * 2048;
+  // two workgroups per CU with a 4-stage ring; one with RoPE above 128
+  // columns (the rotation's registers do not fit two waves per SIMD there).
+  // Measured at S=4096, d=128: three per CU with 3 stages the same, four with
+  // 2 stages and one with 9 slower (0.187, 0.185, 0.203, 0.341 ms): the
+  // kernel wants waves, not a deeper ring
+  static constexpr int WG_PER_CU = ROPE && DP > 128 ? 1 : 2;
+  static constexpr int BUDGET = (WG_PER_CU == 1 ? 150 : 72) * 1024;
+  static constexpr int NBUF = BUDGET / STAGE >= 4 ? 4 : BUDGET / STAGE;
+  static constexpr int LPS = KT::CPW + 2;  // loads per wave per block
+  static_assert(NBUF >= 2, "a stage in flight");
+  static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
+};
+
+// Wait until this wave's loads of the block `ahead` blocks before the last
+// issued one have landed: at most ahead * LPS loads (those of the later
+// blocks) outstanding; ahead is at most MAXA.
+template <int MAXA, int LPS>
+__device__ __forceinline__ void wait_blocks(int ahead) {
+  if constexpr (MAXA <= 0) {
+    wait_vm<0>();
+  } else {
+    if (ahead >= MAXA) wait_vm<MAXA * LPS>();
+    else wait_blocks<MAXA - 1, LPS>(ahead);
+  }
+}
+
+template <int DP, bool ROPE>
+__global__ __launch_bounds__(256, (DqsGeom<DP, ROPE>::WG_PER_CU)) void k_dqs16(F16Args a) {
+  using G = DqsGeom<DP, ROPE>;
+  using KT = typename G::KT;
+  using DT = typename G::DT;
+  constexpr int NO = DP / 32, NBUF = G::NBUF, STAGE = G::STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[NBUF * STAGE];
+  __shared__ uint32_t sMin[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, l32 = lane & 31;
+  const int S = a.S, H = a.H;
+  const int g = H / a.KV;
+  const int nblk = (S + 31) / 32;
+  const int qt_hi = (S - 1) / 128;
+  const uint32_t smem0 = lds_addr(smem);
+  Loader16<32, DP / 8> ldr;
+  ldr.init(DP * 2, wave, lane);
+  // this lane's two chunks of its wave's dS tile: physical chunk p = lane +
+  // 64 i of the 32 x 4 chunk tile takes chunk c = (p % 4) ^ swz(p / 4) of key
+  // row r = p / 4, i.e. columns 8c .. 8c + 7, stored at 1024 (c % 2) + 16 (r
+  // + 32 (c / 2))
+  uint32_t doff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = lane + 64 * i, r = p >> 2, c = (p & 3) ^ swz<4>(r);
+    doff[i] = (uint32_t)(1024 * (c & 1) + 16 * (r + 32 * (c >> 1)));
+  }
+
+  auto tile = [&](const int qt) __attribute__((always_inline)) {
+    const int h = xcd_head((int)(blockIdx.x % H), H), kvh = h / g;
+    const int i0 = qt * 128;
+    const int qb = (i0 >> 5) + wave;
+    const uint32_t lo = qb < nblk ? a.blk_min[qb] : 0xffffffffu;
+    const long long slot0 = qb < nblk ? a.slot_off[qb] : 0;
+    if (lane == 0) sMin[wave] = lo;
+    __syncthreads();
+    const uint32_t lo_all = min(min(sMin[0], sMin[1]), min(sMin[2], sMin[3]));
+    const int kb_last = min(i0 + 127, S - 1) / 32;
+    const int kb_first = (int)min(lo_all / 32u, (uint32_t)kb_last + 1u);
+    const int n = kb_last - kb_first + 1;  // blocks of the tile (0: none)
+    // this wave's key blocks, the slots of its query block (a wave past S
+    // has lo = ~0 and sees none)
+    const int w_lo = (int)min(lo / 32u, 0x7fffffffu);
+    const int w_hi = min(i0 + 32 * wave + 31, S - 1) / 32;
+
+    auto issue = [&](int kb, int buf) {
+      const uint32_t st = smem0 + (uint32_t)(buf * STAGE);
+      ldr.load(buf_rsrc(a.Kh + ((size_t)kvh * a.Sp + (size_t)kb * 32) * DP, 32 * DP * 2), st, wave);
+      // the wave's dS tile (zeros, without a memory access, when the block
+      // has no slot for this wave's queries)
+      const bool vis = kb >= w_lo && kb <= w_hi;
+      const size_t t = vis ? (size_t)(slot0 + kb - w_lo) * H + h : 0;
+      const i32x4 rs = buf_rsrc(a.dS + t * 1024, vis ? 2048u : 0u);
+      const uint32_t dst = st + G::OFF_DS + (uint32_t)wave * 2048u;
+      dma16_nt(rs, doff[0], dst);
+      dma16_nt(rs, doff[1], dst + 1024);
+    };
+
+    f32x16 acc[NO];
+#pragma unroll
+    for (int o = 0; o < NO; ++o) acc[o] = zero16();
+
+    auto compute = [&](int kb, int buf) {
+      if (kb < w_lo || kb > w_hi) return;
+      const char* st = smem + buf * STAGE;
+      const char* dt = st + G::OFF_DS + wave * 2048;
+      // A operands: column l%32 (query ds_query(l%32)) of keys crow(j, hf),
+      // then the same plus 16; the B operands take the same keys of K
+      const h8 a0 = tr_operand<DT>(dt, 4 * hf, 8 + 4 * hf, 0, lane);
+      const h8 a1 = tr_operand<DT>(dt, 16 + 4 * hf, 24 + 4 * hf, 0, lane);
 #pragma unroll
       for (int o = 0; o < NO; ++o) {
-        const int col = 32 * o + l32;
-        const double fq = rope_freq(col, a.d, a.rope_base);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rr = crow(r, hf);
-          const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * qstride + col) * 4)
-                                                         : ATTN_BUF_OOB;
-          const float v = buf_ld(rq, off) + a.scale * acc[o][r];
-          buf_st(rq, off, rope_back(v, __shfl_xor(v, 1), col, (long long)r0 + rr + a.rope_pos, fq));
-        }
-        __builtin_amdgcn_sched_barrier(0);  // one output tile at a time
+        const h8 k0 = tr_operand<KT>(st, 4 * hf, 8 + 4 * hf, 32 * o, lane);
+        const h8 k1 = tr_operand<KT>(st, 16 + 4 * hf, 24 + 4 * hf, 32 * o, lane);
+        acc[o] = mfma16(a0, k0, acc[o]);
+        acc[o] = mfma16(a1, k1, acc[o]);
       }
+    };
+
+    // the ring: blocks i .. i + NBUF - 2 issued ahead of the compute of block i
+#pragma unroll
+    for (int k = 0; k < NBUF - 1; ++k)
+      if (k < n) issue(kb_first + k, k);
+    for (int i = 0; i < n; ++i) {
+      // this wave's loads of block i have landed once at most those of the
+      // later issued blocks are outstanding
+      wait_blocks<NBUF - 2, G::LPS>(min(NBUF - 2, n - 1 - i));
+      // every wave: block i resident and done with block i - 1 (whose buffer
+      // the next issue refills)
+      asm volatile("s_barrier" ::: "memory");
+      if (i + NBUF - 1 < n) issue(kb_first + i + NBUF - 1, (i + NBUF - 1) % NBUF);
+      compute(kb_first + i, i % NBUF);
     }
+    dq_writeback<NO, ROPE>(a, acc, h, i0 + 32 * wave, hf, l32,
+                           [&](int r) { return ds_query(crow(r, hf)); });
   };
   // longest rows first; paired: then the mirror tile
   const int first = qt_hi - (int)(blockIdx.x / H);
@@ -588,12 +809,10 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         dma4(buf_rsrc(a.seg ? (const void*)(a.seg + (size_t)qb * 32) : (const void*)a.LSE,
                       a.seg ? (uint32_t)rows * 4u : 0u),
              rok ? (uint32_t)l32 * 4u : ATTN_BUF_OOB, st + G::OFF_ROW + 512);
-      else dma4(buf_rsrc(a.seg ? (const void*)(a.blk_max + qb) : (const void*)a.LSE,
-                         a.seg ? 4u : 0u),
-                lane == 0 ? 0u : ATTN_BUF_OOB, st + G::OFF_ROW + 768);
+      else dma4(buf_rsrc(a.blk_min, a.meta_bytes), meta_off(a, qb, lane), st + G::OFF_ROW + 768);
     };
 
-    auto compute = [&](int qb, int buf) {
+    auto compute = [&](int qb, int hh, int buf) {
       const int q0 = qb * 32, k0 = j0 + 32 * wave;
       if (k0 > q0 + 31) return;  // every key of the block after every query
       const char* st = smem + buf * STAGE;
@@ -648,6 +867,10 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
         }
       }
       const h8 p0 = pack8(s, 0), p1 = pack8(s, 1), d0 = pack8(dp, 0), d1 = pack8(dp, 1);
+      if (a.dS && cpart == 0) {
+        _Float16* t = ds_tile(a, st + G::OFF_ROW + 768, k0 >> 5, kvh * g + split * gs + hh);
+        if (t) ds_write(t, lane, d0, d1);
+      }
       // B operands from the Q and dO row tiles (transposing loads): the k
       // order of p0 / d0 is queries crow(j, hf), j = 0..7, i.e. rows 4 hf ..
       // 4 hf + 3 then 8 + 4 hf .. ; of p1 / d1 the same plus 16
@@ -701,7 +924,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       // next issue refills)
       asm volatile("s_barrier" ::: "memory");
       if (rq[NBUF - 1] >= 0) issue(rq[NBUF - 1], rh[NBUF - 1], (buf + NBUF - 1) % NBUF);
-      compute(rq[0], buf);
+      compute(rq[0], rh[0], buf);
       // shift the ring
       int nq = rq[NBUF - 1], nh = rh[NBUF - 1];
       next_step(nq, nh);
@@ -831,12 +1054,9 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
     const int key = k0 + l32;  // < Sp: the copies hold zero rows up to Sp
     // role P holds its keys' K rows (B operand of S = Q K^T), role dS their V
     // rows (B operand of dP = dO V^T)
+    // (loaded once the ring's first steps are found, so that they are not
+    // live across that search)
     h8 xreg[NT];
-    const size_t boff = ((size_t)kvh * a.Sp + key) * DP + 8 * hf;
-    const _Float16* xsrc = role == 0 ? a.Kh : a.Vh;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) xreg[t] = *reinterpret_cast<const h8*>(xsrc + boff + 16 * t);
-    wait_vm<0>();
     f32x16 acc[NOW];  // role P: dV; role dS: dK / scale
 #pragma unroll
     for (int o = 0; o < NOW; ++o) {
@@ -888,9 +1108,7 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
         dma4(buf_rsrc(a.seg ? (const void*)(a.seg + (size_t)qb * 32) : (const void*)a.LSE,
                       a.seg ? (uint32_t)rows * 4u : 0u),
              rok ? (uint32_t)l32 * 4u : ATTN_BUF_OOB, st + G::OFF_ROW + 512);
-      else dma4(buf_rsrc(a.seg ? (const void*)(a.blk_max + qb) : (const void*)a.LSE,
-                         a.seg ? 4u : 0u),
-                lane == 0 ? 0u : ATTN_BUF_OOB, st + G::OFF_ROW + 768);
+      else dma4(buf_rsrc(a.blk_min, a.meta_bytes), meta_off(a, qb, lane), st + G::OFF_ROW + 768);
     };
 
     // role P, step (qb, buf): S, P (written to the hand-over slot), dV.  The
@@ -973,18 +1191,19 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
       if (k0 > qb * 32 + 31) return;
       const char* st = smem + buf * STAGE;
       dpc = zero16();
+      // (groups of 4: with 8 the role's registers spill at 128 columns)
 #pragma unroll
-      for (int t0 = 0; t0 < NT; t0 += 8) {
-        h8 dop[8];
+      for (int t0 = 0; t0 < NT; t0 += 4) {
+        h8 dop[4];
 #pragma unroll
-        for (int t = 0; t < 8 && t0 + t < NT; ++t)
+        for (int t = 0; t < 4 && t0 + t < NT; ++t)
           dop[t] = *reinterpret_cast<const h8*>(st + G::OFF_DO + RT::at(l32, 2 * (t0 + t) + hf));
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 8 && t0 + t < NT; ++t) dpc = mfma16(dop[t], xreg[t0 + t], dpc);
+        for (int t = 0; t < 4 && t0 + t < NT; ++t) dpc = mfma16(dop[t], xreg[t0 + t], dpc);
       }
     };
-    auto ds_finish = [&](int qb, int buf, int par) {
+    auto ds_finish = [&](int qb, int hh, int buf, int par) {
       if (k0 > qb * 32 + 31) return;
       const char* st = smem + buf * STAGE;
       h8 qv[NOW][2];
@@ -1020,6 +1239,15 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
         acc[o] = mfma16(d1, qv[o][1], acc[o]);
         asm volatile("" : "+v"(acc[o]));
       }
+      // the tile for the query-major dQ pass (after the products: stored
+      // before them, or through role P, the role's registers spilled or the
+      // hand-over's LDS traffic cost more).  These stores join the wave's
+      // count of memory operations, so the ring's waits for its stage loads,
+      // which count only loads, wait for somewhat more than they need.
+      if (a.dS) {
+        _Float16* t = ds_tile(a, st + G::OFF_ROW + 768, k0 >> 5, kvh * g + split * gs + hh);
+        if (t) ds_write(t, lane, d0, d1);
+      }
     };
 
     // the ring: role P computes step i in stage buf, role dS step i - 1 in
@@ -1037,12 +1265,17 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
         rh[k] = rh[k - 1];
         next_step(rq[k], rh[k]);
       }
+      const size_t boff = ((size_t)kvh * a.Sp + key) * DP + 8 * hf;
+      const _Float16* xsrc = role == 0 ? a.Kh : a.Vh;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xreg[t] = *reinterpret_cast<const h8*>(xsrc + boff + 16 * t);
+      wait_vm<0>();
       if (role == 1) {
 #pragma unroll
         for (int k = 0; k < NBUF - 2; ++k)
           if (rq[k] >= 0) issue(rq[k], rh[k], k);
       }
-      int pq = -1, pbuf = 0, buf = 0, par = 0;
+      int pq = -1, ph = 0, pbuf = 0, buf = 0, par = 0;
       while (rq[0] >= 0 || pq >= 0) {
         if (role == 1) {
           // this wave's loads of step i have landed once at most those of the
@@ -1071,8 +1304,9 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
         asm volatile("s_barrier" ::: "memory");
         if (role == 1 && rq[NBUF - 2] >= 0)
           issue(rq[NBUF - 2], rh[NBUF - 2], (buf + NBUF - 2) % NBUF);
-        work(rq[0], buf, par, pq, pbuf);
+        work(rq[0], buf, par, pq, ph, pbuf);
         pq = rq[0];
+        ph = rh[0];
         pbuf = buf;
         int nq = rq[NBUF - 2], nh = rh[NBUF - 2];
         next_step(nq, nh);
@@ -1088,12 +1322,12 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
       }
     };
     if (role == 0)
-      ring([&](int q, int bf, int pr, int, int) {
+      ring([&](int q, int bf, int pr, int, int, int) {
         if (q >= 0) compute_p(q, bf, pr);
       });
     else
-      ring([&](int q, int bf, int pr, int pq, int pbf) {
-        if (pq >= 0) ds_finish(pq, pbf, pr ^ 1);
+      ring([&](int q, int bf, int pr, int pq, int ph, int pbf) {
+        if (pq >= 0) ds_finish(pq, ph, pbf, pr ^ 1);
         if (q >= 0) ds_start(q, bf);
       });
     __syncthreads();  // every wave done with the ring before it is reused
@@ -1188,11 +1422,16 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   }
   if (rc == ATTN_OK) rc = profile_mark(st);
   if (rc != ATTN_OK) return rc;
-  if (f.rope)
+  // dQ from the stored dS tiles, or with dS formed again from the scores
+  if (f.dS && f.rope)
+    hipLaunchKernelGGL((k_dqs16<DP, true>), dim3(nqt * f.H), dim3(256), 0, st, f);
+  else if (f.dS)
+    hipLaunchKernelGGL((k_dqs16<DP, false>), dim3(nqt * f.H), dim3(256), 0, st, f);
+  else if (f.rope)
     hipLaunchKernelGGL((k_q16<DP, false, true>), dim3(nqt * f.H), dim3(256), 0, st, f);
   else
     hipLaunchKernelGGL((k_q16<DP, false, false>), dim3(nqt * f.H), dim3(256), 0, st, f);
-  rc = hip_check(hipGetLastError(), "launching k_q16");
+  rc = hip_check(hipGetLastError(), f.dS ? "launching k_dqs16" : "launching k_q16");
   if (rc == ATTN_OK) rc = profile_mark(st);
   return rc;
 }
@@ -1249,6 +1488,13 @@ static attn_status_t run_f16(const float* Q, const float* K, const float* V, con
   while (kv_blocks * splits < target && g % (2 * splits) == 0) splits *= 2;
   const size_t off_part = off;
   if (splits > 1) off += align256((size_t)2 * splits * seq_len * n_kv_heads * head_dim * 4);
+  // the dS/scale tiles of every (query block, key block) pair up to the
+  // causal bound (a document mask uses fewer slots), 2 KiB per pair and head,
+  // within the scratch limit; beyond it the query-major pass forms dS again
+  const long long ds_pairs = nblk * (nblk + 1) / 2;
+  const bool store_ds = ds_pairs <= scratch_limit() / (n_heads * 2048ll);
+  const size_t off_ds = off;
+  if (store_ds) off += align256((size_t)ds_pairs * n_heads * 2048);
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipMemPool_t pool;
@@ -1267,6 +1513,11 @@ static attn_status_t run_f16(const float* Q, const float* K, const float* V, con
   f.blk_min = reinterpret_cast<const uint32_t*>(w + off_min);
   f.blk_max = reinterpret_cast<const uint32_t*>(w + off_max);
   f.LSE2 = reinterpret_cast<const float*>(w + off_L2);
+  f.slot_off = reinterpret_cast<const long long*>(w + off_slot);
+  f.meta_bytes = (uint32_t)(off_slot + (size_t)(nblk + 1) * 8 - off_min);
+  f.meta_max = (uint32_t)(off_max - off_min);
+  f.meta_slot = (uint32_t)(off_slot - off_min);
+  f.dS = store_ds ? reinterpret_cast<_Float16*>(w + off_ds) : nullptr;
   f.S = seq_len; f.Sp = (int)Sp; f.H = n_heads; f.KV = n_kv_heads; f.d = head_dim; f.scale = scale;
   f.pair = pair;
   f.splits = splits;

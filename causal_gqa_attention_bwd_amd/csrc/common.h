@@ -55,6 +55,7 @@ __device__ __forceinline__ float rope_back(float mine, float partner, int col, l
 // ---------------------------------------------------------------------------
 #define ATTN_BUF_OOB 0x80000000u        // beyond every buffer range used here
 #define ATTN_BUF_WORD3 0x00020000       // raw buffer, 32-bit data format
+#define ATTN_CPOL_NT 2                  // cache policy of a buffer access: non-temporal
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
@@ -112,6 +113,18 @@ __device__ __forceinline__ void dma4(const i32x4& r, uint32_t voff, uint32_t lds
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
       "buffer_load_dword %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(r)
+      : "memory");
+}
+// dma16 for data read once (non-temporal: the caches need not keep it).
+__device__ __forceinline__ void dma16_nt(const i32x4& r, uint32_t voff, uint32_t lds_byte) {
+  int saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
       : "s"(__builtin_amdgcn_readfirstlane((int)lds_byte)), "v"(voff), "s"(r)
@@ -177,6 +190,8 @@ ATTN_INTERNAL bool misaligned(const void* p);
 ATTN_INTERNAL int padded_dim(int d);
 // The library's stream-ordered memory pool of the current device.
 ATTN_INTERNAL attn_status_t device_pool(hipMemPool_t* out);
+// The most bytes of stored tiles one call may take (attn_set_scratch_limit).
+ATTN_INTERNAL long long scratch_limit();
 // Record one profile event on st when the measurement hooks are on; `first`
 // opens the record of a new call.
 ATTN_INTERNAL attn_status_t profile_mark(hipStream_t st, bool first = false);

@@ -15,6 +15,8 @@ zero in exact arithmetic.
 Covered: the small workloads whole, every padded head-dim class with ragged
 tails and every mask kind (plain causal, documents, arbitrary starts, empty
 rows), with and without the forward output, nonzero initial outputs (+=),
+dQ from the dS tiles the key-major pass stores and, below the scratch limit
+they need, with dS formed again by the query-major pass,
 the paired schedule of plain causal calls against the unpaired one (bit for
 bit), repeatability, and the two large workloads element by element over
 whole tensors in the launch configuration bench.py times.
@@ -91,6 +93,33 @@ def test_f16_edge_parity(case, with_o):
     p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
     check_full(p, "edge f16 " + "S%dH%dKV%dd%d_%s" % case, with_o=with_o, f16=True,
                f16_bound=True)
+
+
+DS_CASES = [(513, 16, 2, 64, "docs"), (320, 8, 1, 128, "arbitrary"), (257, 4, 2, 192, "docs"),
+            (161, 4, 2, 256, "docs"), (300, 2, 1, 240, "empty_rows"), (700, 8, 2, 128, "causal")]
+
+
+def ds_tile_bytes(S, H):
+    # the stored dS/scale tiles of every slot of the causal bound, 2 KiB each
+    nblk = (S + 31) // 32
+    return nblk * (nblk + 1) // 2 * H * 2048
+
+
+@pytest.mark.parametrize("rope", [None, (500.0, 13)], ids=["plain", "rope"])
+@pytest.mark.parametrize("limit", ["exact", "below"])
+@pytest.mark.parametrize("case", DS_CASES, ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
+def test_f16_stored_and_recomputed_ds(case, limit, rope, scratch_limit):
+    # dQ from the dS tiles the key-major pass stored (a scratch limit they
+    # fill exactly), or, one byte below it, with dS formed again by the
+    # query-major pass; both with and without the forward output
+    S, H, KV, d, kind = case
+    rng = np.random.default_rng(9700 + S + d)
+    p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
+    init = [rng.standard_normal(p[k].shape).astype(np.float32) for k in ("Q", "K", "V")]
+    scratch_limit(ds_tile_bytes(S, H) - (limit == "below"))
+    for with_o in (False, True):
+        check_full(p, f"f16 dS {limit} rope={rope} " + "S%dH%dKV%dd%d_%s" % case, init=init,
+                   with_o=with_o, f16=True, rope=rope, f16_bound=True)
 
 
 def test_f16_accumulates():
