@@ -28,7 +28,8 @@ PEAK_FP32_MFMA = 157.3   # TFLOP/s, MI355X dense fp32 matrix
 PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16/bf16 matrix
 PEAK_HBM = 8.0           # TB/s
 CSRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc")
-F16_KERNELS = ("k_cvt16", "k_kv16", "k_q16")
+F16_KERNELS = ("k_cvt16", "k_kv16", "k_q16", "k_dqs16")
+DEFAULT_SCRATCH_LIMIT = 32 << 30  # bytes, the library's default (attn_set_scratch_limit)
 DEC_KERNELS = ("k_dec_dp", "k_dec_kv", "k_dec_dq")
 SHORT_KERNELS = ("k_short", "k_short_rowterm")
 
@@ -175,8 +176,16 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     stored = heads > 0
     dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
     f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + 2 * w.S * w.H * 4
+    # the fp16 path's stored dS/scale tiles (2 KiB per slot of the causal
+    # bound and head), when they fit the scratch limit (never changed here)
+    nblk = (w.S + 31) // 32
+    ds_bytes = nblk * (nblk + 1) // 2 * w.H * 2048
+    ds_stored = ds_bytes <= DEFAULT_SCRATCH_LIMIT
+    if ds_stored:
+        f16_ws += ds_bytes
     if entry.startswith("attn_bwd_f16"):
-        log(f"bench: {entry}, fp16 copies {f16_ws / 2**30:.2f} GiB")
+        log(f"bench: {entry}, workspace {f16_ws / 2**30:.2f} GiB (fp16 copies"
+            + (", stored dS tiles)" if ds_stored else "; dS formed again by the query-major pass)"))
     elif entry != "attn_bwd_short":
         log(f"bench: workspace at most {ws_bytes / 2**30:.2f} GiB (attn_bwd_plan), "
             + (f"stored probability tiles for {heads} heads at a time" if stored
@@ -227,8 +236,9 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     # (the O entry's row-term kernel, k_rowdot, runs before the first pass and
     # is in ms_per_step only)
     # attn_bwd_f16: the fp16 copies plus the row term (S and dP once more when
-    # no forward output is given), k_kv16 (S, dP, P^T.dO, dS^T.Q) and k_q16
-    # (S, dP, dS.K)
+    # no forward output is given), k_kv16 (S, dP, P^T.dO, dS^T.Q, storing dS)
+    # and k_dqs16 (dS.K from the stored tiles), or k_q16 (S, dP, dS.K) when
+    # the tiles do not fit the scratch limit
     # attn_bwd_short: one launch whose key-role workgroups form S, dP, P^T.dO,
     # dS^T.Q and whose query-role workgroups form S, dP, dS.K (14 d per pair
     # and head together), after a row-term launch (S, dP) when no O is given
@@ -237,7 +247,7 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
                   [("k_short_rowterm", ms_q, 4.0), ("k_short", ms_k, 14.0)])
     elif entry.startswith("attn_bwd_f16"):
         passes = [("k_cvt16", ms_q, 0.0 if with_o else 4.0), ("k_kv16", ms_k, 8.0),
-                  ("k_q16", ms_s, 6.0)]
+                  ("k_dqs16", ms_s, 2.0) if ds_stored else ("k_q16", ms_s, 6.0)]
     elif stored:
         # above 128 columns the query-major pass that stores the tiles is k_dqw
         passes = [("k_dqw" if w.d > 128 else "k_dq", ms_q, 4.0), ("k_dkdv_p", ms_k, 4.0),
@@ -261,10 +271,11 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
                 "traffic": read_traffic(kname, w.name), "avg_launch_ms": round(kms, 4),
                 "launches_per_step": launches}
     # general path: attn_bwd_plan's figure, the most a call of this size takes
-    # (with a seg: head-split partial sums); fp16: the operand copies, D and
-    # LSE*log2e, before any partial sums; short: the row term D
+    # (with a seg: head-split partial sums); fp16: the operand copies, D,
+    # LSE*log2e and the stored dS tiles, before any partial sums; short: the
+    # row term D
     ws_key = ("row_term_bytes" if entry == "attn_bwd_short" else
-              "fp16_copies_bytes" if f16 else "workspace_bytes_max")
+              "f16_workspace_bytes" if f16 else "workspace_bytes_max")
     ws_val = (0 if entry == "attn_bwd_short" and with_o else
               w.S * w.H * 4 if entry == "attn_bwd_short" else
               f16_ws if f16 else ws_bytes)

@@ -181,8 +181,14 @@ attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, cons
  * from the shape: one round of resident workgroups for plain causal calls,
  * about 1024 workgroups under a document mask), 2 * splits * seq_len * n_kv_heads *
  * head_dim * 4 bytes of partial dK, dV sums, added in split order (the result
- * does not depend on the schedule).  0.14 GiB at seq_len 4096, 32 heads,
- * 8 KV heads, head_dim 128, plain causal (2 splits).
+ * does not depend on the schedule); and the score-gradient tiles scale*dS in
+ * fp16 that the key-major pass stores for the dQ pass, 2 KiB per (32-query
+ * block, 32-key block, head) slot of the causal bound, nblk * (nblk + 1) / 2
+ * * n_heads * 2048 bytes with nblk = ceil(seq_len / 32), when that fits the
+ * scratch limit (attn_set_scratch_limit); above it the dQ pass forms dS
+ * again from the scores instead (the same sums, three products per visible
+ * pair instead of one).  0.64 GiB at seq_len 4096, 32 heads, 8 KV heads,
+ * head_dim 128, plain causal (2 splits, 0.50 GiB of dS tiles).
  */
 attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
                            const float* dO, const float* LSE, const uint32_t* seg,
@@ -310,9 +316,11 @@ attn_status_t attn_bwd_plan(int seq_len, int n_heads, int n_kv_heads, int head_d
 
 /*
  * attn_set_scratch_limit -- the most bytes of stored probability tiles one
- * attn_bwd, attn_bwd_o or attn_bwd_rope call may take (default 32 GiB, about
- * 11% of the 288 GB of HBM3E); 0 turns the stored tiles off (the key-major
- * pass then recomputes the scores).  Process-wide, read when a call is
+ * attn_bwd, attn_bwd_o or attn_bwd_rope call may take, and of stored fp16
+ * score-gradient tiles one attn_bwd_f16 or attn_bwd_f16_rope call may take
+ * (default 32 GiB, about 11% of the 288 GB of HBM3E); 0 turns the stored
+ * tiles off (the key-major pass then recomputes the scores; the fp16 dQ pass
+ * forms dS again).  Process-wide, read when a call is
  * planned; calls already enqueued keep their workspace.  The previous limit
  * goes to *previous when it is not NULL.  Always ATTN_OK.
  */
