@@ -185,10 +185,12 @@ struct F16Args {
 // 4.. deposit zeros): lane 0 the block's largest document start (0 without a
 // seg), lane 1 its smallest, lanes 2 and 3 its first tile slot (64-bit).
 __device__ __forceinline__ uint32_t meta_off(const F16Args& a, int qb, int lane) {
-  return lane == 0 ? a.meta_max + 4u * (uint32_t)qb
-       : lane == 1 ? 4u * (uint32_t)qb
-       : lane < 4  ? a.meta_slot + 8u * (uint32_t)qb + 4u * (uint32_t)(lane - 2)
-                   : ATTN_BUF_OOB;
+  // every candidate formed, then selected (no divergent branch per lane)
+  const uint32_t q4 = 4u * (uint32_t)qb;
+  const uint32_t o_max = a.meta_max + q4, o_slot = a.meta_slot + 2u * q4 + 4u * (uint32_t)(lane & 1);
+  uint32_t off = lane < 4 ? o_slot : ATTN_BUF_OOB;
+  off = lane == 1 ? q4 : off;
+  return lane == 0 ? o_max : off;
 }
 
 // Stored dS/scale tiles.  The tile of (query block qb, key block kb, head h)
