@@ -51,6 +51,17 @@ typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// out_rsrc for an address and size that every lane of the wave holds, taken
+// from lane 0: the compiler then keeps the descriptor in scalar registers
+// (else, not proving the values uniform, it wraps every access in a loop
+// over the distinct descriptors of the wave and waits for each access)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t wave_rsrc(const float* p, uint32_t bytes) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return out_rsrc((void*)(((uint64_t)hi << 32) | lo), (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
+}
+
 __device__ __forceinline__ f32x16 mfma16(const h8& a, const h8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
@@ -282,11 +293,13 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
 // rows past S and columns past head_dim read zero and drop their stores, so
 // every lane reaches the partner exchange.
 // ---------------------------------------------------------------------------
-template <int NO, bool ROPE, class RowOf>
+template <int NO, bool ROPE, bool BUF, class RowOf>
 __device__ __forceinline__ void dq_writeback(const F16Args& a, const f32x16 (&acc)[NO], int h, int r0,
                                              int hf, int l32, RowOf rowof) {
   const size_t qstride = (size_t)a.H * a.d;
-  if constexpr (!ROPE) {
+  if constexpr (!ROPE && !BUF) {
+    // (a load, add and store per element behind a branch: the k_q16 form,
+    // whose registers do not hold the buffer form's offsets)
     float* dQh = a.dQ + (size_t)h * a.d;
 #pragma unroll
     for (int o = 0; o < NO; ++o) {
@@ -295,6 +308,30 @@ __device__ __forceinline__ void dq_writeback(const F16Args& a, const f32x16 (&ac
       for (int r = 0; r < 16; ++r) {
         const int row = r0 + rowof(r);
         if (row < a.S && col < a.d) dQh[(size_t)row * qstride + col] += a.scale * acc[o][r];
+      }
+    }
+  } else if constexpr (!ROPE) {
+    // through a buffer over the wave's rows, no branch per element: every
+    // load of an output tile is issued before its adds and stores
+    const int nrows = max(0, min(32, a.S - r0));
+    const auto rq = out_rsrc(a.dQ + (size_t)h * a.d + (size_t)r0 * qstride,
+                             nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * qstride + a.d) * 4) : 0u);
+#pragma unroll
+    for (int o = 0; o < NO; ++o) {
+      const int col = 32 * o + l32;
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 8) {
+        uint32_t off[8];
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int rr = rowof(r0 + r);
+          off[r] = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * qstride + col) * 4) : ATTN_BUF_OOB;
+          v[r] = buf_ld(rq, off[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) buf_st(rq, off[r], v[r] + a.scale * acc[o][r0 + r]);
+        __builtin_amdgcn_sched_barrier(0);  // eight rows at a time
       }
     }
   } else {
@@ -503,7 +540,7 @@ __global__ __launch_bounds__(256, (QGeom<DP, DONLY>::WAVES_PER_SIMD)) void k_q16
       const float Dt = Dacc + __shfl_xor(Dacc, 32);  // the half-waves saw disjoint keys
       if (q_ok && hf == 0) a.D[(size_t)q * H + h] = Dt;
     } else {
-      dq_writeback<NO, ROPE>(a, acc, h, i0 + 32 * wave, hf, l32, [&](int r) { return crow(r, hf); });
+      dq_writeback<NO, ROPE, false>(a, acc, h, i0 + 32 * wave, hf, l32, [&](int r) { return crow(r, hf); });
     }
   };
   // longest rows first; paired: then the mirror tile
@@ -544,6 +581,9 @@ struct DqsGeom {
   static constexpr int BUDGET = (WG_PER_CU == 1 ? 150 : 72) * 1024;
   static constexpr int NBUF = BUDGET / STAGE >= 4 ? 4 : BUDGET / STAGE;
   static constexpr int LPS = KT::CPW + 2;  // loads per wave per block
+  // output tiles whose K operands are read ahead of their products at once
+  // (above 128 columns the accumulators leave room for two)
+  static constexpr int GO = DP > 128 ? 2 : 4;
   static_assert(NBUF >= 2, "a stage in flight");
   static_assert((NBUF - 2) * LPS < 64, "loads in flight fit vmcnt");
 };
@@ -631,14 +671,23 @@ __global__ __launch_bounds__(256, (DqsGeom<DP, ROPE>::WG_PER_CU)) void k_dqs16(F
       const char* dt = st + G::OFF_DS + wave * 2048;
       // A operands: column l%32 (query ds_query(l%32)) of keys crow(j, hf),
       // then the same plus 16; the B operands take the same keys of K
+      // every operand read before the products (in groups of GO output
+      // tiles), so that one wait covers the reads' latency
       const h8 a0 = tr_operand<DT>(dt, 4 * hf, 8 + 4 * hf, 0, lane);
       const h8 a1 = tr_operand<DT>(dt, 16 + 4 * hf, 24 + 4 * hf, 0, lane);
 #pragma unroll
-      for (int o = 0; o < NO; ++o) {
-        const h8 k0 = tr_operand<KT>(st, 4 * hf, 8 + 4 * hf, 32 * o, lane);
-        const h8 k1 = tr_operand<KT>(st, 16 + 4 * hf, 24 + 4 * hf, 32 * o, lane);
-        acc[o] = mfma16(a0, k0, acc[o]);
-        acc[o] = mfma16(a1, k1, acc[o]);
+      for (int o0 = 0; o0 < NO; o0 += G::GO) {
+        h8 kv[G::GO][2];
+#pragma unroll
+        for (int o = o0; o < o0 + G::GO && o < NO; ++o) {
+          kv[o - o0][0] = tr_operand<KT>(st, 4 * hf, 8 + 4 * hf, 32 * o, lane);
+          kv[o - o0][1] = tr_operand<KT>(st, 16 + 4 * hf, 24 + 4 * hf, 32 * o, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int o = o0; o < o0 + G::GO && o < NO; ++o) acc[o] = mfma16(a0, kv[o - o0][0], acc[o]);
+#pragma unroll
+        for (int o = o0; o < o0 + G::GO && o < NO; ++o) acc[o] = mfma16(a1, kv[o - o0][1], acc[o]);
       }
     };
 
@@ -656,8 +705,10 @@ __global__ __launch_bounds__(256, (DqsGeom<DP, ROPE>::WG_PER_CU)) void k_dqs16(F
       if (i + NBUF - 1 < n) issue(kb_first + i + NBUF - 1, (i + NBUF - 1) % NBUF);
       compute(kb_first + i, i % NBUF);
     }
-    dq_writeback<NO, ROPE>(a, acc, h, i0 + 32 * wave, hf, l32,
-                           [&](int r) { return ds_query(crow(r, hf)); });
+    // (above 128 columns the buffer form's offsets do not fit beside the
+    // accumulators)
+    dq_writeback<NO, ROPE, (DP <= 128)>(a, acc, h, i0 + 32 * wave, hf, l32,
+                                        [&](int r) { return ds_query(crow(r, hf)); });
   };
   // longest rows first; paired: then the mirror tile
   const int first = qt_hi - (int)(blockIdx.x / H);
@@ -952,29 +1003,43 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
     const uint32_t rbytes =
         nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * kstride + a.d) * 4) : 0u;
     const size_t base = (size_t)kvh * a.d + (size_t)r0 * kstride;
-    const auto rK = out_rsrc((a.splits == 1 ? a.dK : a.part + (size_t)(2 * split) * slice) + base,
-                             rbytes);
-    const auto rV = out_rsrc((a.splits == 1 ? a.dV : a.part + (size_t)(2 * split + 1) * slice) + base,
-                             rbytes);
+    const auto rK = wave_rsrc((a.splits == 1 ? a.dK : a.part + (size_t)(2 * split) * slice) + base,
+                              rbytes);
+    const auto rV = wave_rsrc((a.splits == 1 ? a.dV : a.part + (size_t)(2 * split + 1) * slice) + base,
+                              rbytes);
+    const bool add = a.splits == 1;
+    // eight rows at a time: their loads, then their adds and stores
 #pragma unroll
     for (int o = 0; o < NOW; ++o) {
       const int col = cpart * G::DW + 32 * o + l32;
       const double fq = ROPE ? rope_freq(col, a.d, a.rope_base) : 0.0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = crow(r, hf);
-        const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * kstride + col) * 4)
-                                                       : ATTN_BUF_OOB;
-        if (a.splits == 1) {
-          float vk = buf_ld(rK, off) + a.scale * accK[o][r];
-          if constexpr (ROPE)
-            vk = rope_back(vk, __shfl_xor(vk, 1), col, (long long)r0 + rr + a.rope_pos, fq);
-          buf_st(rK, off, vk);
-          buf_st(rV, off, buf_ld(rV, off) + accV[o][r]);
-        } else {
-          buf_st(rK, off, a.scale * accK[o][r]);
-          buf_st(rV, off, accV[o][r]);
+      for (int q0 = 0; q0 < 16; q0 += 8) {
+        uint32_t off[8];
+        float vk[8], vv[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int rr = crow(q0 + r, hf);
+          off[r] = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * kstride + col) * 4) : ATTN_BUF_OOB;
+          vk[r] = add ? buf_ld(rK, off[r]) : 0.f;
+          vv[r] = add ? buf_ld(rV, off[r]) : 0.f;
         }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          vk[r] += a.scale * accK[o][q0 + r];
+          vv[r] += accV[o][q0 + r];
+          if constexpr (ROPE) {
+            if (add)
+              vk[r] = rope_back(vk[r], __shfl_xor(vk[r], 1), col,
+                                (long long)r0 + crow(q0 + r, hf) + a.rope_pos, fq);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          buf_st(rK, off[r], vk[r]);
+          buf_st(rV, off[r], vv[r]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
@@ -1344,12 +1409,46 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
         nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * kstride + a.d) * 4) : 0u;
     const size_t base = (size_t)kvh * a.d + (size_t)k0 * kstride;
     float* const whole = role == 0 ? a.dV : a.dK;
-    const auto rO = out_rsrc((a.splits == 1 ? whole : a.part + (size_t)(2 * split + (role == 0)) * slice) +
-                                 base,
-                             rbytes);
+    const auto rO = wave_rsrc((a.splits == 1 ? whole : a.part + (size_t)(2 * split + (role == 0)) * slice) +
+                                  base,
+                              rbytes);
     const float f = role == 0 ? 1.f : a.scale;
+    const bool add = a.splits == 1;
+    // eight rows at a time: their loads, then their adds and stores.  At
+    // 128 columns the registers hold only one element at a time (the
+    // batched form spilled inside the step loop): a load, add and store each
 #pragma unroll
-    for (int o = 0; o < NOW; ++o) {
+    for (int o = 0; o < NOW && DP < 128; ++o) {
+      const int col = cpart * G::DW + 32 * o + l32;
+      const double fq = ROPE ? rope_freq(col, a.d, a.rope_base) : 0.0;
+#pragma unroll
+      for (int r0 = 0; r0 < 16; r0 += 8) {
+        uint32_t off[8];
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int rr = crow(r0 + r, hf);
+          off[r] = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * kstride + col) * 4) : ATTN_BUF_OOB;
+          v[r] = add ? buf_ld(rO, off[r]) : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          v[r] += f * acc[o][r0 + r];
+          if constexpr (ROPE) {
+            if (add) {
+              const float partner = __shfl_xor(v[r], 1);
+              if (role == 1)
+                v[r] = rope_back(v[r], partner, col, (long long)k0 + crow(r0 + r, hf) + a.rope_pos, fq);
+            }
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) buf_st(rO, off[r], v[r]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int o = 0; o < NOW && DP == 128; ++o) {
       const int col = cpart * G::DW + 32 * o + l32;
       const double fq = ROPE ? rope_freq(col, a.d, a.rope_base) : 0.0;
 #pragma unroll
@@ -1357,7 +1456,7 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
         const int rr = crow(r, hf);
         const uint32_t off = (rr < nrows && col < a.d) ? (uint32_t)(((size_t)rr * kstride + col) * 4)
                                                        : ATTN_BUF_OOB;
-        if (a.splits == 1) {
+        if (add) {
           float v = buf_ld(rO, off) + f * acc[o][r];
           if constexpr (ROPE) {
             const float partner = __shfl_xor(v, 1);
