@@ -1593,16 +1593,23 @@ static attn_status_t run_f16(const float* Q, const float* K, const float* V, con
   // causal bound (a document mask uses fewer slots), 2 KiB per pair and head,
   // within the scratch limit; beyond it the query-major pass forms dS again
   const long long ds_pairs = nblk * (nblk + 1) / 2;
-  const bool store_ds = ds_pairs <= scratch_limit() / (n_heads * 2048ll);
+  bool store_ds = ds_pairs <= scratch_limit() / (n_heads * 2048ll);
   const size_t off_ds = off;
-  if (store_ds) off += align256((size_t)ds_pairs * n_heads * 2048);
+  const size_t ds_bytes = store_ds ? align256((size_t)ds_pairs * n_heads * 2048) : 0;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipMemPool_t pool;
   rc = device_pool(&pool);
   if (rc != ATTN_OK) return rc;
   void* ws = nullptr;
-  rc = hip_check(hipMallocFromPoolAsync(&ws, off, pool, st), "hipMallocFromPoolAsync(workspace)");
+  hipError_t e = hipMallocFromPoolAsync(&ws, off + ds_bytes, pool, st);
+  if (e == hipErrorOutOfMemory && store_ds) {
+    // no room for the dS tiles: the query-major pass forms dS again instead
+    (void)hipGetLastError();  // the failed allocation is not a launch error
+    store_ds = false;
+    e = hipMallocFromPoolAsync(&ws, off, pool, st);
+  }
+  rc = hip_check(e, "hipMallocFromPoolAsync(workspace)");
   if (rc != ATTN_OK) return rc;
   char* w = static_cast<char*>(ws);
   auto half_at = [&](int i) { return reinterpret_cast<_Float16*>(w + off_x[i]); };

@@ -185,9 +185,9 @@ attn_status_t attn_bwd_rope(const float* Q, const float* K, const float* V, cons
  * fp16 that the key-major pass stores for the dQ pass, 2 KiB per (32-query
  * block, 32-key block, head) slot of the causal bound, nblk * (nblk + 1) / 2
  * * n_heads * 2048 bytes with nblk = ceil(seq_len / 32), when that fits the
- * scratch limit (attn_set_scratch_limit); above it the dQ pass forms dS
- * again from the scores instead (the same sums, three products per visible
- * pair instead of one).  0.64 GiB at seq_len 4096, 32 heads, 8 KV heads,
+ * scratch limit (attn_set_scratch_limit) and the pool can supply it; else
+ * the dQ pass forms dS again from the scores instead (the same sums, three
+ * products per visible pair instead of one).  0.64 GiB at seq_len 4096, 32 heads, 8 KV heads,
  * head_dim 128, plain causal (2 splits, 0.50 GiB of dS tiles).
  */
 attn_status_t attn_bwd_f16(const float* Q, const float* K, const float* V, const float* O,
