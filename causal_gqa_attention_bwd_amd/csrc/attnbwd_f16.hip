@@ -9,7 +9,8 @@
 // the same sums, at 16 times the fp32 matrix rate of the hardware.
 //
 // Per call:
-//   k_prep    per 32-row query block seg min / max (shared with attn_bwd).
+//   k_prep    per 32-row query block seg min / max and tile slots (shared
+//             with attn_bwd).
 //   k_cvt16   fp16 copies of Q, dO, K, V as head-major row tiles [head][Sp][DP]
 //             (Sp = S rounded up to 128, DP = head_dim rounded up to a tile
 //             width; padding is zero).
@@ -18,11 +19,14 @@
 //   k_kv16    key-major, one workgroup per (128-key tile, KV head, head
 //             split, column part), owns its dK / dV rows and sums its heads:
 //             S = Q K^T, dP = dO V^T, P, dS, dV += P^T dO, dK += dS^T Q.  4
-//             products per visible pair.  k_kv16r: the same with each key
-//             block's work split over two waves by role (up to 128 columns).
-//   k_q16     query-major, one workgroup per (128-query tile, head): S^T, dP^T,
-//             dS, dQ += dS K.  3 products per visible pair.
-// Executed products per visible pair: 7 with the forward output, 9 without
+//             products per visible pair; stores each dS/scale tile in fp16
+//             for the dQ pass.  k_kv16r: the same with each key block's work
+//             split over two waves by role (up to 128 columns).
+//   k_dqs16   query-major, one workgroup per (128-query tile, head): dQ +=
+//             (dS/scale) K from the stored tiles.  1 product per visible pair.
+//   k_q16     (only when the dS tiles do not fit the scratch limit or the
+//             pool) the same dQ, forming S^T, dP^T and dS again: 3 products.
+// Executed products per visible pair: 5 with the forward output, 7 without
 // (the page's method credits 5).
 //
 // MFMA v_mfma_f32_32x32x16_f16 (C[32x32] += A[32x16] B[16x32]), lane layout
@@ -748,7 +752,7 @@ struct KvGeom {
   static constexpr int NOW = DW / 32;          // 32-column output tiles per part
   using RT = Tile16<32, DP / 8>;
   static constexpr int OFF_DO = RT::BYTES;
-  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE*log2e, D, seg, max seg (256 B each)
+  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE*log2e, D, seg, block metadata (256 B each)
   static constexpr int STAGE = OFF_ROW + 4 * 256;
   static constexpr int NBUF = 4 * STAGE <= 150 * 1024 ? 4 : 3 * STAGE <= 150 * 1024 ? 3 : 2;
   static constexpr int LPS = 2 * RT::CPW + 1;  // loads per wave per step
@@ -851,7 +855,7 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       ldr.load(buf_rsrc(a.Qh + roff, 32 * DP * 2), st, wave);
       ldr.load(buf_rsrc(a.dOh + roff, 32 * DP * 2), st + G::OFF_DO, wave);
       // LSE, D and seg of the block's rows (lanes 0..31; the rest deposit
-      // zeros), and the block's largest seg (wave 3, lane 0; 0 without a seg)
+      // zeros), and the block's metadata (wave 3: meta_off)
       const int rows = min(32, S - qb * 32);
       const bool rok = hf == 0 && l32 < rows;
       const uint32_t roff4 = rok ? (uint32_t)(l32 * H + head) * 4u : ATTN_BUF_OOB;
@@ -1071,7 +1075,7 @@ struct KvrGeom {
   static constexpr int NOW = DW / 32;
   using RT = Tile16<32, DP / 8>;
   static constexpr int OFF_DO = RT::BYTES;
-  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE*log2e, D, seg, max seg (256 B each)
+  static constexpr int OFF_ROW = 2 * RT::BYTES;  // LSE*log2e, D, seg, block metadata (256 B each)
   static constexpr int STAGE = OFF_ROW + 4 * 256;
   static constexpr int PBYTES = 2 * 4 * 2048;    // P hand-over: [step parity][key block]
   static constexpr int NBUF = (150 * 1024 - PBYTES) / STAGE >= 6 ? 6 : (150 * 1024 - PBYTES) / STAGE;
