@@ -29,7 +29,6 @@ PEAK_FP16_MFMA = 2516.6  # TFLOP/s, MI355X dense fp16/bf16 matrix
 PEAK_HBM = 8.0           # TB/s
 CSRC = os.path.join(ROOT, "causal_gqa_attention_bwd_amd", "csrc")
 F16_KERNELS = ("k_cvt16", "k_kv16", "k_q16", "k_dqs16")
-DEFAULT_SCRATCH_LIMIT = 32 << 30  # bytes, the library's default (attn_set_scratch_limit)
 DEC_KERNELS = ("k_dec_dp", "k_dec_kv", "k_dec_dq")
 SHORT_KERNELS = ("k_short", "k_short_rowterm")
 
@@ -177,10 +176,13 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     dpad = next(p for p in (32, 64, 96, 128, 192, 256) if p >= w.d)
     f16_ws = (2 * w.H + 2 * w.KV) * ((w.S + 127) // 128 * 128) * dpad * 2 + 2 * w.S * w.H * 4
     # the fp16 path's stored dS/scale tiles (2 KiB per slot of the causal
-    # bound and head), when they fit the scratch limit (never changed here)
+    # bound and head), when they fit the library's current scratch limit
+    # (read back by setting it to itself)
     nblk = (w.S + 31) // 32
     ds_bytes = nblk * (nblk + 1) // 2 * w.H * 2048
-    ds_stored = ds_bytes <= DEFAULT_SCRATCH_LIMIT
+    limit = binding.set_scratch_limit(0)
+    binding.set_scratch_limit(limit)
+    ds_stored = ds_bytes <= limit
     if ds_stored:
         f16_ws += ds_bytes
     if entry.startswith("attn_bwd_f16"):
@@ -268,7 +270,7 @@ def time_entry(wid, entry, with_o, steps, warmup, calib_copy_mb):
     peak = PEAK_FP16_MFMA if entry.startswith("attn_bwd_f16") else PEAK_FP32_MFMA
     roofline = {"bound": "mfma", "kernel": kname, "achieved": round(kach, 3),
                 "peak": peak, "unit": "TFLOP/s", "frac": round(kach / peak, 4),
-                "traffic": read_traffic(kname, w.name), "avg_launch_ms": round(kms, 4),
+                "traffic": (None if f16 and not ds_stored else read_traffic(kname, w.name)), "avg_launch_ms": round(kms, 4),
                 "launches_per_step": launches}
     # general path: attn_bwd_plan's figure, the most a call of this size takes
     # (with a seg: head-split partial sums); fp16: the operand copies, D,
