@@ -84,7 +84,7 @@ def check_assembly(paths):
     if bad:
         text = "\n".join(f"  {f}: {fn} line {line}: {ins[:3]}" for f, fn, line, ins in bad)
         raise RuntimeError("vector instructions between a join label and the restore of the "
-                           "execution mask (a miscompile this build refuses):\n" + text)
+                           "execution mask (a miscompile the library build refuses):\n" + text)
 
 
 if __name__ == "__main__":
