@@ -223,16 +223,14 @@ __device__ __forceinline__ int ds_query(int c) {
 }
 
 // The dS/scale tile of key block kbk, head `head`, for the query block whose
-// staged metadata is at `meta` (see meta_off), or NULL when the key block
-// lies before the block's first document start (the tile has no slot, and
-// its dS is zero).
-__device__ __forceinline__ _Float16* ds_tile(const F16Args& a, const char* meta, int kbk, int head) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(
-                          (int)*reinterpret_cast<const uint32_t*>(meta + 4)) / 32u;
+// staged metadata `m` is (the 16 bytes meta_off places: largest and smallest
+// document start, first slot), or NULL when the key block lies before the
+// block's first document start (the tile has no slot, and its dS is zero).
+__device__ __forceinline__ _Float16* ds_tile(const F16Args& a, const uint4& m, int kbk, int head) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)m.y) / 32u;
   if ((uint32_t)kbk < lo) return nullptr;
-  const uint2 sl = *reinterpret_cast<const uint2*>(meta + 8);
-  const long long slot = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)sl.y) << 32) |
-                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)sl.x));
+  const long long slot = (long long)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)m.w) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)m.z));
   return a.dS + ((size_t)(slot + kbk - (long long)lo) * a.H + head) * 1024;
 }
 
@@ -925,7 +923,8 @@ __global__ __launch_bounds__(256, 1) void k_kv16(F16Args a) {
       }
       const h8 p0 = pack8(s, 0), p1 = pack8(s, 1), d0 = pack8(dp, 0), d1 = pack8(dp, 1);
       if (a.dS && cpart == 0) {
-        _Float16* t = ds_tile(a, st + G::OFF_ROW + 768, k0 >> 5, kvh * g + split * gs + hh);
+        _Float16* t = ds_tile(a, *reinterpret_cast<const uint4*>(st + G::OFF_ROW + 768), k0 >> 5,
+                              kvh * g + split * gs + hh);
         if (t) ds_write(t, lane, d0, d1);
       }
       // B operands from the Q and dO row tiles (transposing loads): the k
@@ -1286,6 +1285,8 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
       const char* pb = pbuf0 + (par * 4 + kb) * 2048;
       const h8 p0 = *reinterpret_cast<const h8*>(pb + 16 * lane);
       const h8 p1 = *reinterpret_cast<const h8*>(pb + 1024 + 16 * lane);
+      // the block's metadata for the dS store, read with the step's other LDS reads
+      const uint4 meta = *reinterpret_cast<const uint4*>(st + G::OFF_ROW + 768);
       float dv[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
@@ -1316,7 +1317,7 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
       // count of memory operations, so the ring's waits for its stage loads,
       // which count only loads, wait for somewhat more than they need.
       if (a.dS) {
-        _Float16* t = ds_tile(a, st + G::OFF_ROW + 768, k0 >> 5, kvh * g + split * gs + hh);
+        _Float16* t = ds_tile(a, meta, k0 >> 5, kvh * g + split * gs + hh);
         if (t) ds_write(t, lane, d0, d1);
       }
     };
@@ -1350,7 +1351,9 @@ __global__ __launch_bounds__(512, 1) void k_kv16r(F16Args a) {
       while (rq[0] >= 0 || pq >= 0) {
         if (role == 1) {
           // this wave's loads of step i have landed once at most those of the
-          // later issued steps (i + 1 .. i + NBUF - 3) are outstanding
+          // later issued steps (i + 1 .. i + NBUF - 3) are outstanding (the
+          // dS stores issued since count too, so these waits cover a little
+          // more than step i: counting the stores exactly gained nothing)
           int ahead = 0;
 #pragma unroll
           for (int k = 1; k < NBUF - 2; ++k) ahead += rq[k] >= 0;
