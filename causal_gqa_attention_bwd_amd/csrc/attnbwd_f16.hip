@@ -707,10 +707,55 @@ __global__ __launch_bounds__(256, (DqsGeom<DP, ROPE>::WG_PER_CU)) void k_dqs16(F
       if (i + NBUF - 1 < n) issue(kb_first + i + NBUF - 1, (i + NBUF - 1) % NBUF);
       compute(kb_first + i, i % NBUF);
     }
-    // (above 128 columns the buffer form's offsets do not fit beside the
-    // accumulators)
-    dq_writeback<NO, ROPE, (DP <= 128)>(a, acc, h, i0 + 32 * wave, hf, l32,
-                                        [&](int r) { return ds_query(crow(r, hf)); });
+    if constexpr (DP > 128 && !ROPE) {
+      // above 128 columns the buffer form's offsets do not fit beside the
+      // accumulators: the sums go through LDS (free once every wave is done
+      // with the ring), half the columns at a time, each wave into its own
+      // 32-row region; then each lane adds whole 16-byte row chunks into dQ,
+      // four chunks' loads before their stores
+      constexpr int HALF = DP / 2;      // columns per half
+      constexpr int LW = HALF + 4;      // floats per staged row: the half and 4 of padding
+      constexpr int NCL = HALF / 4;     // 16-byte chunks per staged row
+      constexpr int NPL = 32 * NCL / 64;  // chunks per lane
+      static_assert(4 * 32 * LW * 4 <= NBUF * STAGE, "the staging regions fit the ring");
+      static_assert(NPL % 4 == 0, "whole batches of four chunks");
+      __syncthreads();
+      float* const stg = reinterpret_cast<float*>(smem) + wave * 32 * LW;
+      const size_t qstride = (size_t)H * a.d;
+      const int r0 = i0 + 32 * wave, nrows = max(0, min(32, S - r0));
+      const auto rq = out_rsrc(a.dQ + (size_t)h * a.d + (size_t)r0 * qstride,
+                               nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * qstride + a.d) * 4) : 0u);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int oo = 0; oo < NO / 2; ++oo)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            stg[ds_query(crow(r, hf)) * LW + 32 * oo + l32] = a.scale * acc[half * (NO / 2) + oo][r];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i0c = 0; i0c < NPL; i0c += 4) {
+          uint32_t off[4];
+          f32x4 v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = lane + 64 * (i0c + i), row = c / NCL, col = HALF * half + 4 * (c % NCL);
+            off[i] = (row < nrows && col < a.d) ? (uint32_t)(((size_t)row * qstride + col) * 4) : ATTN_BUF_OOB;
+            v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off[i], 0, 0));
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = lane + 64 * (i0c + i);
+            v[i] += *reinterpret_cast<const f32x4*>(stg + (c / NCL) * LW + 4 * (c % NCL));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[i]), rq, off[i], 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      dq_writeback<NO, ROPE, true>(a, acc, h, i0 + 32 * wave, hf, l32,
+                                   [&](int r) { return ds_query(crow(r, hf)); });
+    }
   };
   // longest rows first; paired: then the mirror tile
   const int first = qt_hi - (int)(blockIdx.x / H);
