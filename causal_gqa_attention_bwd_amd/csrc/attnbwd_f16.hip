@@ -288,6 +288,15 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
   }
 }
 
+// Column pair (2p, 2p + 1) = (x0, x1) of a row at position pos turned back by
+// the RoPE rotation, both columns from one sincos: the arithmetic of
+// rope_back for each column.
+__device__ __forceinline__ f32x2 rope_back_pair(float x0, float x1, long long pos, double freq) {
+  double sn, cs;
+  sincos((double)pos * freq, &sn, &cs);
+  return f32x2{(float)((double)x0 * cs + (double)x1 * sn), (float)(-(double)x0 * sn + (double)x1 * cs)};
+}
+
 // ---------------------------------------------------------------------------
 // dQ += scale * acc for one wave's 32 query rows r0 + rowof(r) (register r of
 // each 32-column output tile o), or with RoPE dQ = R^T (dQ + scale * acc), the
@@ -707,18 +716,22 @@ __global__ __launch_bounds__(256, (DqsGeom<DP, ROPE>::WG_PER_CU)) void k_dqs16(F
       if (i + NBUF - 1 < n) issue(kb_first + i + NBUF - 1, (i + NBUF - 1) % NBUF);
       compute(kb_first + i, i % NBUF);
     }
-    if constexpr (DP > 128 && !ROPE) {
-      // above 128 columns the buffer form's offsets do not fit beside the
-      // accumulators: the sums go through LDS (free once every wave is done
-      // with the ring), half the columns at a time, each wave into its own
-      // 32-row region; then each lane adds whole 16-byte row chunks into dQ,
-      // four chunks' loads before their stores
-      constexpr int HALF = DP / 2;      // columns per half
-      constexpr int LW = HALF + 4;      // floats per staged row: the half and 4 of padding
-      constexpr int NCL = HALF / 4;     // 16-byte chunks per staged row
+    if constexpr (DP > 128 || (ROPE && NO % 2 == 0)) {
+      // through LDS (free once every wave is done with the ring): the sums,
+      // half the columns (an even number of output tiles: NO / 2 of them) at
+      // a time, each wave into its own 32-row region;
+      // then each lane adds whole 16-byte row chunks into dQ, a few chunks'
+      // loads before their stores (above 128 columns the buffer form's
+      // offsets do not fit beside the accumulators).  With RoPE each chunk
+      // holds two whole column pairs, which it turns back before the store.
+      constexpr int HALF = DP / 2;        // columns per half
+      constexpr int LW = HALF + 4;        // floats per staged row: the half and 4 of padding
+      constexpr int NCL = HALF / 4;       // 16-byte chunks per staged row
       constexpr int NPL = 32 * NCL / 64;  // chunks per lane
+      constexpr int BT = NPL % 4 == 0 ? 4 : 2;  // chunks per batch
       static_assert(4 * 32 * LW * 4 <= NBUF * STAGE, "the staging regions fit the ring");
-      static_assert(NPL % 4 == 0, "whole batches of four chunks");
+      static_assert(NPL % BT == 0, "whole batches");
+      static_assert(NO % 2 == 0, "each half is NO / 2 whole output tiles");
       __syncthreads();
       float* const stg = reinterpret_cast<float*>(smem) + wave * 32 * LW;
       const size_t qstride = (size_t)H * a.d;
@@ -734,19 +747,25 @@ __global__ __launch_bounds__(256, (DqsGeom<DP, ROPE>::WG_PER_CU)) void k_dqs16(F
             stg[ds_query(crow(r, hf)) * LW + 32 * oo + l32] = a.scale * acc[half * (NO / 2) + oo][r];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i0c = 0; i0c < NPL; i0c += 4) {
-          uint32_t off[4];
-          f32x4 v[4];
+        for (int i0c = 0; i0c < NPL; i0c += BT) {
+          uint32_t off[BT];
+          f32x4 v[BT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
+          for (int i = 0; i < BT; ++i) {
             const int c = lane + 64 * (i0c + i), row = c / NCL, col = HALF * half + 4 * (c % NCL);
             off[i] = (row < nrows && col < a.d) ? (uint32_t)(((size_t)row * qstride + col) * 4) : ATTN_BUF_OOB;
             v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, off[i], 0, 0));
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = lane + 64 * (i0c + i);
-            v[i] += *reinterpret_cast<const f32x4*>(stg + (c / NCL) * LW + 4 * (c % NCL));
+          for (int i = 0; i < BT; ++i) {
+            const int c = lane + 64 * (i0c + i), row = c / NCL, col = HALF * half + 4 * (c % NCL);
+            v[i] += *reinterpret_cast<const f32x4*>(stg + row * LW + 4 * (c % NCL));
+            if constexpr (ROPE) {
+              const long long pos = (long long)r0 + row + a.rope_pos;
+              const f32x2 p0 = rope_back_pair(v[i][0], v[i][1], pos, rope_freq(col, a.d, a.rope_base));
+              const f32x2 p1 = rope_back_pair(v[i][2], v[i][3], pos, rope_freq(col + 2, a.d, a.rope_base));
+              v[i] = f32x4{p0[0], p0[1], p1[0], p1[1]};
+            }
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v[i]), rq, off[i], 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
