@@ -273,14 +273,26 @@ __global__ __launch_bounds__(256) void k_cvt16(CvtArgs a) {
   const float* src = which == 0 ? a.Q : which == 1 ? a.dO : which == 2 ? a.K : a.V;
   _Float16* dst = which == 0 ? a.Qh : which == 1 ? a.dOh : which == 2 ? a.Kh : a.Vh;
   const size_t stride = (size_t)heads * a.d;
-  // 4 columns per thread: 16-byte reads, 8-byte writes (head_dim is a multiple of 16)
-  for (int i = threadIdx.x; i < 32 * (DP / 4); i += 256) {
-    const int r = i / (DP / 4), c = 4 * (i % (DP / 4));
-    const int s = r0 + r;
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (s < a.S && c < a.d)
-      v = *reinterpret_cast<const f32x4*>(src + (size_t)s * stride + (size_t)head * a.d + c);
-    *reinterpret_cast<h4*>(dst + ((size_t)head * a.Sp + s) * DP + c) = __builtin_convertvector(v, h4);
+  const int nrows = max(0, min(32, a.S - r0));
+  // chunks of 4 columns: 16-byte reads, 8-byte writes (head_dim is a multiple
+  // of 16).  Every read of the thread is issued before its first write, so
+  // the reads overlap instead of each waiting behind the previous write; a
+  // chunk past S or head_dim reads zeros from beyond the buffer range.
+  constexpr int PER = 32 * (DP / 4) / 256;  // chunks per thread
+  static_assert(32 * (DP / 4) % 256 == 0, "whole chunks per thread");
+  const auto rs = wave_rsrc(src + (size_t)r0 * stride + (size_t)head * a.d,
+                            nrows > 0 ? (uint32_t)(((size_t)(nrows - 1) * stride + a.d) * 4) : 0u);
+  f32x4 v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + 256 * k, r = i / (DP / 4), c = 4 * (i % (DP / 4));
+    const uint32_t off = (r < nrows && c < a.d) ? (uint32_t)(((size_t)r * stride + c) * 4) : ATTN_BUF_OOB;
+    v[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int i = threadIdx.x + 256 * k, r = i / (DP / 4), c = 4 * (i % (DP / 4));
+    *reinterpret_cast<h4*>(dst + ((size_t)head * a.Sp + r0 + r) * DP + c) = __builtin_convertvector(v[k], h4);
   }
   if (which == 0 && threadIdx.x < 32 && r0 + (int)threadIdx.x < a.S) {
     const size_t i = (size_t)(r0 + threadIdx.x) * a.H + head;
