@@ -49,6 +49,19 @@ def test_f16_rope_large_offset():
     check_full(make_inputs(3), "workload 3 f16 rope offset 1e6", f16=True, rope=(10000.0, 1_000_000))
 
 
+@pytest.mark.parametrize("case", [(257, 4, 2, 192, "docs"), (161, 4, 2, 256, "docs"),
+                                  (129, 4, 1, 128, "causal")],
+                         ids=lambda c: "S%dH%dKV%dd%d_%s" % c)
+def test_f16_rope_large_offset_wide_heads(case):
+    # positions near 2^31 at the head dims whose dQ write-back rotates whole
+    # 16-byte row chunks: angles up to ~2e9 rad in the fp64 sincos
+    S, H, KV, d, kind = case
+    rng = np.random.default_rng(8600 + S + d)
+    p = random_problem(rng, S, H, KV, d, seg=make_seg(rng, S, kind))
+    check_full(p, "f16 rope offset 2^31-S-1 " + "S%dH%dKV%dd%d_%s" % case, f16=True,
+               rope=(10000.0, 2**31 - S - 1), f16_bound=True)
+
+
 @pytest.mark.parametrize("wid", [4, 5])
 def test_f16_rope_fullsize_whole_tensor(wid):
     x, _, lse, _ = reference(wid)
