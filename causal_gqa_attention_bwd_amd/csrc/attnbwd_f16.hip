@@ -1585,13 +1585,15 @@ static attn_status_t launch_f16(const F16Args& f, const CvtArgs& c, const float*
   // the role-split key-major kernel where its 256 registers per wave hold
   // the work without spilling (up to 128 columns; at 128 with RoPE the
   // write-back's rotation spills, 0.535 against 0.452 ms); else one wave per
-  // key block
+  // key block.  With split heads the pass writes unrotated partial sums and
+  // k_sumparts rotates the total, so there the kernel without the rotation
+  // serves RoPE calls too
   if constexpr (DP <= 96) {
-    if (f.rope)
+    if (f.rope && f.splits == 1)
       hipLaunchKernelGGL((k_kv16r<DP, true>), dim3(kv_grid), dim3(512), 0, st, f);
     else
       hipLaunchKernelGGL((k_kv16r<DP, false>), dim3(kv_grid), dim3(512), 0, st, f);
-  } else if (DP == 128 && !f.rope) {
+  } else if (DP == 128 && (!f.rope || f.splits > 1)) {
     hipLaunchKernelGGL((k_kv16r<128, false>), dim3(kv_grid), dim3(512), 0, st, f);
   } else {
     if (f.rope)
