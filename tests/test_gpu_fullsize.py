@@ -10,7 +10,9 @@ dV.  Covered here: attn_bwd, attn_bwd_o (given the oracle's O: its row term
 dO . O equals the pages' sum_j P dP up to the fp32 rounding of O and LSE,
 about 1e-7 relative), the forward attn_fwd_lse, and the document-sum
 invariants on the GPU's own forward LSE.  attn_bwd_f16 at these sizes is in
-test_gpu_f16.py, on the same references."""
+test_gpu_f16.py, on the same references.  At S=32768 (H=32, KV=8, d=128)
+attn_bwd and attn_bwd_f16 (its dS tiles stored, or formed again) are compared
+on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -90,44 +92,66 @@ def test_fullsize_document_invariants(wid):
     assert worst_k <= 1e-4 and worst_v <= 1e-4
 
 
+_LONG = {}
+
+
+def long_sample():
+    """S=32768, H=32, KV=8, d=128 plain causal (the long workload): its inputs,
+    the sampled rows and the oracle's gradients of them, computed once per
+    session.  The oracle computes LSE for the rows the compared outputs read
+    and the gradients of sampled rows: 24 dQ rows spread over the sequence and
+    the dK, dV rows of 6 keys in the last 256 positions (each output row covers
+    every head); the other rows get ln(#visible keys), a finite LSE none of
+    the compared outputs reads."""
+    if not _LONG:
+        import oracle
+        from causal_gqa_attention_bwd_amd.workloads import make_inputs
+        x = make_inputs(6)
+        w = x["workload"]
+        rng = np.random.default_rng(6060)
+        q_rows = np.unique(np.r_[0, 1, 31, 32, 4095, 16384, w.S - 1,
+                                 rng.integers(0, w.S, 17)]).astype(np.int32)
+        k_rows = np.array([w.S - 256, w.S - 193, w.S - 128, w.S - 65, w.S - 2, w.S - 1], np.int32)
+        need = oracle.rows_needed(None, w.S, q_rows, k_rows)
+        say(f"[oracle] workload 6: LSE of {len(need)} rows, gradients of {len(q_rows)} dQ rows "
+            f"and {len(k_rows)} dK/dV rows")
+        lse = np.log(np.arange(1, w.S + 1, dtype=np.float64))[:, None].repeat(w.H, axis=1)
+        _, lse_need = oracle.attn_fwd_rows(x["Q"], x["K"], x["V"], None, x["scale"], need,
+                                           nthreads=16)
+        lse = lse.astype(np.float32)
+        lse[need] = lse_need
+        ref = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], x["dO"], lse, None, x["scale"],
+                                   q_rows, k_rows, nthreads=16)
+        _LONG.update(x=x, lse=lse, q_rows=q_rows, k_rows=k_rows, ref=ref)
+    return _LONG
+
+
+def check_long_sample(tag, got):
+    s = long_sample()
+    rq, rk, rv = s["ref"]
+    dQ, dK, dV = got
+    for name, g, r in (("dQ", dQ[s["q_rows"]], rq), ("dK", dK[s["k_rows"]], rk),
+                       ("dV", dV[s["k_rows"]], rv)):
+        e = float(np.max(np.abs(g - r))) / float(np.max(np.abs(r)))
+        say(f"[gpu] {tag} sampled {name}: rel err {e:.2e}")
+        assert e <= TOL, f"{tag}: {name} rel err {e:.3e} > {TOL}"
+
+
 def test_long_sequence_in_head_chunks_sampled():
-    # S=32768, H=32, KV=8, d=128 plain causal: the stored tiles of all heads
-    # (137 GB) exceed the default scratch limit, so the stored-tile passes run
-    # in chunks of one KV group, the launch configuration bench.py times for
-    # this workload.  The oracle computes LSE for the rows the compared
-    # outputs read and the gradients of sampled rows: 24 dQ rows spread over
-    # the sequence and the dK, dV rows of 6 keys in the last 256 positions
-    # (each output row covers every head, so every chunk); the other rows get
-    # ln(#visible keys), a finite LSE none of the compared outputs reads.
-    # Every row is then held to the document-sum invariants on the GPU's own
-    # forward LSE below.
-    import oracle
-    from causal_gqa_attention_bwd_amd.workloads import make_inputs
-    x = make_inputs(6)
+    # the stored tiles of all heads (137 GB) exceed the default scratch limit,
+    # so the stored-tile passes run in chunks of one KV group, the launch
+    # configuration bench.py times for this workload; the sampled rows against
+    # the oracle, then every row held to the document-sum invariants on the
+    # GPU's own forward LSE
+    s = long_sample()
+    x, lse = s["x"], s["lse"]
     w = x["workload"]
     heads = binding.bwd_plan_heads(w.S, w.H, w.KV, w.d)[1]
     assert 0 < heads < w.H, "expected stored tiles in head chunks at this size"
-    rng = np.random.default_rng(6060)
-    q_rows = np.unique(np.r_[0, 1, 31, 32, 4095, 16384, w.S - 1,
-                             rng.integers(0, w.S, 17)]).astype(np.int32)
-    k_rows = np.array([w.S - 256, w.S - 193, w.S - 128, w.S - 65, w.S - 2, w.S - 1], np.int32)
-    need = oracle.rows_needed(None, w.S, q_rows, k_rows)
-    say(f"[oracle] workload 6: LSE of {len(need)} rows, gradients of {len(q_rows)} dQ rows "
-        f"and {len(k_rows)} dK/dV rows")
-    lse = np.log(np.arange(1, w.S + 1, dtype=np.float64))[:, None].repeat(w.H, axis=1)
-    _, lse_need = oracle.attn_fwd_rows(x["Q"], x["K"], x["V"], None, x["scale"], need,
-                                       nthreads=16)
-    lse = lse.astype(np.float32)
-    lse[need] = lse_need
-    rq, rk, rv = oracle.attn_bwd_rows(x["Q"], x["K"], x["V"], x["dO"], lse, None, x["scale"],
-                                      q_rows, k_rows, nthreads=16)
     say(f"[gpu] workload 6: attn_bwd S={w.S} H={w.H} in chunks of {heads} heads")
-    dQ, dK, dV = gpu_bwd(x, lse, use_seg=False)
-    for name, g, r in (("dQ", dQ[q_rows], rq), ("dK", dK[k_rows], rk), ("dV", dV[k_rows], rv)):
-        e = float(np.max(np.abs(g - r))) / float(np.max(np.abs(r)))
-        say(f"[gpu] workload 6 sampled {name}: rel err {e:.2e}")
-        assert e <= TOL, f"workload 6: {name} rel err {e:.3e} > {TOL}"
-    del dQ, dK, dV
+    got = gpu_bwd(x, lse, use_seg=False)
+    check_long_sample("workload 6", got)
+    del got
     # invariants over every row: sum_j dK_j = 0 and sum_j dV_j = sum_s dO_s
     # (over the group's heads) with the GPU's own exact-row LSE
     t = {k: to_dev(x[k]) for k in ("Q", "K", "V", "dO")}
@@ -143,3 +167,21 @@ def test_long_sequence_in_head_chunks_sampled():
         w.S, w.KV, -1, w.d).sum(dim=(0, 2)).max())
     say(f"[gpu] workload 6: sums over every key: dK {ek:.2e}, dV - dO {ev:.2e}")
     assert ek <= 1e-4 and ev <= 1e-4
+
+
+@pytest.mark.parametrize("stored", [False, True], ids=["ds_formed_again", "ds_stored"])
+def test_f16_long_sequence_sampled(stored):
+    # attn_bwd_f16 on the long workload: its dS tiles (2 KiB per block pair
+    # and head, 34.4 GB) either just exceed the scratch limit (the query-major
+    # pass forms dS again) or just fit it (k_dqs16 reads them), at the fp32
+    # entry's bar
+    s = long_sample()
+    x, lse = s["x"], s["lse"]
+    w = x["workload"]
+    nblk = (w.S + 31) // 32
+    ds_bytes = nblk * (nblk + 1) // 2 * w.H * 2048
+    mode = "stored dS" if stored else "dS formed again"
+    say(f"[gpu] workload 6: attn_bwd_f16 S={w.S} H={w.H}, {mode}")
+    with binding.scratch_limit(ds_bytes if stored else ds_bytes - 1):
+        got = gpu_bwd(x, lse, use_seg=False, f16=True)
+    check_long_sample(f"workload 6 f16 {mode}", got)
