@@ -2011,10 +2011,17 @@ extern "C" attn_status_t attn_profile_end(double* ms, int* n_calls) {
 // opens the record of a new call.
 attn_status_t profile_mark(hipStream_t st, bool first) {
   if (!g_prof.on) return ATTN_OK;
+  // timing only, so without the system-scope fence: its cache writeback and
+  // invalidation would hold the stream a few microseconds between the passes
+  // it measures
   hipEvent_t e;
-  hipError_t err = hipEventCreate(&e);
-  if (err == hipSuccess) err = hipEventRecord(e, st);
+  hipError_t err = hipEventCreateWithFlags(&e, hipEventDisableSystemFence);
   if (err != hipSuccess) return fail(ATTN_ERR_HIP, "profile event: %s", hipGetErrorString(err));
+  err = hipEventRecord(e, st);
+  if (err != hipSuccess) {
+    (void)hipEventDestroy(e);
+    return fail(ATTN_ERR_HIP, "profile event: %s", hipGetErrorString(err));
+  }
   if (first || g_prof.calls.empty()) g_prof.calls.emplace_back();
   g_prof.calls.back().push_back(e);
   return ATTN_OK;
